@@ -1,0 +1,264 @@
+"""Plain CPU oracle for the IntAttention fully-integer attention forward pass.
+
+TEST INFRASTRUCTURE ONLY. This module is the slow, obviously-correct statement
+of what the GPU path must compute. Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it; the product path never does, and
+this module imports nothing from the product package (numpy and the standard
+library only).
+
+Source: the IntAttention digest pages (euno.news, arXiv 2511.21513v1, Chinese
+and Korean editions), section "Methodology":
+  * step 2 "Integer-only softmax (IndexSoftmax)": raw int32 scores are clipped
+    with a sparsity-aware threshold into a small range; a precomputed
+    32-entry table holds exp approximations over that range and is indexed
+    directly by the integer score; the pseudo-exponents are summed in int32
+    and scaled by an integer reciprocal (multiply + right shift) into a
+    softmax-like distribution, with no floating point;
+  * step 3 "Integration": Q.K^T and the value product stay in the integer
+    domain, keeping the data flow INT8 end to end.
+The pages fix none of the integer widths, roundings, the table contents or the
+threshold value. Every such choice below is a stated reading of the pages,
+described where it is made, and is the specification the GPU path must
+reproduce bit for bit.
+
+Arithmetic conventions
+  * Host parameters: IEEE-754 binary64 from float32 inputs, correctly rounded
+    operations only (*, /, sqrt), round-half-even (Python round == C rint),
+    math.frexp (exact), math.exp (the platform libm) for the table.
+  * Device-side steps: exact integers. Python ints or numpy int64. The two
+    contractions use float64 BLAS, which is exact here because every partial
+    sum is an integer of magnitude below 2**53 (|Q.K| <= D*127**2 and
+    |P.V| <= Skv*255*127), so any summation order gives the exact integer.
+
+Parity pins: see tests/test_oracle_*.py. Every function here is pinned by a
+property, closed form, brute-force twin or exact-rational bound; none is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Fixed widths of the integer encoding.
+# ---------------------------------------------------------------------------
+LUT_SIZE = 32                 # the pages: a 32-entry exp table
+LUT_ONE = 1 << 15             # Q15: table entry for a zero relative score
+IDX_SHIFT = 24                # fixed-point fraction bits of the bin multiplier
+P_ONE = 255                   # uint8 probabilities, target row sum 255
+R_SHIFT = 23                  # reciprocal fixed point: R = round(255*2^23 / E)
+REQ_FRAC = 31                 # requantisation multiplier normalised to [2^30, 2^31)
+SKV_MAX = 65535               # keeps E < 2^31 and every int32 accumulator exact
+MU_MIN = 2.0 ** -16           # bin multiplier range (index units per score unit)
+MU_MAX = 2.0 ** -1
+REQ_SHIFT_MIN = 1
+REQ_SHIFT_MAX = 63
+
+# Default sparsity-aware threshold, in logit units: a key whose
+# logit trails the row max by more than ln(510) has exact softmax weight
+# below 1/510 of the max key's, i.e. below half a uint8 step, so it is a
+# provable zero of the 8-bit probability and may be dropped.
+DEFAULT_CLIP = float(np.float32(math.log(510.0)))
+
+
+class OracleRangeError(ValueError):
+    """Arguments outside the ranges the integer encoding is defined for."""
+
+
+@dataclass(frozen=True)
+class Params:
+    """Integers frozen on the host before any score is computed."""
+    lut: tuple            # 32 uint16 table entries, lut[31] == 0
+    idx_mul: int          # M: bin multiplier, idx = (x*M + 2^23) >> 24
+    idx_shift: int        # always IDX_SHIFT
+    x_clip: int           # smallest relative score x that lands in slot 31
+    req_mul: int          # M_o in [2^30, 2^31)
+    req_shift: int        # sh_o
+    alpha: float          # logit units per integer score unit
+    delta: float          # table bin width in logit units
+    mu: float             # alpha / delta
+    mu_o: float           # s_v / (255 * s_o)
+
+
+def _f32(x) -> float:
+    """Round to float32 and widen to binary64 (the C ABI takes float32)."""
+    return float(np.float32(x))
+
+
+def build_lut(clip: float) -> tuple:
+    """The 32-entry exp table.
+
+    Slot k approximates exp(-k * delta) with delta = clip / 31, stored as
+    round-half-even(2^15 * exp(-k*delta)) for k < 31. Slot 31 is the sparse
+    tail and holds 0: every key clipped there drops out of the sum.
+    """
+    c = _f32(clip)
+    if not (math.isfinite(c) and c > 0.0):
+        raise OracleRangeError("clip must be finite and > 0")
+    delta = c / 31.0
+    lut = [int(round(LUT_ONE * math.exp(-(float(k) * delta)))) for k in range(LUT_SIZE - 1)]
+    lut.append(0)
+    return tuple(lut)
+
+
+def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
+                  clip: float) -> Params:
+    """Host parameter derivation.
+
+    alpha = s_q*s_k/sqrt(D) folds the 1/sqrt(d) attention scale into the
+    index multiplier; mu = alpha/delta converts an integer score gap into
+    table slots; M = round(mu * 2^24).
+    """
+    if D < 1:
+        raise OracleRangeError("D must be >= 1")
+    sq, sk, sv, so, c = (_f32(s) for s in (s_q, s_k, s_v, s_o, clip))
+    for s in (sq, sk, sv, so):
+        if not (math.isfinite(s) and s > 0.0):
+            raise OracleRangeError("scales must be finite and > 0")
+    lut = build_lut(c)
+    alpha = (sq * sk) / math.sqrt(float(D))
+    delta = c / 31.0
+    mu = alpha / delta
+    if not (MU_MIN <= mu < MU_MAX):
+        raise OracleRangeError("index multiplier outside [2^-16, 2^-1)")
+    idx_mul = int(round(math.ldexp(mu, IDX_SHIFT)))
+    # smallest x with (x*M + 2^23) >> 24 >= 31, i.e. x*M >= 61 * 2^23
+    num = 61 << (IDX_SHIFT - 1)
+    x_clip = -(-num // idx_mul)
+    mu_o = sv / (255.0 * so)
+    m_o, e_o = math.frexp(mu_o)
+    req_mul = int(round(math.ldexp(m_o, REQ_FRAC)))
+    if req_mul == (1 << REQ_FRAC):
+        req_mul = 1 << (REQ_FRAC - 1)
+        e_o += 1
+    req_shift = REQ_FRAC - e_o
+    if not (REQ_SHIFT_MIN <= req_shift <= REQ_SHIFT_MAX):
+        raise OracleRangeError("output multiplier outside the encodable range")
+    return Params(lut=lut, idx_mul=idx_mul, idx_shift=IDX_SHIFT, x_clip=x_clip,
+                  req_mul=req_mul, req_shift=req_shift, alpha=alpha, delta=delta,
+                  mu=mu, mu_o=mu_o)
+
+
+# ---------------------------------------------------------------------------
+# Elementwise steps (numpy int64, exact)
+# ---------------------------------------------------------------------------
+def slot_index(x, prm: Params):
+    """Table slot of a relative score x = m - s >= 0.
+
+    Uniform bins of width delta, nearest bin: idx = (x*M + 2^23) >> 24,
+    clipped to the last slot (the sparsity-aware clip).
+    """
+    x = np.asarray(x, dtype=np.int64)
+    half = np.int64(1 << (prm.idx_shift - 1))
+    idx = (x * np.int64(prm.idx_mul) + half) >> np.int64(prm.idx_shift)
+    return np.minimum(idx, LUT_SIZE - 1)
+
+
+def reciprocal(E):
+    """Integer reciprocal of the row sum: R = floor((255*2^23 + floor(E/2)) / E)."""
+    E = np.asarray(E, dtype=np.int64)
+    return (np.int64(P_ONE << R_SHIFT) + E // 2) // E
+
+
+def normalise(e, R):
+    """uint8 probability p = (e*R + 2^22) >> 23 (round half up)."""
+    e = np.asarray(e, dtype=np.int64)
+    return (e * R + np.int64(1 << (R_SHIFT - 1))) >> np.int64(R_SHIFT)
+
+
+def requantise(a, prm: Params):
+    """int32 accumulator -> int8 output, symmetric round half away from zero.
+
+    out = sign(a) * min(127, (|a|*M_o + 2^(sh_o-1)) >> sh_o). With
+    |a| < 2^31 and M_o < 2^31 the product and the rounding term stay below
+    2^63, so uint64 holds them exactly.
+    """
+    a = np.asarray(a, dtype=np.int64)
+    mag = np.abs(a)
+    if mag.size and int(mag.max()) >= (1 << 31):
+        raise OracleRangeError("accumulator outside int32")
+    mag = mag.astype(np.uint64)
+    q = (mag * np.uint64(prm.req_mul) + np.uint64(1 << (prm.req_shift - 1))) >> np.uint64(prm.req_shift)
+    q = np.minimum(q, np.uint64(127)).astype(np.int64)
+    return (np.sign(a) * q).astype(np.int8)
+
+
+# ---------------------------------------------------------------------------
+# One attention head
+# ---------------------------------------------------------------------------
+def allowed_mask(Sq: int, Skv: int, causal: bool):
+    """allowed(i, j): j < Skv and, when causal, j <= i + Skv - Sq (bottom-right)."""
+    j = np.arange(Skv)[None, :]
+    if not causal:
+        return np.ones((Sq, Skv), dtype=bool)
+    i = np.arange(Sq)[:, None]
+    return j <= i + (Skv - Sq)
+
+
+def head_forward(qh, kh, vh, prm: Params, causal: bool):
+    """One (b, h) slice. Returns out int8 [Sq, D], m int64 [Sq], E int64 [Sq],
+    P uint8 [Sq, Skv]."""
+    Sq, D = qh.shape
+    Skv = kh.shape[0]
+    # Q.K^T: exact integer contraction (float64 BLAS, exact below 2^53)
+    S = np.rint(qh.astype(np.float64) @ kh.astype(np.float64).T).astype(np.int64)
+    allow = allowed_mask(Sq, Skv, causal)
+    lo = np.iinfo(np.int64).min
+    m = np.where(allow, S, lo).max(axis=1)
+    x = m[:, None] - S
+    idx = np.where(allow, slot_index(np.where(allow, x, 0), prm), LUT_SIZE - 1)
+    lut = np.asarray(prm.lut, dtype=np.int64)
+    e = lut[idx]
+    E = e.sum(axis=1)
+    R = reciprocal(E)
+    P = normalise(e, R[:, None])
+    # P.V: exact integer contraction
+    A = np.rint(P.astype(np.float64) @ vh.astype(np.float64)).astype(np.int64)
+    out = requantise(A, prm)
+    return out, m, E, P.astype(np.uint8)
+
+
+def check_args(q, k, v, causal):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise OracleRangeError("tensors must be [B, H, S, D]")
+    B, H, Sq, D = q.shape
+    if k.shape[:2] != (B, H) or v.shape != k.shape or k.shape[3] != D:
+        raise OracleRangeError("shape mismatch")
+    Skv = k.shape[2]
+    if Skv < 1 or Skv > SKV_MAX:
+        raise OracleRangeError("Skv must be in [1, 65535]")
+    if causal and Sq > Skv:
+        raise OracleRangeError("causal attention needs Sq <= Skv")
+    for t in (q, k, v):
+        if t.dtype != np.int8:
+            raise OracleRangeError("inputs must be int8")
+        if t.size and int(t.min()) < -127:
+            raise OracleRangeError("inputs must lie in [-127, 127]")
+    return B, H, Sq, Skv, D
+
+
+def forward(q, k, v, scales, clip=DEFAULT_CLIP, causal=False, stats=False):
+    """Full forward over [B, H, S, D] int8 tensors.
+
+    scales = (s_q, s_k, s_v, s_o). Returns out int8 [B, H, Sq, D]; with
+    stats=True also (m int64 [B,H,Sq], E int64 [B,H,Sq], P uint8 [B,H,Sq,Skv]).
+    """
+    q, k, v = (np.ascontiguousarray(t) for t in (q, k, v))
+    B, H, Sq, Skv, D = check_args(q, k, v, causal)
+    prm = derive_params(D, *scales, clip)
+    out = np.zeros((B, H, Sq, D), dtype=np.int8)
+    if stats:
+        M = np.zeros((B, H, Sq), dtype=np.int64)
+        Es = np.zeros((B, H, Sq), dtype=np.int64)
+        Ps = np.zeros((B, H, Sq, Skv), dtype=np.uint8)
+    for b in range(B):
+        for h in range(H):
+            o, m, E, P = head_forward(q[b, h], k[b, h], v[b, h], prm, causal)
+            out[b, h] = o
+            if stats:
+                M[b, h], Es[b, h], Ps[b, h] = m, E, P
+    if stats:
+        return out, M, Es, Ps
+    return out
