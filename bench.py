@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Benchmark of the integer attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config bert]
+
+A step is one intattn_forward call over the whole workload (every head of
+every batch entry: Q.K^T, IndexSoftmax, P.V, requantisation), with inputs
+already resident in HBM. Prints one JSON line. The default workload is
+BERT-base encoder attention (B=8, H=12, S=512, d=64, non-causal); --config
+selects one of the other four workloads (tiny, vit, llama_prefill, decode).
+
+Work counted (algorithmic only): 4*d integer ops per allowed score (2*d for
+Q.K^T, 2*d for P.V; causal counts the lower triangle with the diagonal), and
+Q + K + V + O bytes of int8 read or written once.
+
+Timing: W untimed calls, then K calls bracketed by synchronisation and HIP
+events recorded on the stream the library launches on (the caller's current
+stream). The same events give the kernel's average duration per launch used
+for the roofline fraction.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+
+DEFAULT_STEPS = {"tiny": 2000, "bert": 500, "vit": 500, "llama_prefill": 50, "decode": 100}
+BOUND = {"tiny": "mfma", "bert": "mfma", "vit": "mfma", "llama_prefill": "mfma", "decode": "hbm"}
+KERNEL_NAME = {"tiny": "ia_general_kernel<64>", "bert": "ia_general_kernel<64>",
+               "vit": "ia_general_kernel<64>", "llama_prefill": "ia_general_kernel<128>",
+               "decode": "ia_general_kernel<128>"}
+
+
+def algorithmic_work(w):
+    """(ops, bytes, allowed scores) of one forward call."""
+    B, H, Sq, Skv, D = w.shape
+    if w.causal:
+        shift = Skv - Sq
+        # row i attends keys 0 .. i + shift
+        scores_per_head = sum(min(Skv, i + shift + 1) for i in range(Sq))
+    else:
+        scores_per_head = Sq * Skv
+    scores = B * H * scores_per_head
+    ops = 4 * D * scores
+    nbytes = B * H * D * (2 * Sq + 2 * Skv)
+    return ops, nbytes, scores
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """Time the CPU oracle on a bounded sample of the workload's heads.
+
+    Heads are processed one oracle call each, cycling over the workload's
+    (b, h) pairs until about budget_s seconds of CPU work have run (a large
+    workload stops part-way through its heads; a small one is repeated).
+    Returns (summary dict, {(b, h): oracle output of the first pass}).
+    """
+    from oracle import intattn_oracle as O
+    from integer_only_quantized_amd import workloads as W
+
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    cores = len(os.sched_getaffinity(0))
+    sub = W.slice_heads(w, heads[:1])               # warm-up (BLAS thread start-up)
+    O.forward(sub.q, sub.k, sub.v, sub.scales, sub.clip, sub.causal)
+    n_calls, t_total, results = 0, 0.0, {}
+    while t_total < budget_s:
+        bh = heads[n_calls % len(heads)]
+        sub = W.slice_heads(w, [bh])
+        t0 = time.perf_counter()
+        o = O.forward(sub.q, sub.k, sub.v, sub.scales, sub.clip, sub.causal)
+        t_total += time.perf_counter() - t0
+        if bh not in results:
+            results[bh] = o[0, 0]
+        n_calls += 1
+    ops_all, _, _ = algorithmic_work(w)
+    frac = n_calls / len(heads)                       # workload calls' worth of heads
+    tops = ops_all * frac / t_total / 1e12
+    info = {
+        "value": tops, "unit": "TOPS", "cores": cores, "kind": "oracle",
+        "sample": f"{n_calls} single-head oracle calls cycling over the {len(heads)} (b,h) heads "
+                  f"of the same workload ({frac:.3g} workload calls), {t_total:.2f} s wall; "
+                  f"numpy float64 BLAS contractions (exact) + int64 elementwise; "
+                  f"CPU {platform.processor() or platform.machine()}",
+        "seconds": t_total,
+        "calls_per_s": frac / t_total,
+    }
+    return info, results
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="bert",
+                    choices=["tiny", "bert", "vit", "llama_prefill", "decode"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention heads are independent and "
+              "this build runs no multi-GPU path (see the sharding notes in the design "
+              "document). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from integer_only_quantized_amd import _binding as ia
+    from integer_only_quantized_amd import workloads as W
+
+    steps = args.steps or DEFAULT_STEPS[args.config]
+    w = W.make_config(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        ia.forward(q, k, v, w.scales, w.clip, w.causal, out=out)
+    torch.cuda.synchronize(dev)
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t_wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        ia.forward(q, k, v, w.scales, w.clip, w.causal, out=out)
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    t_wall = time.perf_counter() - t_wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / steps
+
+    ops, nbytes, scores = algorithmic_work(w)
+    sec = ms_per_step / 1e3
+    tops = ops / sec / 1e12
+    gbs = nbytes / sec / 1e9
+    calls = 1.0 / sec
+
+    bound = BOUND[args.config]
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": tops, "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                "frac": tops / PEAK_INT8_TOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS}
+    roof["kernel"] = KERNEL_NAME[args.config]
+    roof["per_launch"] = {"ops": ops, "bytes": nbytes, "scores": scores,
+                          "avg_launch_us": ms_per_step * 1e3}
+    roof["traffic"] = None
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        cpu, ref = cpu_baseline(w, args.cpu_budget)
+        got = out.cpu().numpy()
+        parity = all(np.array_equal(got[b, h], r) for (b, h), r in ref.items())
+        cpu["parity_on_sample"] = parity
+
+    if args.config == "decode":
+        metric_value, unit = gbs, "GB/s"
+    else:
+        metric_value, unit = tops, "TOPS"
+    line = {
+        "metric": f"int8 attention throughput ({args.config})" if args.config != "bert"
+        else "int8 attention TOPS (BERT-base S=512)",
+        "value": metric_value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": args.config, "description": w.meta.get("description"),
+                   "B": w.B, "H": w.H, "Sq": w.Sq, "Skv": w.Skv, "D": w.D, "causal": w.causal},
+        "calls_per_s": calls,
+        "int8_tops": tops,
+        "gb_per_s": gbs,
+        "wall_s_timed_region": t_wall,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

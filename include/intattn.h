@@ -1,0 +1,131 @@
+/*
+ * intattn.h - C ABI of the MI355X (gfx950) fully-integer attention library.
+ *
+ * The operation is the IntAttention forward pass (IntAttention digest pages,
+ * euno.news, arXiv 2511.21513v1, section "Methodology", steps 2 and 3):
+ * int8 Q.K^T gives int32 scores; IndexSoftmax clips each score relative to
+ * its row maximum at a sparsity-aware threshold, indexes a 32-entry exp
+ * table, sums the pseudo-exponents in int32, and scales them by an integer
+ * reciprocal (multiply + right shift) into uint8 probabilities; the uint8
+ * probabilities multiply int8 V; the int32 result is requantised to int8.
+ * No floating point is used on the device.
+ *
+ * Integer specification (the pages leave every width and rounding open; this
+ * is the reading the library implements, bit for bit):
+ *   alpha = s_q*s_k/sqrt(D), delta = clip/31, mu = alpha/delta   (binary64)
+ *   lut[k] = rint(2^15 * exp(-k*delta)) for k < 31, lut[31] = 0
+ *   M = rint(mu * 2^24), required 2^-16 <= mu < 2^-1
+ *   s_ij = sum_d q_id k_jd                        (int32)
+ *   m_i = max over allowed j of s_ij
+ *   idx_ij = min(31, ((m_i - s_ij)*M + 2^23) >> 24), 31 for masked keys
+ *   E_i = sum_j lut[idx_ij]                        (< 2^31)
+ *   R_i = (255*2^23 + E_i/2) / E_i                  (integer division)
+ *   p_ij = (lut[idx_ij]*R_i + 2^22) >> 23           (uint8)
+ *   a_id = sum_j p_ij v_jd                          (int32)
+ *   mu_o = s_v/(255*s_o) = M_o * 2^-sh_o, M_o in [2^30, 2^31)
+ *   out_id = sign(a)*min(127, (|a|*M_o + 2^(sh_o-1)) >> sh_o)
+ * A key j is allowed for query i when j < Skv and, if causal, when
+ * j <= i + Skv - Sq (causal masks are aligned to the bottom-right corner).
+ *
+ * Layout: every tensor is contiguous row-major [B, H, S, D] int8 in device
+ * memory (S = Sq for q and out, Skv for k and v). Inputs are expected in the
+ * symmetric range [-127, 127]; the library does not read device data to check
+ * this.
+ *
+ * Ownership: all tensor pointers are caller-owned device memory and must stay
+ * valid until the work queued on `stream` has finished. Structs are
+ * caller-owned host memory read during the call only. The library keeps no
+ * reference to any argument after returning.
+ *
+ * Errors: every function returns INTATTN_OK (0) or a negative code. All
+ * argument validation runs on the host before any HIP call, so an invalid
+ * call queues no work and writes nothing. A failed kernel launch returns
+ * INTATTN_E_HIP. Work is asynchronous: device faults surface at the next
+ * synchronisation of `stream`, not in the return code.
+ */
+#ifndef INTATTN_H
+#define INTATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct intattn_shape {
+    int32_t B;    /* batch, >= 0 (0: nothing to do)                          */
+    int32_t H;    /* heads, >= 0 (0: nothing to do)                          */
+    int32_t Sq;   /* query rows, >= 0 (0: nothing to do)                     */
+    int32_t Skv;  /* key/value rows, 1 .. 65535                              */
+    int32_t D;    /* head dimension; 64 or 128 on the device                 */
+} intattn_shape;
+
+typedef struct intattn_scales {
+    float q, k, v, o;  /* real value = scale * int8, each finite and > 0     */
+} intattn_scales;
+
+/* Integers derived on the host from (D, scales, clip). */
+typedef struct intattn_params {
+    uint16_t lut[32];   /* exp table, lut[0] = 32768, lut[31] = 0           */
+    int32_t  idx_mul;   /* M                                                 */
+    int32_t  idx_shift; /* always 24                                         */
+    int32_t  x_clip;    /* smallest m - s that lands in slot 31              */
+    int32_t  req_shift; /* sh_o, 1 .. 63                                     */
+    int64_t  req_mul;   /* M_o                                               */
+} intattn_params;
+
+enum {
+    INTATTN_OK      =  0,
+    INTATTN_E_NULL  = -1,  /* a required pointer is NULL                     */
+    INTATTN_E_SHAPE = -2,  /* negative size, Skv outside 1..65535, causal
+                              with Sq > Skv, or a size product overflowing  */
+    INTATTN_E_DIM   = -3,  /* D not supported by the device kernels         */
+    INTATTN_E_SCALE = -4,  /* a scale is not finite and > 0                  */
+    INTATTN_E_CLIP  = -5,  /* clip is not finite and > 0                     */
+    INTATTN_E_RANGE = -6,  /* mu outside [2^-16, 2^-1) or sh_o outside 1..63 */
+    INTATTN_E_HIP   = -7,  /* the HIP runtime reported an error              */
+    INTATTN_E_ALIGN = -8   /* a tensor pointer is not 16-byte aligned        */
+};
+
+/* The 32-entry exp table for a clip threshold (in logit units): lut_out[k] =
+ * rint(2^15 exp(-k clip/31)) for k < 31 and lut_out[31] = 0 (the table of
+ * the pages' IndexSoftmax lookup step). Host only, pure. Errors: E_NULL,
+ * E_CLIP. */
+int intattn_build_lut(float clip, uint16_t lut_out[32]);
+
+/* All host-derived integers for a call (the parameters the device kernels
+ * receive). Host only, pure. Validates shape->D >= 1 but not the device's D
+ * restriction. Errors: E_NULL, E_SHAPE, E_SCALE, E_CLIP, E_RANGE. */
+int intattn_derive_params(const intattn_shape* shape, const intattn_scales* scales,
+                          float clip, intattn_params* out);
+
+/* The attention forward pass of the pages' "Methodology" steps 2-3:
+ * out = IntAttention(q, k, v). q, k, v, out: device pointers (see Layout).
+ * causal: 0 or 1. stream: a hipStream_t (NULL for the null stream); the
+ * kernels are queued on it and the call returns without synchronising.
+ * Every tensor pointer must be 16-byte aligned. Allocates no device memory.
+ * Errors: E_NULL, E_SHAPE, E_DIM, E_ALIGN, E_SCALE, E_CLIP, E_RANGE, E_HIP. */
+int intattn_forward(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
+                    const intattn_shape* shape, const intattn_scales* scales,
+                    float clip, int causal, void* stream);
+
+/* intattn_forward plus the per-row integer state of IndexSoftmax, for parity
+ * checks: row_max [B,H,Sq] int32 (m_i), row_sum [B,H,Sq] uint32 (E_i), and,
+ * when probs is not NULL, probs [B,H,Sq,Skv] uint8 (p_ij, 0 for masked keys).
+ * row_max and row_sum are required device pointers. Runs the general kernel
+ * (not the shape-specialised ones), so it is slower than intattn_forward.
+ * Errors: as intattn_forward. */
+int intattn_forward_debug(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
+                          const intattn_shape* shape, const intattn_scales* scales,
+                          float clip, int causal, void* stream,
+                          int32_t* row_max, uint32_t* row_sum, uint8_t* probs);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* intattn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INTATTN_H */

@@ -1,0 +1,161 @@
+"""ctypes binding over libintattn.so: argument marshalling only.
+
+Every step of the attention runs in the library's HIP kernels; this module
+converts torch tensors to device pointers, reads the caller's current HIP
+stream, and turns a nonzero status into an exception. Importing it raises if
+the library has not been built (there is no CPU fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+LIB_NAME = "libintattn.so"
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, LIB_NAME)
+
+INTATTN_OK = 0
+STATUS_NAMES = {
+    0: "INTATTN_OK", -1: "INTATTN_E_NULL", -2: "INTATTN_E_SHAPE", -3: "INTATTN_E_DIM",
+    -4: "INTATTN_E_SCALE", -5: "INTATTN_E_CLIP", -6: "INTATTN_E_RANGE", -7: "INTATTN_E_HIP",
+    -8: "INTATTN_E_ALIGN",
+}
+DEFAULT_CLIP = float(ctypes.c_float(math.log(510.0)).value)
+
+
+class IntAttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS_NAMES.get(code, code)} ({strerror(code)})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Sq", ctypes.c_int32),
+                ("Skv", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
+class Scales(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_float), ("k", ctypes.c_float), ("v", ctypes.c_float),
+                ("o", ctypes.c_float)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("lut", ctypes.c_uint16 * 32), ("idx_mul", ctypes.c_int32),
+                ("idx_shift", ctypes.c_int32), ("x_clip", ctypes.c_int32),
+                ("req_shift", ctypes.c_int32), ("req_mul", ctypes.c_int64)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run `python -m integer_only_quantized_amd.build` "
+            "(the integer attention path has no CPU fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.intattn_build_lut.argtypes = [f32, ctypes.POINTER(ctypes.c_uint16)]
+    lib.intattn_build_lut.restype = i32
+    lib.intattn_derive_params.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Scales), f32,
+                                          ctypes.POINTER(Params)]
+    lib.intattn_derive_params.restype = i32
+    lib.intattn_forward.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), ctypes.POINTER(Scales),
+                                    f32, i32, vp]
+    lib.intattn_forward.restype = i32
+    lib.intattn_forward_debug.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape),
+                                          ctypes.POINTER(Scales), f32, i32, vp, vp, vp, vp]
+    lib.intattn_forward_debug.restype = i32
+    lib.intattn_strerror.argtypes = [i32]
+    lib.intattn_strerror.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def strerror(code: int) -> str:
+    return _lib.intattn_strerror(int(code)).decode()
+
+
+def _check(code: int, where: str):
+    if code != INTATTN_OK:
+        raise IntAttnError(code, where)
+
+
+def build_lut(clip: float = DEFAULT_CLIP) -> list:
+    buf = (ctypes.c_uint16 * 32)()
+    _check(_lib.intattn_build_lut(float(clip), buf), "intattn_build_lut")
+    return list(buf)
+
+
+def derive_params(D: int, scales, clip: float = DEFAULT_CLIP) -> dict:
+    shape = Shape(1, 1, 1, 1, int(D))
+    sc = Scales(*[float(s) for s in scales])
+    p = Params()
+    _check(_lib.intattn_derive_params(ctypes.byref(shape), ctypes.byref(sc), float(clip),
+                                      ctypes.byref(p)), "intattn_derive_params")
+    return {"lut": list(p.lut), "idx_mul": p.idx_mul, "idx_shift": p.idx_shift,
+            "x_clip": p.x_clip, "req_shift": p.req_shift, "req_mul": p.req_mul}
+
+
+def forward_raw(q_ptr, k_ptr, v_ptr, out_ptr, shape, scales, clip, causal, stream=None,
+                debug=None) -> int:
+    """Call the C entry point with raw integer addresses; returns the status code."""
+    sh = Shape(*[int(x) for x in shape])
+    sc = Scales(*[float(s) for s in scales])
+    if debug is None:
+        return _lib.intattn_forward(q_ptr, k_ptr, v_ptr, out_ptr, ctypes.byref(sh), ctypes.byref(sc),
+                                    float(clip), int(bool(causal)), stream)
+    rm, rs, pr = debug
+    return _lib.intattn_forward_debug(q_ptr, k_ptr, v_ptr, out_ptr, ctypes.byref(sh),
+                                      ctypes.byref(sc), float(clip), int(bool(causal)), stream,
+                                      rm, rs, pr)
+
+
+def _check_tensors(q, k, v):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.int8 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D int8 CUDA tensor [B, H, S, D]")
+    B, H, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError("shape mismatch between q, k and v")
+    return (B, H, Sq, k.shape[2], D)
+
+
+def _stream(q):
+    import torch
+    return torch.cuda.current_stream(q.device).cuda_stream
+
+
+def forward(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False, out=None):
+    """out[B,H,Sq,D] int8 = integer attention of int8 q, k, v (torch CUDA tensors)."""
+    import torch
+    shape = _check_tensors(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.int8 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int8 tensor shaped like q")
+    code = forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), shape, scales,
+                       clip, causal, _stream(q))
+    _check(code, "intattn_forward")
+    return out
+
+
+def forward_debug(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False,
+                  with_probs: bool = False):
+    """(out, row_max int32 [B,H,Sq], row_sum int32 view of uint32 [B,H,Sq], probs uint8 or None)."""
+    import torch
+    B, H, Sq, Skv, D = _check_tensors(q, k, v)
+    out = torch.empty_like(q)
+    rm = torch.empty((B, H, Sq), dtype=torch.int32, device=q.device)
+    rs = torch.empty((B, H, Sq), dtype=torch.int32, device=q.device)
+    pr = torch.empty((B, H, Sq, Skv), dtype=torch.uint8, device=q.device) if with_probs else None
+    code = forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                       (B, H, Sq, Skv, D), scales, clip, causal, _stream(q),
+                       debug=(rm.data_ptr(), rs.data_ptr(), pr.data_ptr() if pr is not None else None))
+    _check(code, "intattn_forward_debug")
+    return out, rm, rs, pr

@@ -1,0 +1,58 @@
+"""Build libintattn.so in-tree for gfx950 (hipcc cross-compiles without a GPU).
+
+    python -m integer_only_quantized_amd.build
+
+Host derivation (intattn_host.cpp) is compiled by g++ with -ffp-contract=off
+so its binary64 arithmetic matches a plain IEEE evaluation; the HIP kernels
+are compiled by hipcc for gfx950 with packed-FP32 instruction selection
+disabled (the kernels use no floating point; the flag is set uniformly).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libintattn.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+BUILD_DIR = os.path.join(ROOT, "_build")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wextra"]
+
+
+def _run(cmd):
+    print("+ " + " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link libintattn.so; returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    inc = ["-I" + INCLUDE, "-I" + CSRC]
+    host_obj = os.path.join(BUILD_DIR, "intattn_host.o")
+    kern_obj = os.path.join(BUILD_DIR, "intattn_kernels.o")
+    cxx = shutil.which("g++") or "g++"
+    _run([cxx] + HOST_FLAGS + inc + ["-c", os.path.join(CSRC, "intattn_host.cpp"), "-o", host_obj])
+    _run([HIPCC] + HIP_FLAGS + inc + ["-c", os.path.join(CSRC, "intattn_kernels.hip"), "-o", kern_obj])
+    tmp = LIB_PATH + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", host_obj, kern_obj, "-o", tmp])
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

@@ -1,0 +1,126 @@
+// Host side of the integer attention library: argument validation and the
+// derivation of every integer the device kernels receive.
+//
+// The pages (IntAttention digest, "Methodology" step 2) describe a 32-entry
+// exp table indexed by the clipped integer score and an integer reciprocal
+// normalisation; the widths below are this library's fixed reading of them
+// (stated in include/intattn.h). All arithmetic is IEEE binary64 from float32
+// inputs with correctly rounded operations only; the file is compiled with
+// -ffp-contract=off so no multiply-add is fused, and rint() (round half to
+// even in the default rounding mode) is the only rounding used.
+#include <cfenv>
+#include <cmath>
+#include <cstdint>
+
+#include "intattn.h"
+#include "intattn_internal.h"
+
+namespace {
+
+constexpr int kLutSize = 32;
+constexpr double kLutOne = 32768.0;
+constexpr int kIdxShift = 24;
+constexpr int kReqFrac = 31;
+
+bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
+
+// The derivation assumes round-to-nearest for every binary64 operation. The
+// floating-point environment is per thread; a caller that changed the mode
+// gets it back on return.
+struct NearestRounding {
+    int saved;
+    NearestRounding() : saved(std::fegetround()) {
+        if (saved != FE_TONEAREST) std::fesetround(FE_TONEAREST);
+    }
+    ~NearestRounding() {
+        if (saved != FE_TONEAREST) std::fesetround(saved);
+    }
+};
+
+void fill_lut(double clip, uint16_t* lut) {
+    const double delta = clip / 31.0;
+    for (int k = 0; k < kLutSize - 1; ++k) {
+        const double v = std::rint(kLutOne * std::exp(-(static_cast<double>(k) * delta)));
+        lut[k] = static_cast<uint16_t>(v);
+    }
+    lut[kLutSize - 1] = 0;
+}
+
+}  // namespace
+
+extern "C" int intattn_build_lut(float clip, uint16_t lut_out[32]) {
+    if (!lut_out) return INTATTN_E_NULL;
+    if (!finite_positive(clip)) return INTATTN_E_CLIP;
+    NearestRounding guard;
+    fill_lut(static_cast<double>(clip), lut_out);
+    return INTATTN_OK;
+}
+
+int intattn_validate_shape(const intattn_shape* s, int causal) {
+    if (!s) return INTATTN_E_NULL;
+    if (s->B < 0 || s->H < 0 || s->Sq < 0) return INTATTN_E_SHAPE;
+    if (s->Skv < 1 || s->Skv > 65535) return INTATTN_E_SHAPE;
+    if (s->D < 1) return INTATTN_E_SHAPE;
+    if (causal && s->Sq > s->Skv) return INTATTN_E_SHAPE;
+    // element counts must fit size_t comfortably (64-bit indexing on device)
+    const double nq = static_cast<double>(s->B) * s->H * s->Sq * s->D;
+    const double nk = static_cast<double>(s->B) * s->H * s->Skv * s->D;
+    if (nq > 9.0e15 || nk > 9.0e15) return INTATTN_E_SHAPE;
+    return INTATTN_OK;
+}
+
+extern "C" int intattn_derive_params(const intattn_shape* shape, const intattn_scales* sc,
+                                     float clip, intattn_params* out) {
+    if (!shape || !sc || !out) return INTATTN_E_NULL;
+    if (shape->D < 1) return INTATTN_E_SHAPE;
+    if (!finite_positive(sc->q) || !finite_positive(sc->k) || !finite_positive(sc->v) ||
+        !finite_positive(sc->o))
+        return INTATTN_E_SCALE;
+    if (!finite_positive(clip)) return INTATTN_E_CLIP;
+    NearestRounding guard;
+
+    const double c = static_cast<double>(clip);
+    const double alpha = (static_cast<double>(sc->q) * static_cast<double>(sc->k)) /
+                         std::sqrt(static_cast<double>(shape->D));
+    const double delta = c / 31.0;
+    const double mu = alpha / delta;
+    if (!(mu >= std::ldexp(1.0, -16) && mu < 0.5)) return INTATTN_E_RANGE;
+
+    intattn_params p{};
+    fill_lut(c, p.lut);
+    const int64_t M = static_cast<int64_t>(std::rint(std::ldexp(mu, kIdxShift)));
+    p.idx_mul = static_cast<int32_t>(M);
+    p.idx_shift = kIdxShift;
+    const int64_t num = int64_t(61) << (kIdxShift - 1);  // x*M >= 61*2^23  <=>  slot >= 31
+    p.x_clip = static_cast<int32_t>((num + M - 1) / M);
+
+    const double mu_o = static_cast<double>(sc->v) / (255.0 * static_cast<double>(sc->o));
+    int e_o = 0;
+    const double m_o = std::frexp(mu_o, &e_o);
+    int64_t Mo = static_cast<int64_t>(std::rint(std::ldexp(m_o, kReqFrac)));
+    if (Mo == (int64_t(1) << kReqFrac)) {
+        Mo = int64_t(1) << (kReqFrac - 1);
+        e_o += 1;
+    }
+    const int sh_o = kReqFrac - e_o;
+    if (sh_o < 1 || sh_o > 63) return INTATTN_E_RANGE;
+    p.req_mul = Mo;
+    p.req_shift = sh_o;
+    *out = p;
+    return INTATTN_OK;
+}
+
+extern "C" const char* intattn_strerror(int status) {
+    switch (status) {
+        case INTATTN_OK: return "ok";
+        case INTATTN_E_NULL: return "a required pointer is NULL";
+        case INTATTN_E_SHAPE: return "invalid shape (sizes, Skv outside 1..65535, or causal with Sq > Skv)";
+        case INTATTN_E_DIM: return "head dimension not supported by the device kernels (64 or 128)";
+        case INTATTN_E_SCALE: return "a quantisation scale is not finite and positive";
+        case INTATTN_E_CLIP: return "the clip threshold is not finite and positive";
+        case INTATTN_E_RANGE: return "scales outside the encodable range (index multiplier or output shift)";
+        case INTATTN_E_HIP: return "the HIP runtime reported an error";
+        case INTATTN_E_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        default: return "unknown status";
+    }
+}

@@ -1,0 +1,111 @@
+"""C-ABI boundary checks that need no GPU.
+
+* libintattn.so loads and exports every function include/intattn.h declares;
+* the library's host derivation (table, multipliers, clip point) equals the
+  oracle's, bit for bit, over a sweep of scales, clips and head sizes;
+* every argument error is reported before any HIP call (so these run on a
+  machine without a GPU) and with the documented code.
+"""
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import intattn_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "intattn.h")
+
+B = pytest.importorskip("integer_only_quantized_amd._binding",
+                        reason="libintattn.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(intattn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert names == sorted(["intattn_build_lut", "intattn_derive_params", "intattn_forward",
+                            "intattn_forward_debug", "intattn_strerror"])
+    for n in names:
+        assert hasattr(B._lib, n), n
+
+
+def test_strerror_covers_every_code():
+    for code in list(B.STATUS_NAMES) + [-99, 5]:
+        s = B.strerror(code)
+        assert isinstance(s, str) and s
+
+
+CLIPS = [O.DEFAULT_CLIP, 0.5, 1.0, 2.0, 3.3, 5.0, 6.0, 8.0, 10.0, 16.0]
+
+
+@pytest.mark.parametrize("clip", CLIPS)
+def test_lut_equals_oracle(clip):
+    assert B.build_lut(clip) == list(O.build_lut(clip))
+
+
+def test_params_equal_oracle_sweep():
+    rng = np.random.default_rng(0)
+    n = 0
+    for D in (1, 16, 64, 100, 128, 256):
+        for _ in range(300):
+            sq, sk, sv, so = (float(np.float32(10 ** rng.uniform(-3.5, 0.5))) for _ in range(4))
+            clip = float(np.float32(rng.uniform(0.5, 12.0)))
+            try:
+                ref = O.derive_params(D, sq, sk, sv, so, clip)
+            except O.OracleRangeError:
+                with pytest.raises(B.IntAttnError) as ei:
+                    B.derive_params(D, (sq, sk, sv, so), clip)
+                assert ei.value.code == -6
+                continue
+            got = B.derive_params(D, (sq, sk, sv, so), clip)
+            assert got["lut"] == list(ref.lut)
+            assert got["idx_mul"] == ref.idx_mul
+            assert got["idx_shift"] == ref.idx_shift
+            assert got["x_clip"] == ref.x_clip
+            assert got["req_mul"] == ref.req_mul
+            assert got["req_shift"] == ref.req_shift
+            n += 1
+    assert n > 500
+
+
+def _call(shape=(1, 1, 8, 8, 64), scales=(0.05, 0.05, 0.05, 0.05), clip=O.DEFAULT_CLIP,
+          causal=False, ptrs=(0x1000, 0x2000, 0x3000, 0x4000), debug=None):
+    return B.forward_raw(*ptrs, shape, scales, clip, causal, None, debug=debug)
+
+
+def test_validation_errors_before_any_device_call():
+    E = {v: k for k, v in B.STATUS_NAMES.items()}
+    assert _call(ptrs=(0, 0x2000, 0x3000, 0x4000)) == E["INTATTN_E_NULL"]
+    assert _call(ptrs=(0x1000, 0x2000, 0x3000, 0)) == E["INTATTN_E_NULL"]
+    assert _call(shape=(1, 1, 8, 0, 64)) == E["INTATTN_E_SHAPE"]
+    assert _call(shape=(1, 1, 8, 65536, 64)) == E["INTATTN_E_SHAPE"]
+    assert _call(shape=(-1, 1, 8, 8, 64)) == E["INTATTN_E_SHAPE"]
+    assert _call(shape=(1, 1, 9, 8, 64), causal=True) == E["INTATTN_E_SHAPE"]
+    assert _call(shape=(1, 1, 8, 8, 96)) == E["INTATTN_E_DIM"]
+    assert _call(shape=(1, 1, 8, 8, 32)) == E["INTATTN_E_DIM"]
+    assert _call(ptrs=(0x1001, 0x2000, 0x3000, 0x4000)) == E["INTATTN_E_ALIGN"]
+    assert _call(ptrs=(0x1000, 0x2000, 0x3008, 0x4000)) == E["INTATTN_E_ALIGN"]
+    for bad in (0.0, -1.0, math.inf, math.nan):
+        assert _call(scales=(bad, 0.05, 0.05, 0.05)) == E["INTATTN_E_SCALE"]
+        assert _call(scales=(0.05, 0.05, 0.05, bad)) == E["INTATTN_E_SCALE"]
+        assert _call(clip=bad) == E["INTATTN_E_CLIP"]
+    assert _call(scales=(1e-4, 1e-4, 0.05, 0.05)) == E["INTATTN_E_RANGE"]   # mu < 2^-16
+    assert _call(scales=(3.0, 3.0, 0.05, 0.05)) == E["INTATTN_E_RANGE"]     # mu >= 1/2
+    assert _call(scales=(0.05, 0.05, 1e-30, 1.0)) == E["INTATTN_E_RANGE"]   # output shift
+    # debug entry point: row statistics are required
+    assert _call(debug=(0, 0x5000, None)) == E["INTATTN_E_NULL"]
+    assert _call(debug=(0x5000, 0, None)) == E["INTATTN_E_NULL"]
+
+
+def test_empty_problems_are_noops():
+    # nothing to compute: success without touching the device
+    assert _call(shape=(0, 12, 512, 512, 64)) == 0
+    assert _call(shape=(2, 0, 512, 512, 64)) == 0
+    assert _call(shape=(2, 3, 0, 7, 128), causal=True) == 0
+    assert _call(shape=(0, 12, 512, 512, 64), debug=(0x5000, 0x6000, None)) == 0
