@@ -79,6 +79,10 @@ EDGE = [
     (1, 1, 63, 200, 64, True, 111, "channel_outliers"),
     (1, 1, 129, 65, 128, False, 112, "normal"),
     (3, 1, 1, 777, 64, False, 113, "normal"),         # single query, ragged keys
+    (2, 3, 1, 16384, 128, False, 114, "normal"),      # decode kernel, largest key count
+    (1, 2, 1, 16385, 64, True, 115, "normal"),        # one key past it: general kernel
+    (4, 2, 1, 255, 128, False, 116, "channel_outliers"),
+    (1, 1, 1, 5, 64, False, 117, "student_t_tail"),
 ]
 
 
