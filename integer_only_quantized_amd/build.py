@@ -38,17 +38,30 @@ def _run(cmd):
     subprocess.run(cmd, check=True)
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source and link libintattn.so; returns its path."""
+HOST_SOURCES = ["intattn_host.cpp", "intattn_api.cpp"]
+HIP_SOURCES = ["ia_general.hip", "ia_short.hip", "ia_long.hip", "ia_decode.hip"]
+
+
+def build(verbose: bool = True, jobs: int = 8) -> str:
+    """Compile every source (in parallel) and link libintattn.so; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+
     os.makedirs(BUILD_DIR, exist_ok=True)
     inc = ["-I" + INCLUDE, "-I" + CSRC]
-    host_obj = os.path.join(BUILD_DIR, "intattn_host.o")
-    kern_obj = os.path.join(BUILD_DIR, "intattn_kernels.o")
     cxx = shutil.which("g++") or "g++"
-    _run([cxx] + HOST_FLAGS + inc + ["-c", os.path.join(CSRC, "intattn_host.cpp"), "-o", host_obj])
-    _run([HIPCC] + HIP_FLAGS + inc + ["-c", os.path.join(CSRC, "intattn_kernels.hip"), "-o", kern_obj])
+    cmds, objs = [], []
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD_DIR, src.rsplit(".", 1)[0] + ".o")
+        cmds.append([cxx] + HOST_FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD_DIR, src.rsplit(".", 1)[0] + ".o")
+        cmds.append([HIPCC] + HIP_FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        list(ex.map(_run, cmds))
     tmp = LIB_PATH + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", host_obj, kern_obj, "-o", tmp])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp])
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -1,0 +1,223 @@
+// Decode integer attention kernel (gfx950 / CDNA4): one query row per head,
+// keys and values streamed once from HBM.
+//
+// Method: IntAttention digest pages (arXiv 2511.21513v1), "Methodology",
+// steps 2-3; integer widths and roundings as stated in include/intattn.h.
+#include "ia_device.h"
+
+namespace ia {
+namespace {
+
+// Largest key count served by the decode kernel (5 bytes of LDS per key).
+constexpr int kDecodeMaxKeys = 16384;
+
+// Decode kernel: one query row per head (Sq = 1), keys streamed from HBM.
+// One workgroup (4 waves) per (b, h). D/16 consecutive lanes cover one key
+// row with 16-byte loads (fully coalesced); each lane handles 4 keys.
+//   A: scores s_j = q . k_j: four sdot4 per 16 bytes, then a butterfly over
+//      the D/16 lanes of a row (DPP), scores kept in LDS (int32 per key);
+//   B: row max (wave reduction + LDS);
+//   C: slots, table lookups and row sum; the scores' LDS words are reused
+//      for the slots; then p_j for every key (one 32-entry table per row);
+//   D: P.V: each lane transposes its 4 keys x 16 value columns (v_perm) and
+//      accumulates udot4(p, v + 128) (adding 128 to a signed byte = XOR 0x80),
+//      so a_d = sum_j p_j v_jd = acc_d - 128 * sum_j p_j; lanes and waves are
+//      then reduced and the result requantised.
+// HBM traffic is one read of K and V; the LDS holds 5 bytes per key.
+constexpr int kDecodeThreads = 256;
+
+
+template <int D>
+__global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
+    const int8_t* __restrict__ q, const int8_t* __restrict__ k, const int8_t* __restrict__ v,
+    int8_t* __restrict__ out, const IaKernelParams P, int skv_pad, int32_t* __restrict__ row_max,
+    uint32_t* __restrict__ row_sum) {
+    constexpr int CPR = D / 16;                 // lanes per key row
+    constexpr int GPW = 64 / CPR;               // key groups (of 4 keys) per wave
+    constexpr int KEYS_IT = 4 * GPW * (kDecodeThreads / 64);   // keys per iteration
+    extern __shared__ __attribute__((aligned(16))) int32_t dsm[];
+    int32_t* s_score = dsm;                                     // skv_pad ints (scores, then slots)
+    uint8_t* s_p = reinterpret_cast<uint8_t*>(dsm + skv_pad);   // skv_pad bytes
+    __shared__ uint32_t s_lut[32];
+    __shared__ int32_t s_red[4][D];
+    __shared__ int32_t s_scal[8];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int c = lane % CPR;                   // 16-byte column chunk
+    const int g = lane / CPR;                   // key group within the wave
+    const size_t head = blockIdx.x;
+    const int8_t* kh = k + head * P.Skv * D;
+    const int8_t* vh = v + head * P.Skv * D;
+    const v4i qv = *reinterpret_cast<const v4i*>(q + head * D + 16 * c);
+    if (tid < 32) s_lut[tid] = lut_entry(P, tid);
+
+    // ---- A: scores ---------------------------------------------------------
+    int32_t tmax = INT_MIN;
+    for (int base = 0; base < P.Skv; base += 2 * KEYS_IT) {
+        v4i kr[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = base + u * KEYS_IT + wave * 4 * GPW + 4 * g + i;
+                kr[u][i] = v4i{0, 0, 0, 0};
+                if (key < P.Skv) kr[u][i] = *reinterpret_cast<const v4i*>(kh + static_cast<size_t>(key) * D + 16 * c);
+            }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                int32_t sc = __builtin_amdgcn_sdot4(kr[u][i][0], qv[0], 0, false);
+                sc = __builtin_amdgcn_sdot4(kr[u][i][1], qv[1], sc, false);
+                sc = __builtin_amdgcn_sdot4(kr[u][i][2], qv[2], sc, false);
+                sc = __builtin_amdgcn_sdot4(kr[u][i][3], qv[3], sc, false);
+                sc += dpp_xor1(sc);
+                sc += dpp_xor2(sc);
+                if (CPR == 8) sc += dpp_half_mirror(sc);
+                const int key = base + u * KEYS_IT + wave * 4 * GPW + 4 * g + i;
+                if (key < P.Skv) {
+                    tmax = max(tmax, sc);
+                    if (c == i) s_score[key] = sc;
+                }
+            }
+    }
+    // ---- B: row max ----------------------------------------------------------
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tmax = max(tmax, __shfl_xor(tmax, off));
+    if (lane == 0) s_scal[wave] = tmax;
+    __syncthreads();
+    const int32_t m = max(max(s_scal[0], s_scal[1]), max(s_scal[2], s_scal[3]));
+    const int32_t lo = m - P.x_clip;
+    const uint32_t Cm = static_cast<uint32_t>(m) * static_cast<uint32_t>(P.idx_mul) + (1u << 23);
+    const int32_t negM = -P.idx_mul;
+
+    // ---- C: slots and row sum, then probabilities ------------------------------
+    uint32_t E = 0;
+    for (int j = tid; j < P.Skv; j += kDecodeThreads) {
+        const int32_t sp = max(s_score[j], lo);
+        const uint32_t slot = (Cm + static_cast<uint32_t>(__mul24(sp, negM))) >> 24;
+        E += s_lut[slot];
+        s_score[j] = static_cast<int32_t>(slot);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) E += __shfl_xor(E, off);
+    __syncthreads();
+    if (lane == 0) s_scal[4 + wave] = static_cast<int32_t>(E);
+    __syncthreads();
+    E = static_cast<uint32_t>(s_scal[4]) + static_cast<uint32_t>(s_scal[5]) +
+        static_cast<uint32_t>(s_scal[6]) + static_cast<uint32_t>(s_scal[7]);
+    const uint32_t R = ((255u << 23) + (E >> 1)) / E;
+    if (row_max != nullptr && tid == 0) {
+        row_max[head] = m;
+        row_sum[head] = E;
+    }
+    uint32_t psum = 0;
+    for (int j = tid; j < skv_pad; j += kDecodeThreads) {
+        uint32_t p = 0;
+        if (j < P.Skv) p = (s_lut[s_score[j]] * R + (1u << 22)) >> 23;
+        s_p[j] = static_cast<uint8_t>(p);
+        psum += p;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) psum += __shfl_xor(psum, off);
+    __syncthreads();
+    if (lane == 0) s_scal[wave] = static_cast<int32_t>(psum);
+    __syncthreads();
+    psum = static_cast<uint32_t>(s_scal[0]) + static_cast<uint32_t>(s_scal[1]) +
+           static_cast<uint32_t>(s_scal[2]) + static_cast<uint32_t>(s_scal[3]);
+
+    // ---- D: P.V ----------------------------------------------------------------
+    uint32_t acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0;
+    for (int base = 0; base < P.Skv; base += 2 * KEYS_IT) {
+        v4i vr[2][4];
+        uint32_t pk[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int key0 = base + u * KEYS_IT + wave * 4 * GPW + 4 * g;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vr[u][i] = v4i{0, 0, 0, 0};
+                if (key0 + i < P.Skv)
+                    vr[u][i] = *reinterpret_cast<const v4i*>(vh + static_cast<size_t>(key0 + i) * D + 16 * c);
+            }
+            pk[u] = key0 < skv_pad ? *reinterpret_cast<const uint32_t*>(s_p + key0) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t r0 = static_cast<uint32_t>(vr[u][0][w]) ^ 0x80808080u;
+                const uint32_t r1 = static_cast<uint32_t>(vr[u][1][w]) ^ 0x80808080u;
+                const uint32_t r2 = static_cast<uint32_t>(vr[u][2][w]) ^ 0x80808080u;
+                const uint32_t r3 = static_cast<uint32_t>(vr[u][3][w]) ^ 0x80808080u;
+                const uint32_t u0 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);
+                const uint32_t u1 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);
+                const uint32_t u2 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+                const uint32_t u3 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+                acc[4 * w + 0] = __builtin_amdgcn_udot4(__builtin_amdgcn_perm(u2, u0, 0x05040100u), pk[u], acc[4 * w + 0], false);
+                acc[4 * w + 1] = __builtin_amdgcn_udot4(__builtin_amdgcn_perm(u2, u0, 0x07060302u), pk[u], acc[4 * w + 1], false);
+                acc[4 * w + 2] = __builtin_amdgcn_udot4(__builtin_amdgcn_perm(u3, u1, 0x05040100u), pk[u], acc[4 * w + 2], false);
+                acc[4 * w + 3] = __builtin_amdgcn_udot4(__builtin_amdgcn_perm(u3, u1, 0x07060302u), pk[u], acc[4 * w + 3], false);
+            }
+    }
+    // lanes with the same column chunk (stride CPR) hold partial sums
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int off = CPR; off < 64; off <<= 1) acc[i] += __shfl_xor(acc[i], off);
+    }
+    if (g == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s_red[wave][16 * c + i] = static_cast<int32_t>(acc[i]);
+    }
+    __syncthreads();
+    for (int d = tid; d < D; d += kDecodeThreads) {
+        const uint32_t tot = static_cast<uint32_t>(s_red[0][d]) + static_cast<uint32_t>(s_red[1][d]) +
+                             static_cast<uint32_t>(s_red[2][d]) + static_cast<uint32_t>(s_red[3][d]);
+        out[head * D + d] = requantise(static_cast<int32_t>(tot - 128u * psum), P);
+    }
+}
+
+// Largest key count served by the decode kernel (5 bytes of LDS per key).
+
+}  // namespace
+
+int decode_max_keys() { return kDecodeMaxKeys; }
+
+int launch_decode(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
+                  const IaKernelParams& kp, void* stream_v, int32_t* row_max, uint32_t* row_sum) {
+    const hipStream_t stream = static_cast<hipStream_t>(stream_v);
+    const long long blocks = static_cast<long long>(kp.B) * kp.H;
+    if (blocks > INT_MAX) return INTATTN_E_SHAPE;
+    const int skv_pad = (kp.Skv + 255) / 256 * 256;
+    const size_t shm = static_cast<size_t>(skv_pad) * 5;
+    if (D == 64) {
+        static bool attr64 = false;
+        if (!attr64) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_decode_kernel<64>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, 5 * kDecodeMaxKeys) != hipSuccess)
+                return INTATTN_E_HIP;
+            attr64 = true;
+        }
+        hipLaunchKernelGGL((ia_decode_kernel<64>), dim3(static_cast<unsigned>(blocks)), dim3(kDecodeThreads), shm,
+                           stream, q, k, v, out, kp, skv_pad, row_max, row_sum);
+    } else {
+        static bool attr128 = false;
+        if (!attr128) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_decode_kernel<128>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, 5 * kDecodeMaxKeys) != hipSuccess)
+                return INTATTN_E_HIP;
+            attr128 = true;
+        }
+        hipLaunchKernelGGL((ia_decode_kernel<128>), dim3(static_cast<unsigned>(blocks)), dim3(kDecodeThreads), shm,
+                           stream, q, k, v, out, kp, skv_pad, row_max, row_sum);
+    }
+    return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
+}
+
+
+}  // namespace ia

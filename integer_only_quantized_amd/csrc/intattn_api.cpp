@@ -1,0 +1,78 @@
+// C-ABI entry points of the integer attention library: argument checks,
+// host parameter derivation and the choice of device kernel.
+//
+// Kernel choice (all bit-identical to the specification in include/intattn.h):
+//   Sq == 1 and Skv <= 16384                -> decode kernel (HBM streaming)
+//   Skv <= 512 (d = 64) or 256 (d = 128)      -> short-row kernel (K/V in LDS)
+//   otherwise                                -> long-row kernel (tiled, 3 passes)
+// intattn_forward_debug with a probability buffer runs the general kernel,
+// which is the only one that materialises P.
+#include <climits>
+#include <cstdint>
+
+#include "intattn.h"
+#include "intattn_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int prepare(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
+            const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
+            IaKernelParams* kp) {
+    if (!q || !k || !v || !out || !shape || !scales) return INTATTN_E_NULL;
+    int st = intattn_validate_shape(shape, causal);
+    if (st != INTATTN_OK) return st;
+    if (shape->D != 64 && shape->D != 128) return INTATTN_E_DIM;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return INTATTN_E_ALIGN;
+    intattn_params prm;
+    st = intattn_derive_params(shape, scales, clip, &prm);
+    if (st != INTATTN_OK) return st;
+    kp->B = shape->B;
+    kp->H = shape->H;
+    kp->Sq = shape->Sq;
+    kp->Skv = shape->Skv;
+    kp->causal = causal ? 1 : 0;
+    kp->idx_mul = prm.idx_mul;
+    kp->x_clip = prm.x_clip;
+    kp->req_shift = prm.req_shift;
+    kp->req_mul = static_cast<uint32_t>(prm.req_mul);
+    for (int i = 0; i < 16; ++i)
+        kp->lut2[i] = static_cast<uint32_t>(prm.lut[2 * i]) | (static_cast<uint32_t>(prm.lut[2 * i + 1]) << 16);
+    return INTATTN_OK;
+}
+
+int dispatch(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
+             const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum) {
+    if (kp.Sq == 1 && kp.Skv <= ia::decode_max_keys())
+        return ia::launch_decode(q, k, v, out, D, kp, stream, row_max, row_sum);
+    if (kp.Skv <= ia::short_max_keys(D))
+        return ia::launch_short(q, k, v, out, D, kp, stream, row_max, row_sum);
+    return ia::launch_long(q, k, v, out, D, kp, stream, row_max, row_sum);
+}
+
+}  // namespace
+
+extern "C" int intattn_forward(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
+                               const intattn_shape* shape, const intattn_scales* scales, float clip,
+                               int causal, void* stream) {
+    IaKernelParams kp;
+    const int st = prepare(q, k, v, out, shape, scales, clip, causal, &kp);
+    if (st != INTATTN_OK) return st;
+    if (static_cast<long long>(kp.B) * kp.H * kp.Sq == 0) return INTATTN_OK;
+    return dispatch(q, k, v, out, shape->D, kp, stream, nullptr, nullptr);
+}
+
+extern "C" int intattn_forward_debug(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
+                                     const intattn_shape* shape, const intattn_scales* scales, float clip,
+                                     int causal, void* stream, int32_t* row_max, uint32_t* row_sum,
+                                     uint8_t* probs) {
+    if (!row_max || !row_sum) return INTATTN_E_NULL;
+    IaKernelParams kp;
+    const int st = prepare(q, k, v, out, shape, scales, clip, causal, &kp);
+    if (st != INTATTN_OK) return st;
+    if (static_cast<long long>(kp.B) * kp.H * kp.Sq == 0) return INTATTN_OK;
+    if (probs != nullptr)
+        return ia::launch_general(q, k, v, out, shape->D, kp, stream, row_max, row_sum, probs);
+    return dispatch(q, k, v, out, shape->D, kp, stream, row_max, row_sum);
+}

@@ -1,5 +1,6 @@
-// Declarations shared by the host derivation and the HIP launchers of the
-// integer attention library (not part of the public C ABI).
+// Declarations shared by the host code and the HIP launchers of the integer
+// attention library (not part of the public C ABI). Host-only types: the
+// HIP stream travels as void* so this header needs no HIP headers.
 #pragma once
 
 #include <cstdint>
@@ -20,3 +21,30 @@ struct IaKernelParams {
     uint32_t req_mul;    // M_o, in [2^30, 2^31)
     uint32_t lut2[16];   // exp table, entries 2i and 2i+1 packed lo/hi
 };
+
+namespace ia {
+
+// Each launcher queues one kernel on `stream` (a hipStream_t) and returns
+// INTATTN_OK or INTATTN_E_HIP / INTATTN_E_SHAPE. row_max / row_sum are
+// optional per-row outputs [B, H, Sq] (both NULL or both set).
+
+// Any shape; also writes the probabilities [B, H, Sq, Skv] when probs != NULL.
+int launch_general(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
+                   const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum,
+                   uint8_t* probs);
+
+// Skv <= short_max_keys(D): K and V of a head resident in LDS.
+int short_max_keys(int D);
+int launch_short(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
+                 const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum);
+
+// Sq == 1 and Skv <= decode_max_keys(): one head per workgroup, HBM streaming.
+int decode_max_keys();
+int launch_decode(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
+                  const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum);
+
+// Any shape (used for long rows): K/V tiles streamed through LDS, three passes.
+int launch_long(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
+                const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum);
+
+}  // namespace ia
