@@ -36,9 +36,41 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 
 DEFAULT_STEPS = {"tiny": 2000, "bert": 500, "vit": 500, "llama_prefill": 50, "decode": 100}
 BOUND = {"tiny": "mfma", "bert": "mfma", "vit": "mfma", "llama_prefill": "mfma", "decode": "hbm"}
-KERNEL_NAME = {"tiny": "ia_general_kernel<64>", "bert": "ia_general_kernel<64>",
-               "vit": "ia_general_kernel<64>", "llama_prefill": "ia_general_kernel<128>",
-               "decode": "ia_general_kernel<128>"}
+# kernel the library dispatches for each workload, and its source file
+KERNEL = {"tiny": ("ia_short_kernel", "ia_short.hip"), "bert": ("ia_short_kernel", "ia_short.hip"),
+          "vit": ("ia_short_kernel", "ia_short.hip"), "llama_prefill": ("ia_long_kernel", "ia_long.hip"),
+          "decode": ("ia_decode_kernel", "ia_decode.hip")}
+
+
+def kernel_source_sha(src: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "integer_only_quantized_amd", "csrc")
+    for f in (src, "ia_device.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when there is none or the kernel source changed since."""
+    kname, src = KERNEL[config]
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kname}_{config}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line:
+                k, _, val = line.partition(":")
+                fields[k.strip()] = val.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_sha(src):
+        return None
+    try:
+        return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def algorithmic_work(w):
@@ -108,9 +140,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the attention heads are independent and "
-              "this build runs no multi-GPU path (see the sharding notes in the design "
-              "document). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: attention heads are independent, so a "
+              "multi-GPU run is the same kernel on each GPU's share of the heads, and this "
+              "library runs on one GPU. Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -157,10 +189,10 @@ def main(argv=None):
     else:
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS}
-    roof["kernel"] = KERNEL_NAME[args.config]
+    roof["kernel"] = KERNEL[args.config][0]
     roof["per_launch"] = {"ops": ops, "bytes": nbytes, "scores": scores,
                           "avg_launch_us": ms_per_step * 1e3}
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(args.config)
 
     cpu = None
     parity = None
@@ -175,8 +207,8 @@ def main(argv=None):
     else:
         metric_value, unit = tops, "TOPS"
     line = {
-        "metric": f"int8 attention throughput ({args.config})" if args.config != "bert"
-        else "int8 attention TOPS (BERT-base S=512)",
+        "metric": "int8 attention TOPS + calls/s (BERT-base S=512) and decode GB/s; % of roofline"
+        if args.config == "bert" else f"int8 attention throughput ({args.config})",
         "value": metric_value,
         "unit": unit,
         "n_gpus": 1,
