@@ -40,6 +40,10 @@ def _run(cmd):
 
 HOST_SOURCES = ["intattn_host.cpp", "intattn_api.cpp"]
 HIP_SOURCES = ["ia_general.hip", "ia_short.hip", "ia_long.hip", "ia_decode.hip"]
+# Per-source code-generation options: the long-row kernel keeps its MFMA
+# accumulators in ordinary VGPRs (no accumulator-register copies when the
+# scores are post-processed on the VALU).
+HIP_EXTRA = {"ia_long.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = True, jobs: int = 8) -> str:
@@ -56,7 +60,7 @@ def build(verbose: bool = True, jobs: int = 8) -> str:
         objs.append(obj)
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src.rsplit(".", 1)[0] + ".o")
-        cmds.append([HIPCC] + HIP_FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC] + HIP_FLAGS + HIP_EXTRA.get(src, []) + inc + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         list(ex.map(_run, cmds))

@@ -1,6 +1,7 @@
 // Long-row integer attention kernel (gfx950 / CDNA4): key/value tiles
-// streamed through LDS, three exact passes per query block. Used for rows
-// longer than the short-row kernel holds (e.g. causal prefill at S = 4096).
+// streamed into LDS by asynchronous global->LDS loads, three exact passes per
+// query block. Used for rows longer than the short-row kernel holds (e.g.
+// causal prefill at S = 4096).
 //
 // Method: IntAttention digest pages (arXiv 2511.21513v1), "Methodology",
 // steps 2-3; integer widths and roundings as stated in include/intattn.h.
@@ -9,25 +10,37 @@
 //   * one workgroup = 4 waves = 128 query rows of one (b, h); each wave owns
 //     32 rows, holds their Q fragments, and produces S^T blocks (32 keys x
 //     32 queries) on v_mfma_i32_32x32x32_i8, so each lane holds one row;
-//   * keys arrive in tiles of 64 rows, double-buffered in LDS: the next
-//     tile's global loads are issued into registers before the current
-//     tile is computed and written to the other buffer afterwards (one
-//     barrier per tile);
+//   * keys and values arrive in tiles of 64 rows through a three-stage LDS
+//     ring filled by global_load_lds_dwordx4 (no register staging): tile
+//     t+2 is requested while tile t is computed, and only tile t+1 is
+//     waited for (s_waitcnt vmcnt) before the per-tile barrier;
+//   * LDS reads are bank-conflict free on the 64-bank LDS (16 lanes per
+//     cycle for 16-byte reads): K rows have their 16-byte chunks XOR-swizzled
+//     by the row; V rows stay row-major (chunks swizzled by the key) and the
+//     P.V B operand (16 keys of one value column) comes from two
+//     ds_read_b64_tr_b8 transpose reads;
 //   * the row max must be known before any slot and the row sum before any
 //     probability, so there are three passes over the tiles with Q.K^T
 //     recomputed in each: (1) row max; (2) the MFMA accumulator is seeded
-//     with -m, so it yields s - m directly, from which the slot and the
-//     table entry follow, summed into E; (3) the same slot indexes a per-row
-//     table of the 32 probabilities (stored as p - 128), which is the P
-//     operand of P.V; V^T tiles are column-summed on the side for the
-//     +128 * colsum(V) correction;
-//   * causal workgroups are dispatched heaviest first (the last query
-//     blocks have the most keys), and when the head count allows, every XCD
-//     owns a fixed subset of heads so their K/V stay in its L2.
-// Slot forms: with y = s - m <= 0, if 4M < 2^23 the slot comes from a
-// saturating multiply-add (the clip is free, slot bits 26..30, byte 3 =
-// 4*slot + fraction); otherwise y is first clipped at -x_clip and the slot
-// lands in byte 3 directly. The per-row table layout follows the form.
+//     with -m, so it yields y = s - m directly; a clamped 24-bit
+//     multiply-add turns y into the slot word, whose top byte addresses the
+//     shared exp table; the entries are summed into E; (3) the same table
+//     entry e gives the probability byte arithmetically: the top byte of
+//     e * 2R + 2^23 + 2^31 (mod 2^32) is p XOR 0x80, i.e. p - 128 as int8,
+//     which is the P operand of P.V. The +128 * colsum(V) correction is
+//     summed from the same B operands, each tile by one wave in turn;
+//   * rows past Skv read in-bounds bytes of the last valid row; their scores
+//     are masked to p = 0, and since colsum covers exactly the rows fed,
+//     their values cancel: sum (p - 128) v + 128 sum v = sum p v;
+//   * causal workgroups are dispatched heaviest first, and when the head
+//     count allows, every XCD owns a fixed subset of heads (L2 locality).
+// Slot word, y = s - m in [-2^23, 0]:
+//   4M < 2^23: t = sat(y * -4M + 2^25); byte 3 = 4 * slot + fraction, and
+//              saturation lands in slot 31 (table address: byte 3 & 0x7c);
+//   otherwise: t = sat(y * -M + 2^23); byte 3 = min(127, raw slot), and the
+//              table has 128 entries with entries 31..127 equal to zero.
+#include <type_traits>
+
 #include "ia_device.h"
 
 namespace ia {
@@ -36,18 +49,57 @@ namespace {
 constexpr int kLongWaves = 4;
 constexpr int kLongRows = 32 * kLongWaves;   // query rows per workgroup
 constexpr int kLongTile = 64;                // keys per tile
+constexpr int kStages = 3;                   // LDS ring depth
+constexpr int kLutEntries = 128;
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int D>
 struct LongLds {
-    static constexpr int KStride = D + 16;          // padded K row (conflict-free 16-byte reads)
-    static constexpr int VStride = kLongTile + 16;  // padded V^T row
-    static constexpr int PTRow = 132;               // per-row table: up to 128 entries + pad
-    uint32_t lut[32];                               // first member: LDS byte address 0
-    int32_t colsum[D];
-    int8_t k[2][kLongTile * KStride];
-    int8_t vt[2][D * VStride];
-    uint8_t ptab[kLongWaves * 32 * PTRow];
+    static constexpr int TB = kLongTile * D;        // bytes per K or V tile
+    uint32_t lut[kLutEntries];                      // first member: LDS byte address 0
+    int32_t colsum[kLongWaves][D];
+    int8_t k[kStages][TB];
+    int8_t v[kStages][TB];
 };
+
+// 16-byte chunk position of logical chunk c of K row r: the 16 rows read by
+// one 16-lane phase land in 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+    return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+// Chunk position of logical chunk c of V row (key) r: the 8 keys of one
+// transpose read land in 8 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+    return D == 128 ? ((r & 3) | ((r >> 1) & 4)) : (((r >> 1) & 1) | ((r >> 2) & 2));
+}
+
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    // s_waitcnt with only the vector-memory counter constrained (lgkm/exp at max)
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
+// Workgroup barrier for the LDS ring: this wave's LDS operations complete,
+// then all waves meet. Outstanding global->LDS loads are not waited for here
+// (the caller waits for exactly the tile it needs with wait_vmcnt first).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 32-bit LDS load from a byte address (the kernel's LDS block starts at 0).
+__device__ __forceinline__ uint32_t lds_u32(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(static_cast<uintptr_t>(addr));
+}
 
 template <int D, bool FAST>
 __global__ __launch_bounds__(256) void ia_long_kernel(
@@ -57,18 +109,14 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     using L = LongLds<D>;
     constexpr int KS = D / 32;
     constexpr int DB = D / 32;
-    constexpr int KStride = L::KStride;
-    constexpr int VStride = L::VStride;
-    constexpr int KCH = kLongTile * D / 16 / 256;           // 16-byte K chunks per thread per tile
-    constexpr int VITEMS = (kLongTile / 4) * (D / 16);      // V items (4 keys x 16 columns) per tile
-    constexpr int CS_PARTS = 256 / D;                       // threads per column sum
-    constexpr int CS_DW = kLongTile / 4 / CS_PARTS;         // dwords of a V^T row per thread
-
-    __shared__ __attribute__((aligned(16))) L lds;
+    constexpr int CPR = D / 16;                              // 16-byte chunks per row
+    constexpr int LOADS = L::TB / 1024 / kLongWaves;          // 1 KB load instructions per wave per tile
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+    L& lds = *reinterpret_cast<L*>(lds_raw);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int hh = lane >> 5;
 
@@ -103,7 +151,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     const int kend_wg = P.causal ? min(P.Skv, qlast + shift + 1) : P.Skv;
     const int ntiles = (kend_wg + kLongTile - 1) / kLongTile;
 
-    if (tid < 32) lds.lut[tid] = lut_entry(P, tid);
+    if (tid < kLutEntries) lds.lut[tid] = tid < 32 ? lut_entry(P, tid) : 0u;
 
     v4i qf[KS];
 #pragma unroll
@@ -114,61 +162,39 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
             qf[ks] = v4i{0, 0, 0, 0};
     }
 
-    // ---- tile staging ----------------------------------------------------------
-    auto load_k = [&](int t, v4i (&kr)[KCH]) {
+    // ---- asynchronous tile loads -------------------------------------------
+    // Wave w, instruction i fills LDS bytes [(w*LOADS + i) KB, +1 KB) of the
+    // stage; lane l writes 16 bytes at l*16, i.e. row (1 KB offset)/D + l/CPR,
+    // stored chunk l % CPR, which holds logical chunk (l % CPR) ^ swizzle(row).
+    // Per-lane source offsets within a tile are fixed; a tile adds t*64*D.
+    uint32_t koff[LOADS], voff[LOADS];
 #pragma unroll
-        for (int u = 0; u < KCH; ++u) {
-            const int c = u * 256 + tid;
-            const int row = c / (D / 16), ch = c % (D / 16);
-            const int key = t * kLongTile + row;
-            kr[u] = v4i{0, 0, 0, 0};
-            if (key < P.Skv) kr[u] = *reinterpret_cast<const v4i*>(kh + static_cast<size_t>(key) * D + 16 * ch);
-        }
-    };
-    auto store_k = [&](int buf, const v4i (&kr)[KCH]) {
+    for (int i = 0; i < LOADS; ++i) {
+        const int row = (wave * LOADS + i) * (1024 / D) + lane / CPR;
+        const int pos = lane % CPR;
+        koff[i] = static_cast<uint32_t>(row * D + 16 * (pos ^ k_swz<D>(row)));
+        voff[i] = static_cast<uint32_t>(row * D + 16 * (pos ^ v_swz<D>(row)));
+    }
+    auto issue = [&](const int8_t* src, int8_t* dst, const uint32_t (&off)[LOADS], int t) {
+        const int8_t* base = src + static_cast<size_t>(t) * kLongTile * D;
+        const bool tail = (t + 1) * kLongTile > P.Skv;
+        const uint32_t lim = static_cast<uint32_t>((P.Skv - t * kLongTile) * D - 16);
 #pragma unroll
-        for (int u = 0; u < KCH; ++u) {
-            const int c = u * 256 + tid;
-            const int row = c / (D / 16), ch = c % (D / 16);
-            *reinterpret_cast<v4i*>(&lds.k[buf][row * KStride + 16 * ch]) = kr[u];
-        }
-    };
-    auto load_v = [&](int t, v4i (&vr)[4]) {
-        const int dc = tid % (D / 16), key0 = t * kLongTile + 4 * (tid / (D / 16));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            vr[i] = v4i{0, 0, 0, 0};
-            if (tid < VITEMS && key0 + i < P.Skv)
-                vr[i] = *reinterpret_cast<const v4i*>(vh + static_cast<size_t>(key0 + i) * D + 16 * dc);
-        }
-    };
-    auto store_vt = [&](int buf, const v4i (&vr)[4]) {
-        if (tid >= VITEMS) return;
-        const int dc = tid % (D / 16), kt = 4 * (tid / (D / 16));   // key within the tile
-        const int pos = 32 * (kt >> 5) + vt_pos(kt & 31);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            // 4x4 byte transpose: keys kt..kt+3, value columns 16dc+4w..+3
-            const uint32_t r0 = vr[0][w], r1 = vr[1][w], r2 = vr[2][w], r3 = vr[3][w];
-            const uint32_t u0 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);
-            const uint32_t u1 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);
-            const uint32_t u2 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
-            const uint32_t u3 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
-            const int d0 = 16 * dc + 4 * w;
-            int8_t* vt = lds.vt[buf];
-            *reinterpret_cast<uint32_t*>(&vt[(d0 + 0) * VStride + pos]) = __builtin_amdgcn_perm(u2, u0, 0x05040100u);
-            *reinterpret_cast<uint32_t*>(&vt[(d0 + 1) * VStride + pos]) = __builtin_amdgcn_perm(u2, u0, 0x07060302u);
-            *reinterpret_cast<uint32_t*>(&vt[(d0 + 2) * VStride + pos]) = __builtin_amdgcn_perm(u3, u1, 0x05040100u);
-            *reinterpret_cast<uint32_t*>(&vt[(d0 + 3) * VStride + pos]) = __builtin_amdgcn_perm(u3, u1, 0x07060302u);
+        for (int i = 0; i < LOADS; ++i) {
+            // rows past Skv: any in-bounds bytes (masked, and cancelled by colsum)
+            const uint32_t o = tail ? min(off[i], lim) : off[i];
+            __builtin_amdgcn_global_load_lds(base + o, (lds_void_t*)(dst + (wave * LOADS + i) * 1024), 16, 0, 0);
         }
     };
 
-    // S^T block kb (0 or 1) of the tile in LDS buffer buf, from accumulator c0
-    auto scores = [&](int buf, int kb, const v16i& c0) {
+    // S^T block kb (0 or 1) of the K tile in stage st, from accumulator c0
+    auto scores = [&](int st, int kb, const v16i& c0) {
         v16i s = c0;
+        const int r = 32 * kb + l32;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const v4i a = *reinterpret_cast<const v4i*>(&lds.k[buf][(32 * kb + l32) * KStride + 32 * ks + 16 * hh]);
+            const int c = (2 * ks + hh) ^ k_swz<D>(r);
+            const v4i a = *reinterpret_cast<const v4i*>(&lds.k[st][r * D + 16 * c]);
             s = mfma_i8_32x32x32(a, qf[ks], s);
         }
         return s;
@@ -183,27 +209,101 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
         }
     };
 
+    // P.V B operand for key block kb, value columns 32db..32db+31 of the V tile
+    // in a stage: lane (l32, hh) gets V[key(b)][32db + l32] for its 16 keys
+    // key(b) = 32kb + acc_row(b, hh), b = 0..15, via two transpose reads.
+    // Within each 16-lane group, lane pair (2i, 2i+1) supplies the two 8-byte
+    // halves of row key(b) (b = i for the first read, 8 + i for the second);
+    // lane j of the group receives column j of those 8 rows. The addresses
+    // below are for stage 0, key block 0; the stage adds a register offset,
+    // key block 1 the immediate 32*D.
+    uint32_t vaddr[2 * DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+            const int i = (lane & 15) >> 1;
+            const int key = acc_row(8 * rd + i, hh);
+            const int col = 32 * db + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+            const int c = (col >> 4) ^ v_swz<D>(key);
+            vaddr[2 * db + rd] = static_cast<uint32_t>(offsetof(L, v)) + key * D + 16 * c + (col & 15);
+        }
+    }
+    // All 2*DB transpose reads of one key block, waited for in the same asm
+    // statement (the destination registers are final when it ends).
+    auto vfrag_all = [&](const uint32_t (&va)[2 * DB], auto kbc, v4i (&vb)[DB]) {
+        constexpr int OFF = decltype(kbc)::value * 32 * D;
+        v2i r[2 * DB];
+        if constexpr (DB == 4) {
+            asm volatile(
+                "ds_read_b64_tr_b8 %0, %8 offset:%16\n\t"
+                "ds_read_b64_tr_b8 %1, %9 offset:%16\n\t"
+                "ds_read_b64_tr_b8 %2, %10 offset:%16\n\t"
+                "ds_read_b64_tr_b8 %3, %11 offset:%16\n\t"
+                "ds_read_b64_tr_b8 %4, %12 offset:%16\n\t"
+                "ds_read_b64_tr_b8 %5, %13 offset:%16\n\t"
+                "ds_read_b64_tr_b8 %6, %14 offset:%16\n\t"
+                "ds_read_b64_tr_b8 %7, %15 offset:%16\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+                  "=&v"(r[7])
+                : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]),
+                  "i"(OFF));
+        } else {
+            asm volatile(
+                "ds_read_b64_tr_b8 %0, %4 offset:%8\n\t"
+                "ds_read_b64_tr_b8 %1, %5 offset:%8\n\t"
+                "ds_read_b64_tr_b8 %2, %6 offset:%8\n\t"
+                "ds_read_b64_tr_b8 %3, %7 offset:%8\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+                : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "i"(OFF));
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            vb[db] = v4i{r[2 * db][0], r[2 * db][1], r[2 * db + 1][0], r[2 * db + 1][1]};
+    };
+
+    auto run_tiles = [&](bool with_v, auto&& body) {
+        // prologue: tiles 0 and 1 requested, tile 0 waited for
+        const int per_tile = with_v ? 2 * LOADS : LOADS;
+        wait_vmcnt(0);                       // nothing else in flight when counting
+        issue(kh, lds.k[0], koff, 0);
+        if (with_v) issue(vh, lds.v[0], voff, 0);
+        if (ntiles > 1) {
+            issue(kh, lds.k[1], koff, 1);
+            if (with_v) issue(vh, lds.v[1], voff, 1);
+            wait_vmcnt(per_tile);
+        } else {
+            wait_vmcnt(0);
+        }
+        lds_barrier();
+        for (int t = 0; t < ntiles; ++t) {
+            const int st = t % kStages;
+            if (t + 2 < ntiles) {
+                const int st2 = (t + 2) % kStages;
+                issue(kh, lds.k[st2], koff, t + 2);
+                if (with_v) issue(vh, lds.v[st2], voff, t + 2);
+            }
+            body(t, st);
+            // tile t+1 must have landed; tile t+2 may stay in flight
+            if (t + 2 < ntiles) wait_vmcnt(per_tile);
+            else wait_vmcnt(0);
+            lds_barrier();
+        }
+    };
+
     // ---- pass 1: row max ---------------------------------------------------
     const v16i zero16 = v16i{};
     int32_t mrow = INT_MIN;
-    {
-        v4i kr[KCH];
-        load_k(0, kr);
-        store_k(0, kr);
-        __syncthreads();
-        for (int t = 0; t < ntiles; ++t) {
-            const int buf = t & 1;
-            if (t + 1 < ntiles) load_k(t + 1, kr);
-            v16i s0 = scores(buf, 0, zero16);
-            v16i s1 = scores(buf, 1, zero16);
-            mask(s0, t * kLongTile, INT_MIN);
-            mask(s1, t * kLongTile + 32, INT_MIN);
+    run_tiles(false, [&](int t, int st) {
+        v16i s0 = scores(st, 0, zero16);
+        v16i s1 = scores(st, 1, zero16);
+        mask(s0, t * kLongTile, INT_MIN);
+        mask(s1, t * kLongTile + 32, INT_MIN);
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) mrow = max(mrow, max(max(s0[r], s0[r + 1]), max(s1[r], s1[r + 1])));
-            if (t + 1 < ntiles) store_k(buf ^ 1, kr);
-            __syncthreads();
-        }
-    }
+        for (int r = 0; r < 16; r += 2) mrow = max(mrow, max(max(s0[r], s0[r + 1]), max(s1[r], s1[r + 1])));
+    });
     mrow = max(mrow, __shfl_xor(mrow, 32));
 
     // row constants of the slot arithmetic
@@ -212,150 +312,120 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     for (int r = 0; r < 16; ++r) cinit[r] = -mrow;
     const int32_t negMs = FAST ? -4 * P.idx_mul : -P.idx_mul;
     const int32_t halfs = FAST ? (1 << 25) : (1 << 23);
-    const int32_t ylo = -P.x_clip;
-    // byte 3 of the slot word: 4*slot + fraction (FAST) or slot
-    auto slot_word = [&](int32_t y) -> uint32_t {
-        if constexpr (FAST) {
-            return slot_word_sat(y, negMs, halfs);
-        } else {
-            return static_cast<uint32_t>(__mul24(max(y, ylo), negMs) + halfs);
-        }
-    };
-    // byte address of the table entry of the slot (32 u32 entries at LDS 0)
+    // table byte address of the slot word
     auto lut_addr = [&](uint32_t t) -> uint32_t {
         if constexpr (FAST) return (t >> 24) & 0x7cu;
-        else return (t >> 24) << 2;
+        else return (t >> 22) & 0x1fcu;
     };
-    const int32_t ymask = FAST ? -(1 << 23) : INT_MIN / 2;
+    auto table_entry = [&](int32_t y) -> uint32_t { return lds_u32(lut_addr(slot_word_sat(y, negMs, halfs))); };
+    constexpr int32_t kMasked = -(1 << 23);   // y of a masked key: saturates to the last slot
 
     // ---- pass 2: row sum of the table entries ------------------------------
     uint32_t E = 0;
-    {
-        v4i kr[KCH];
-        load_k(0, kr);
-        store_k(0, kr);
-        __syncthreads();
-        for (int t = 0; t < ntiles; ++t) {
-            const int buf = t & 1;
-            if (t + 1 < ntiles) load_k(t + 1, kr);
-            v16i s0 = scores(buf, 0, cinit);
-            v16i s1 = scores(buf, 1, cinit);
-            mask(s0, t * kLongTile, ymask);
-            mask(s1, t * kLongTile + 32, ymask);
-            const uint8_t* lb = reinterpret_cast<const uint8_t*>(&lds);
+    run_tiles(false, [&](int t, int st) {
+        v16i s0 = scores(st, 0, cinit);
+        v16i s1 = scores(st, 1, cinit);
+        mask(s0, t * kLongTile, kMasked);
+        mask(s1, t * kLongTile + 32, kMasked);
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const uint32_t e0 = *reinterpret_cast<const uint32_t*>(lb + lut_addr(slot_word(s0[r])));
-                const uint32_t e1 = *reinterpret_cast<const uint32_t*>(lb + lut_addr(slot_word(s0[r + 1])));
-                const uint32_t e2 = *reinterpret_cast<const uint32_t*>(lb + lut_addr(slot_word(s1[r])));
-                const uint32_t e3 = *reinterpret_cast<const uint32_t*>(lb + lut_addr(slot_word(s1[r + 1])));
-                E += (e0 + e1) + (e2 + e3);
-            }
-            if (t + 1 < ntiles) store_k(buf ^ 1, kr);
-            __syncthreads();
+        for (int r = 0; r < 16; r += 2) {
+            const uint32_t e0 = table_entry(s0[r]);
+            const uint32_t e1 = table_entry(s0[r + 1]);
+            const uint32_t e2 = table_entry(s1[r]);
+            const uint32_t e3 = table_entry(s1[r + 1]);
+            E += (e0 + e1) + (e2 + e3);
         }
-    }
+    });
     E += __shfl_xor(E, 32);
     const uint32_t R = ((255u << 23) + (E >> 1)) / E;
+    const uint32_t R2 = 2 * R;                       // < 2^17
     if (row_max != nullptr && hh == 0 && qrow < P.Sq) {
         row_max[head * P.Sq + qrow] = mrow;
         row_sum[head * P.Sq + qrow] = E;
     }
 
-    // ---- per-row probability table (wave-private) ---------------------------
-    // FAST: entries 4s..4s+3 hold p_s (indexed by 4*slot + fraction);
-    // otherwise entry s holds p_s. Stored as p ^ 0x80 (p - 128 as int8).
-    uint32_t pbase = static_cast<uint32_t>(offsetof(L, ptab)) + (wave * 32 + l32) * L::PTRow;
-    asm volatile("" : "+v"(pbase));
-    uint8_t* const ldsb = reinterpret_cast<uint8_t*>(&lds);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int s = 16 * hh + j;
-        const uint32_t p = ((lds.lut[s] * R + (1u << 22)) >> 23) ^ 0x80u;
-        if constexpr (FAST) {
-            // row bases are multiples of 4 (132-byte rows)
-            *reinterpret_cast<uint32_t*>(ldsb + pbase + 4 * s) = p * 0x01010101u;
-        } else {
-            ldsb[pbase + s] = static_cast<uint8_t>(p);
-        }
-    }
-    if (tid < D) lds.colsum[tid] = 0;
-    __syncthreads();
-
-    // ---- pass 3: P from the tables, P.V on the MFMA --------------------------
+    // ---- pass 3: P from the table, P.V on the MFMA --------------------------
     v16i o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = v16i{};
-    int32_t csacc = 0;                      // this thread's part of a column sum
-    const int cs_d = tid / CS_PARTS, cs_part = tid % CS_PARTS;
-    auto pword = [&](const v16i& s, int w4) -> uint32_t {
-        uint32_t b[4];
+    int32_t cs[DB];                          // this lane's part of the column sums
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t t = slot_word(s[4 * w4 + c]);
-            b[c] = ldsb[pbase + (t >> 24)];
-        }
-        const uint32_t lo2 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
-        const uint32_t hi2 = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
-        return __builtin_amdgcn_perm(hi2, lo2, 0x05040100u);
+    for (int db = 0; db < DB; ++db) cs[db] = 0;
+    // top byte = p ^ 0x80 (p - 128 as int8); e * 2R + 2^23 < 2^32 for e <= E
+    auto pword = [&](int32_t y) -> uint32_t { return __umul24(table_entry(y), R2) + 0x80800000u; };
+    auto pack = [&](const v16i& s, int w4) -> int {
+        const uint32_t w0 = pword(s[4 * w4]), w1 = pword(s[4 * w4 + 1]);
+        const uint32_t w2 = pword(s[4 * w4 + 2]), w3 = pword(s[4 * w4 + 3]);
+        const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x0c0c0703u);
+        const uint32_t hi = __builtin_amdgcn_perm(w3, w2, 0x07030c0cu);
+        return static_cast<int>(lo | hi);
     };
-    {
-        v4i kr[KCH], vr[4];
-        load_k(0, kr);
-        load_v(0, vr);
-        store_k(0, kr);
-        store_vt(0, vr);
-        __syncthreads();
-        for (int t = 0; t < ntiles; ++t) {
-            const int buf = t & 1;
-            if (t + 1 < ntiles) {
-                load_k(t + 1, kr);
-                load_v(t + 1, vr);
-            }
-            // column sums of this V^T tile (every key of the tile is fed)
-            {
-                const int8_t* row = &lds.vt[buf][cs_d * VStride + 4 * CS_DW * cs_part];
+    run_tiles(true, [&](int t, int st) {
+        const bool colsum_turn = (t % kLongWaves) == wave;
+        uint32_t va[2 * DB];
 #pragma unroll
-                for (int j = 0; j < CS_DW; ++j)
-                    csacc = __builtin_amdgcn_sdot4(*reinterpret_cast<const int*>(row + 4 * j), 0x01010101, csacc, false);
-            }
+        for (int i = 0; i < 2 * DB; ++i) va[i] = vaddr[i] + static_cast<uint32_t>(st * L::TB);
+        auto kblock = [&](auto kbc) {
+            constexpr int kb = decltype(kbc)::value;
+            v16i s = scores(st, kb, cinit);
+            mask(s, t * kLongTile + 32 * kb, kMasked);
+            const v4i pa = v4i{pack(s, 0), pack(s, 1), pack(s, 2), pack(s, 3)};
+            v4i vb[DB];
+            vfrag_all(va, kbc, vb);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                v16i s = scores(buf, kb, cinit);
-                mask(s, t * kLongTile + 32 * kb, ymask);
-                const v4i pa = v4i{static_cast<int>(pword(s, 0)), static_cast<int>(pword(s, 1)),
-                                   static_cast<int>(pword(s, 2)), static_cast<int>(pword(s, 3))};
+            for (int db = 0; db < DB; ++db) o[db] = mfma_i8_32x32x32(pa, vb[db], o[db]);
+            if (colsum_turn) {
+                // one wave per tile; the asm keeps the sums from being
+                // computed on every wave and selected afterwards
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const v4i vb = *reinterpret_cast<const v4i*>(&lds.vt[buf][(32 * db + l32) * VStride + 32 * kb + 16 * hh]);
-                    o[db] = mfma_i8_32x32x32(pa, vb, o[db]);
+                    asm volatile("" : "+v"(cs[db]));
+                    cs[db] = __builtin_amdgcn_sdot4(vb[db][0], 0x01010101, cs[db], false);
+                    cs[db] = __builtin_amdgcn_sdot4(vb[db][1], 0x01010101, cs[db], false);
+                    cs[db] = __builtin_amdgcn_sdot4(vb[db][2], 0x01010101, cs[db], false);
+                    cs[db] = __builtin_amdgcn_sdot4(vb[db][3], 0x01010101, cs[db], false);
                 }
             }
-            if (t + 1 < ntiles) {
-                store_k(buf ^ 1, kr);
-                store_vt(buf ^ 1, vr);
-            }
-            __syncthreads();
-        }
-    }
-    // combine the partial column sums of each value column
+        };
+        kblock(std::integral_constant<int, 0>{});
+        kblock(std::integral_constant<int, 1>{});
+    });
+    // column sums: lanes l and l^32 hold the two key halves; waves hold tiles
 #pragma unroll
-    for (int off = 1; off < CS_PARTS; off <<= 1) csacc += __shfl_xor(csacc, off);
-    if (cs_part == 0) lds.colsum[cs_d] = csacc;
+    for (int db = 0; db < DB; ++db) {
+        const int32_t tot = cs[db] + __shfl_xor(cs[db], 32);
+        if (hh == 0) lds.colsum[wave][32 * db + l32] = tot;
+    }
     __syncthreads();
 
     // ---- requantise and store -----------------------------------------------
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
         const int d = 32 * db + l32;
-        const int32_t cs = lds.colsum[d];
+        const int32_t csum = lds.colsum[0][d] + lds.colsum[1][d] + lds.colsum[2][d] + lds.colsum[3][d];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int qi = qw0 + acc_row(r, hh);
             if (qi >= P.Sq) continue;
-            out[(head * P.Sq + qi) * D + d] = requantise(o[db][r] + 128 * cs, P);
+            out[(head * P.Sq + qi) * D + d] = requantise(o[db][r] + 128 * csum, P);
         }
     }
+}
+
+template <int D, bool FAST>
+int launch_long_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, const IaKernelParams& kp,
+                  hipStream_t s, int nqb, unsigned blocks, int32_t* row_max, uint32_t* row_sum) {
+    static bool attr_set = false;
+    const size_t shm = sizeof(LongLds<D>);
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_long_kernel<D, FAST>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)) != hipSuccess)
+            return INTATTN_E_HIP;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((ia_long_kernel<D, FAST>), dim3(blocks), dim3(256), shm, s, q, k, v, out, kp, nqb,
+                       row_max, row_sum);
+    return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
 }
 
 }  // namespace
@@ -365,21 +435,14 @@ int launch_long(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, 
     const int nqb = (kp.Sq + kLongRows - 1) / kLongRows;
     const long long blocks = static_cast<long long>(nqb) * kp.H * kp.B;
     if (blocks > INT_MAX) return INTATTN_E_SHAPE;
-    const dim3 grid(static_cast<unsigned>(blocks)), block(256);
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    const unsigned nb = static_cast<unsigned>(blocks);
     const bool fast = kp.idx_mul < (1 << 21);
-    if (D == 64) {
-        if (fast)
-            hipLaunchKernelGGL((ia_long_kernel<64, true>), grid, block, 0, s, q, k, v, out, kp, nqb, row_max, row_sum);
-        else
-            hipLaunchKernelGGL((ia_long_kernel<64, false>), grid, block, 0, s, q, k, v, out, kp, nqb, row_max, row_sum);
-    } else {
-        if (fast)
-            hipLaunchKernelGGL((ia_long_kernel<128, true>), grid, block, 0, s, q, k, v, out, kp, nqb, row_max, row_sum);
-        else
-            hipLaunchKernelGGL((ia_long_kernel<128, false>), grid, block, 0, s, q, k, v, out, kp, nqb, row_max, row_sum);
-    }
-    return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
+    if (D == 64)
+        return fast ? launch_long_t<64, true>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum)
+                    : launch_long_t<64, false>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
+    return fast ? launch_long_t<128, true>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum)
+                : launch_long_t<128, false>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
 }
 
 }  // namespace ia

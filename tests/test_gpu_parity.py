@@ -142,6 +142,29 @@ def test_scores_on_bin_edges():
     _check_full(w)
 
 
+LARGE_M_CASES = [
+    # (Sq, Skv, D, causal, scale): every kernel family with M >= 2^21, where
+    # the slot is computed from the clipped score instead of the saturating
+    # multiply-add
+    (40, 200, 64, False, 0.5),     # short-row kernel
+    (130, 700, 64, True, 0.5),     # long-row kernel
+    (70, 400, 128, False, 0.6),    # long-row kernel, d = 128
+    (1, 1000, 64, False, 0.5),     # decode kernel
+]
+
+
+@pytest.mark.parametrize("Sq,Skv,D,causal,scale", LARGE_M_CASES)
+def test_large_index_multiplier(Sq, Skv, D, causal, scale):
+    rng = np.random.default_rng(1000 + Skv)
+    q = rng.integers(-8, 9, (1, 2, Sq, D)).astype(np.int8)
+    k = rng.integers(-8, 9, (1, 2, Skv, D)).astype(np.int8)
+    v = rng.integers(-127, 128, (1, 2, Skv, D)).astype(np.int8)
+    scales = (scale, scale, 0.01, 0.01)
+    prm = O.derive_params(D, *scales, float(O.DEFAULT_CLIP))
+    assert prm.idx_mul >= 2 ** 21
+    _check_full(_custom(q, k, v, scales, causal, name=f"largeM{Skv}"))
+
+
 def test_repeat_launches_identical():
     w = W.make_random(2, 4, 300, 300, 64, False, 31, "channel_outliers", name="repeat")
     _say(f"case repeat shape={w.shape}")
