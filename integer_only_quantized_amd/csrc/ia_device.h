@@ -11,6 +11,8 @@
 #include <climits>
 #include <cstddef>
 #include <cstdint>
+#include <type_traits>
+#include <utility>
 
 #include "intattn_internal.h"
 
@@ -91,5 +93,128 @@ __device__ __forceinline__ uint32_t lut_entry(const IaKernelParams& P, int k) {
 __device__ __forceinline__ int32_t dpp_xor1(int32_t x) { return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true); }
 __device__ __forceinline__ int32_t dpp_xor2(int32_t x) { return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true); }
 __device__ __forceinline__ int32_t dpp_half_mirror(int32_t x) { return __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true); }
+
+
+// f(std::integral_constant<int, i>{}) for i = 0 .. N-1 (compile-time indices).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+
+// LDS tiles of K and V rows (D bytes per row, 16-byte chunks). 16-byte reads
+// are served 16 lanes per cycle over 64 four-byte banks, so the 16 rows read
+// by one 16-lane phase must land in 16 distinct 16-byte bank groups.
+//
+// Chunk position of logical chunk c of K row r: c ^ k_swz<D>(r).
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+    return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+// Chunk position of logical chunk c of V row (key) r: c ^ v_swz<D>(r); the 8
+// keys of one ds_read_b64_tr_b8 (for the P.V operand order below) land in 8
+// distinct bank groups.
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+    return D == 128 ? ((r & 3) | ((r >> 1) & 4)) : (((r >> 1) & 1) | ((r >> 2) & 2));
+}
+
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    // s_waitcnt with only the vector-memory counter constrained (lgkm/exp at max)
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
+// Workgroup barrier: this wave's LDS operations complete, then all waves
+// meet. Outstanding global->LDS loads are not waited for here (the caller
+// waits for exactly the loads it needs with wait_vmcnt first).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 32-bit LDS load from a byte address (the kernel's LDS block starts at 0).
+__device__ __forceinline__ uint32_t lds_u32(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(static_cast<uintptr_t>(addr));
+}
+
+// P.V B operand from a row-major V block of 32 keys in LDS (rows of D bytes,
+// chunks placed by v_swz): lane (l32, hh) needs V[key(b)][32db + l32] for its
+// 16 keys key(b) = acc_row(b, hh), b = 0..15, in that byte order. Two
+// ds_read_b64_tr_b8 per 32-column block provide them: within each 16-lane
+// group, lane pair (2i, 2i+1) supplies the two 8-byte halves of row key(b)
+// (b = i for the first read, 8 + i for the second), and lane j of the group
+// receives column j of those 8 rows. tr8_lane_addr gives this lane's byte
+// offset from the start of the block for read rd of column block db.
+template <int D>
+__device__ __forceinline__ uint32_t tr8_lane_addr(int lane, int db, int rd) {
+    const int hh = lane >> 5;
+    const int i = (lane & 15) >> 1;
+    const int key = acc_row(8 * rd + i, hh);
+    const int col = 32 * db + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+    return static_cast<uint32_t>(key * D + 16 * ((col >> 4) ^ v_swz<D>(key)) + (col & 15));
+}
+
+// All 2*DB transpose reads of one key block at LDS byte addresses va[i] + OFF,
+// waited for inside the same asm statement (its destination registers are
+// final when it ends); vb[db] is the B operand of column block db.
+template <int DB, int OFF>
+__device__ __forceinline__ void tr8_operands(const uint32_t (&va)[2 * DB], v4i (&vb)[DB]) {
+    v2i r[2 * DB];
+    if constexpr (DB == 4) {
+        asm volatile(
+            "ds_read_b64_tr_b8 %0, %8 offset:%16\n\t"
+            "ds_read_b64_tr_b8 %1, %9 offset:%16\n\t"
+            "ds_read_b64_tr_b8 %2, %10 offset:%16\n\t"
+            "ds_read_b64_tr_b8 %3, %11 offset:%16\n\t"
+            "ds_read_b64_tr_b8 %4, %12 offset:%16\n\t"
+            "ds_read_b64_tr_b8 %5, %13 offset:%16\n\t"
+            "ds_read_b64_tr_b8 %6, %14 offset:%16\n\t"
+            "ds_read_b64_tr_b8 %7, %15 offset:%16\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+              "=&v"(r[7])
+            : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]),
+              "i"(OFF));
+    } else {
+        static_assert(DB == 2, "column blocks per head: 2 (d = 64) or 4 (d = 128)");
+        asm volatile(
+            "ds_read_b64_tr_b8 %0, %4 offset:%8\n\t"
+            "ds_read_b64_tr_b8 %1, %5 offset:%8\n\t"
+            "ds_read_b64_tr_b8 %2, %6 offset:%8\n\t"
+            "ds_read_b64_tr_b8 %3, %7 offset:%8\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+            : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "i"(OFF));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        vb[db] = v4i{r[2 * db][0], r[2 * db][1], r[2 * db + 1][0], r[2 * db + 1][1]};
+}
+
+// Top byte of the probability word: for a table entry e <= E and R2 = 2R,
+// e * R2 + 2^23 < 2^32, so the top byte of e * R2 + 2^23 is
+// p = (e * R + 2^22) >> 23, and adding 2^31 flips its top bit: the byte is
+// p ^ 0x80, i.e. p - 128 as int8.
+__device__ __forceinline__ uint32_t prob_word(uint32_t e, uint32_t R2) { return __umul24(e, R2) + 0x80800000u; }
+
+// Top bytes of four words packed into one (byte i from word i).
+__device__ __forceinline__ uint32_t pack_top_bytes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+    const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x0c0c0703u);
+    const uint32_t hi = __builtin_amdgcn_perm(w3, w2, 0x07030c0cu);
+    return lo | hi;
+}
 
 }  // namespace ia

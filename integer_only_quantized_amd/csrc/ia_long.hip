@@ -52,9 +52,6 @@ constexpr int kLongTile = 64;                // keys per tile
 constexpr int kStages = 3;                   // LDS ring depth
 constexpr int kLutEntries = 128;
 
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 template <int D>
 struct LongLds {
     static constexpr int TB = kLongTile * D;        // bytes per K or V tile
@@ -63,43 +60,6 @@ struct LongLds {
     int8_t k[kStages][TB];
     int8_t v[kStages][TB];
 };
-
-// 16-byte chunk position of logical chunk c of K row r: the 16 rows read by
-// one 16-lane phase land in 16 distinct 16-byte bank groups.
-template <int D>
-__device__ __forceinline__ int k_swz(int r) {
-    return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
-}
-// Chunk position of logical chunk c of V row (key) r: the 8 keys of one
-// transpose read land in 8 distinct bank groups.
-template <int D>
-__device__ __forceinline__ int v_swz(int r) {
-    return D == 128 ? ((r & 3) | ((r >> 1) & 4)) : (((r >> 1) & 1) | ((r >> 2) & 2));
-}
-
-__device__ __forceinline__ void wait_vmcnt(int n) {
-    // s_waitcnt with only the vector-memory counter constrained (lgkm/exp at max)
-    switch (n) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    }
-}
-
-// Workgroup barrier for the LDS ring: this wave's LDS operations complete,
-// then all waves meet. Outstanding global->LDS loads are not waited for here
-// (the caller waits for exactly the tile it needs with wait_vmcnt first).
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// 32-bit LDS load from a byte address (the kernel's LDS block starts at 0).
-__device__ __forceinline__ uint32_t lds_u32(uint32_t addr) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(static_cast<uintptr_t>(addr));
-}
 
 template <int D, bool FAST>
 __global__ __launch_bounds__(256) void ia_long_kernel(
@@ -209,60 +169,15 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
         }
     };
 
-    // P.V B operand for key block kb, value columns 32db..32db+31 of the V tile
-    // in a stage: lane (l32, hh) gets V[key(b)][32db + l32] for its 16 keys
-    // key(b) = 32kb + acc_row(b, hh), b = 0..15, via two transpose reads.
-    // Within each 16-lane group, lane pair (2i, 2i+1) supplies the two 8-byte
-    // halves of row key(b) (b = i for the first read, 8 + i for the second);
-    // lane j of the group receives column j of those 8 rows. The addresses
-    // below are for stage 0, key block 0; the stage adds a register offset,
-    // key block 1 the immediate 32*D.
+    // P.V B operand addresses for stage 0, key block 0 (see tr8_lane_addr);
+    // the stage adds a register offset, key block 1 the immediate 32*D
     uint32_t vaddr[2 * DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
-        for (int rd = 0; rd < 2; ++rd) {
-            const int i = (lane & 15) >> 1;
-            const int key = acc_row(8 * rd + i, hh);
-            const int col = 32 * db + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-            const int c = (col >> 4) ^ v_swz<D>(key);
-            vaddr[2 * db + rd] = static_cast<uint32_t>(offsetof(L, v)) + key * D + 16 * c + (col & 15);
-        }
+        for (int rd = 0; rd < 2; ++rd)
+            vaddr[2 * db + rd] = static_cast<uint32_t>(offsetof(L, v)) + tr8_lane_addr<D>(lane, db, rd);
     }
-    // All 2*DB transpose reads of one key block, waited for in the same asm
-    // statement (the destination registers are final when it ends).
-    auto vfrag_all = [&](const uint32_t (&va)[2 * DB], auto kbc, v4i (&vb)[DB]) {
-        constexpr int OFF = decltype(kbc)::value * 32 * D;
-        v2i r[2 * DB];
-        if constexpr (DB == 4) {
-            asm volatile(
-                "ds_read_b64_tr_b8 %0, %8 offset:%16\n\t"
-                "ds_read_b64_tr_b8 %1, %9 offset:%16\n\t"
-                "ds_read_b64_tr_b8 %2, %10 offset:%16\n\t"
-                "ds_read_b64_tr_b8 %3, %11 offset:%16\n\t"
-                "ds_read_b64_tr_b8 %4, %12 offset:%16\n\t"
-                "ds_read_b64_tr_b8 %5, %13 offset:%16\n\t"
-                "ds_read_b64_tr_b8 %6, %14 offset:%16\n\t"
-                "ds_read_b64_tr_b8 %7, %15 offset:%16\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
-                  "=&v"(r[7])
-                : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]),
-                  "i"(OFF));
-        } else {
-            asm volatile(
-                "ds_read_b64_tr_b8 %0, %4 offset:%8\n\t"
-                "ds_read_b64_tr_b8 %1, %5 offset:%8\n\t"
-                "ds_read_b64_tr_b8 %2, %6 offset:%8\n\t"
-                "ds_read_b64_tr_b8 %3, %7 offset:%8\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-                : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "i"(OFF));
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-            vb[db] = v4i{r[2 * db][0], r[2 * db][1], r[2 * db + 1][0], r[2 * db + 1][1]};
-    };
 
     auto run_tiles = [&](bool with_v, auto&& body) {
         // prologue: tiles 0 and 1 requested, tile 0 waited for
@@ -351,14 +266,10 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     int32_t cs[DB];                          // this lane's part of the column sums
 #pragma unroll
     for (int db = 0; db < DB; ++db) cs[db] = 0;
-    // top byte = p ^ 0x80 (p - 128 as int8); e * 2R + 2^23 < 2^32 for e <= E
-    auto pword = [&](int32_t y) -> uint32_t { return __umul24(table_entry(y), R2) + 0x80800000u; };
+    auto pword = [&](int32_t y) -> uint32_t { return prob_word(table_entry(y), R2); };
     auto pack = [&](const v16i& s, int w4) -> int {
-        const uint32_t w0 = pword(s[4 * w4]), w1 = pword(s[4 * w4 + 1]);
-        const uint32_t w2 = pword(s[4 * w4 + 2]), w3 = pword(s[4 * w4 + 3]);
-        const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x0c0c0703u);
-        const uint32_t hi = __builtin_amdgcn_perm(w3, w2, 0x07030c0cu);
-        return static_cast<int>(lo | hi);
+        return static_cast<int>(pack_top_bytes(pword(s[4 * w4]), pword(s[4 * w4 + 1]), pword(s[4 * w4 + 2]),
+                                               pword(s[4 * w4 + 3])));
     };
     run_tiles(true, [&](int t, int st) {
         const bool colsum_turn = (t % kLongWaves) == wave;
@@ -371,7 +282,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
             mask(s, t * kLongTile + 32 * kb, kMasked);
             const v4i pa = v4i{pack(s, 0), pack(s, 1), pack(s, 2), pack(s, 3)};
             v4i vb[DB];
-            vfrag_all(va, kbc, vb);
+            tr8_operands<DB, kb * 32 * D>(va, vb);
 #pragma unroll
             for (int db = 0; db < DB; ++db) o[db] = mfma_i8_32x32x32(pa, vb[db], o[db]);
             if (colsum_turn) {
