@@ -72,7 +72,7 @@ __device__ __forceinline__ uint32_t slot_of(int32_t s, int32_t lo, uint32_t C, i
 // slot is below 31, and saturation to 2^31 - 1 lands exactly in slot 31.
 __device__ __forceinline__ uint32_t slot_word_sat(int32_t y, int32_t negM4, int32_t half4) {
     int32_t t;
-    asm("v_mad_i32_i24 %0, %1, %2, %3 clamp" : "=v"(t) : "v"(y), "v"(negM4), "v"(half4));
+    asm("v_mad_i32_i24 %0, %1, %2, %3 clamp" : "=v"(t) : "v"(y), "s"(negM4), "v"(half4));
     return static_cast<uint32_t>(t);
 }
 
@@ -85,9 +85,31 @@ __device__ __forceinline__ int8_t requantise(int32_t a, const IaKernelParams& P)
     return static_cast<int8_t>(a < 0 ? -static_cast<int32_t>(qv) : static_cast<int32_t>(qv));
 }
 
-// Entry k of the exp table from the packed kernel argument.
+// The same for shifts sh >= 33 in 32-bit arithmetic: 2^(sh-1) is then a
+// multiple of 2^32, so with |a| * M_o = hi * 2^32 + lo,
+//   (|a| * M_o + 2^(sh-1)) >> sh = (hi + 2^(sh-33)) >> (sh-32)
+// (lo / 2^32 < 1 cannot carry an integer numerator across a multiple of
+// 2^(sh-32)); hi + 2^(sh-33) < 2^31. add = 2^(sh-33), rsh = sh - 32.
+__device__ __forceinline__ int32_t requantise_hi(int32_t a, uint32_t mul, uint32_t add, uint32_t rsh) {
+    const uint32_t mag = static_cast<uint32_t>(a < 0 ? -a : a);
+    const uint32_t q = min((__umulhi(mag, mul) + add) >> rsh, 127u);
+    return a < 0 ? -static_cast<int32_t>(q) : static_cast<int32_t>(q);
+}
+
+// Entry k of the exp table from the packed kernel argument. The argument
+// words are wave-uniform (scalar registers); selecting among them keeps a
+// per-lane k from turning into a vector load of the argument segment (whose
+// wait would also cover any loads issued before it).
 __device__ __forceinline__ uint32_t lut_entry(const IaKernelParams& P, int k) {
-    return (P.lut2[k >> 1] >> (16 * (k & 1))) & 0xffffu;
+    const int w = k >> 1;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        uint32_t wi = P.lut2[i];
+        asm("" : "+s"(wi));             // a register value, not an argument-segment address
+        word = (w == i) ? wi : word;
+    }
+    return (word >> (16 * (k & 1))) & 0xffffu;
 }
 
 __device__ __forceinline__ int32_t dpp_xor1(int32_t x) { return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true); }
@@ -124,6 +146,14 @@ __device__ __forceinline__ int k_swz(int r) {
 template <int D>
 __device__ __forceinline__ int v_swz(int r) {
     return D == 128 ? ((r & 3) | ((r >> 1) & 4)) : (((r >> 1) & 1) | ((r >> 2) & 2));
+}
+
+// s_waitcnt vmcnt(N) for a compile-time N <= 63 (vmcnt bits [3:0] and
+// [15:14]; lgkmcnt and expcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_c() {
+    static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 __device__ __forceinline__ void wait_vmcnt(int n) {

@@ -51,6 +51,7 @@ struct ShortLds {
     uint32_t lut[kShortLut];                 // first member: LDS byte address 0
     int32_t xm[2][2][32];                    // row max exchange [query group][half][row]
     uint32_t xe[2][2][32];                   // row sum exchange
+    int32_t xcs[4][D];                       // column-sum partials, one per wave
     int8_t kv[Region];                       // K, then V, then the output partials
 };
 
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
             if (j + 1 < NBH) nxt = scores(kb0 + j + 1, zero16);
             mask(cur, kb0 + j, INT_MIN);
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) mrow = max(mrow, max(cur[r], cur[r + 1]));
+            for (int r = 0; r < 16; r += 2) mrow = max(max(mrow, cur[r]), cur[r + 1]);
             // keep the reduction per block (not one cross-block tree at the end)
             asm volatile("" : "+v"(mrow));
             if (j + 1 < NBH) cur = nxt;
@@ -193,7 +194,8 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
                     const uint32_t a = FAST ? ((t[c] >> 24) & 0x7cu) : ((t[c] >> 22) & 0x1fcu);
                     e[4 * w4 + c] = lds_u32(a);
                 }
-                idxw[j][w4] = pack_top_bytes(t[0], t[1], t[2], t[3]);
+                // FAST: 4 * slot per byte (fraction bits cleared); otherwise min(127, slot)
+                idxw[j][w4] = pack_top_bytes(t[0], t[1], t[2], t[3]) & (FAST ? 0x7c7c7c7cu : 0x7f7f7f7fu);
                 // keep the packed word (not the four values it came from) live
                 asm volatile("" : "+v"(idxw[j][w4]));
             }
@@ -229,8 +231,9 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     // ---- pass 3: P from the slot bytes, P.V on the MFMA -------------------
     // table address of byte i of a kept slot word
     auto byte_addr = [&](uint32_t w, int i) -> uint32_t {
-        if constexpr (FAST) return (w >> (8 * i)) & 0x7cu;
-        else return ((w >> (8 * i)) & 0x7fu) << 2;
+        const uint32_t b = i == 3 ? (w >> 24) : __builtin_amdgcn_ubfe(w, 8 * i, 8);
+        if constexpr (FAST) return b;
+        else return b << 2;
     };
     auto plookup = [&](int j, uint32_t (&pl)[16]) {
 #pragma unroll
@@ -266,50 +269,87 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
             v4i vb[DB];
             tr8_operands<DB, j * 32 * D>(vaddr, vb);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                o[db] = mfma_i8_32x32x32(pa, vb[db], o[db]);
+            for (int db = 0; db < DB; ++db) o[db] = mfma_i8_32x32x32(pa, vb[db], o[db]);
+            // the two query-group waves of a half see the same V blocks: each
+            // sums the columns of every other block (asm: no speculation)
+            if ((j & 1) == qg) {
 #pragma unroll
-                for (int w = 0; w < 4; ++w) cs[db] = __builtin_amdgcn_sdot4(vb[db][w], 0x01010101, cs[db], false);
+                for (int db = 0; db < DB; ++db) {
+                    asm volatile("" : "+v"(cs[db]));
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        cs[db] = __builtin_amdgcn_sdot4(vb[db][w], 0x01010101, cs[db], false);
+                }
             }
             if constexpr (j + 1 < NBH) pa = pnext;
             __builtin_amdgcn_sched_barrier(0);
         });
     }
-    // o + 128 * colsum over the rows fed = sum p v for this half
+    // column-sum partials of this wave (both key halves of the lane pair)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        const int32_t c128 = 128 * (cs[db] + __shfl_xor(cs[db], 32));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] += c128;
+        const int32_t c = cs[db] + __shfl_xor(cs[db], 32);
+        if (hh == 0) lds.xcs[wave][32 * db + l32] = c;
     }
 
     // ---- combine the halves, requantise, store -------------------------------
     // The wave of half h finishes column blocks [h*HDB, (h+1)*HDB); partial of
     // column block j of that set, from the wave (qg, src half), at
-    // kv + (((qg*2 + src)*HDB + j)*16 + r)*256 + 4*lane.
+    // kv + (((qg*2 + src)*HDB + j)*16 + r)*256 + 4*lane. Every row gets
+    // o_half0 + o_half1 + 128 * (sum of the four column-sum partials): the
+    // column sums cover exactly the V rows fed, so this is sum p v.
     lds_barrier();                       // every wave is done with V
     auto xo_addr = [&](int src, int j, int r) {
-        return static_cast<uint32_t>(offsetof(L, kv)) + static_cast<uint32_t>((((qg * 2 + src) * HDB + j) * 16 + r) * 256 + 4 * lane);
+        return static_cast<uint32_t>(offsetof(L, kv)) +
+               static_cast<uint32_t>((((qg * 2 + src) * HDB + j) * 16 + r) * 256 + 4 * lane);
     };
+    // rows of this lane: qw0 + 4hh + acc_row(r, 0); full groups skip the checks
+    int8_t* const obase = out + (head * P.Sq + qw0 + 4 * hh) * D;
+    const bool full = qw0 + 32 <= P.Sq;
+    // requantise 16 accumulators and store them at op + acc_row(r, 0) * D
+    const uint32_t rq_add = P.req_shift >= 33 ? (1u << (P.req_shift - 33)) : 0u;
+    const uint32_t rq_sh = static_cast<uint32_t>(P.req_shift - 32);
+    auto store_rows = [&](const int32_t (&acc)[16], int8_t* op) {
+        auto put = [&](auto rq) {
+            if (full) {
 #pragma unroll
-    for (int j = 0; j < HDB; ++j) {
-        const int db = (half ^ 1) * HDB + j;    // columns the other wave finishes
+                for (int r = 0; r < 16; ++r) op[acc_row(r, 0) * D] = static_cast<int8_t>(rq(acc[r]));
+            } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            *reinterpret_cast<__attribute__((address_space(3))) int32_t*>(static_cast<uintptr_t>(xo_addr(half, j, r))) = o[db][r];
-    }
-    lds_barrier();
+                for (int r = 0; r < 16; ++r)
+                    if (qw0 + 4 * hh + acc_row(r, 0) < P.Sq) op[acc_row(r, 0) * D] = static_cast<int8_t>(rq(acc[r]));
+            }
+        };
+        if (P.req_shift >= 33) put([&](int32_t a) { return requantise_hi(a, P.req_mul, rq_add, rq_sh); });
+        else put([&](int32_t a) { return static_cast<int32_t>(requantise(a, P)); });
+    };
+    auto finish = [&](auto hc) {
+        constexpr int H = decltype(hc)::value;
+        static_for<HDB>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int db = (1 - H) * HDB + j;     // columns the other wave finishes
 #pragma unroll
-    for (int j = 0; j < HDB; ++j) {
-        const int db = half * HDB + j;
-        const int d = 32 * db + l32;
+            for (int r = 0; r < 16; ++r)
+                *reinterpret_cast<__attribute__((address_space(3))) int32_t*>(
+                    static_cast<uintptr_t>(xo_addr(H, j, r))) = o[db][r];
+        });
+        lds_barrier();
+        static_for<HDB>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int db = H * HDB + j;
+            const int d = 32 * db + l32;
+            const int32_t c128 = 128 * (lds.xcs[0][d] + lds.xcs[1][d] + lds.xcs[2][d] + lds.xcs[3][d]);
+            int32_t acc[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int32_t acc = o[db][r] + static_cast<int32_t>(lds_u32(xo_addr(half ^ 1, j, r)));
-            const int qi = qw0 + acc_row(r, hh);
-            if (qi < P.Sq) out[(head * P.Sq + qi) * D + d] = requantise(acc, P);
-        }
-    }
+            for (int r = 0; r < 16; ++r) {
+                acc[r] = o[db][r] + c128 + static_cast<int32_t>(lds_u32(xo_addr(1 - H, j, r)));
+                asm volatile("" : "+v"(acc[r]));    // all reads issued before the stores
+            }
+            store_rows(acc, obase + d);
+        });
+    };
+    if (half == 0) finish(std::integral_constant<int, 0>{});
+    else finish(std::integral_constant<int, 1>{});
 }
 
 template <int D, int NBH>
