@@ -310,16 +310,33 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     __syncthreads();
 
     // ---- requantise and store -----------------------------------------------
+    // rows of this lane: qw0 + 4hh + acc_row(r, 0); full groups skip the checks
+    int8_t* const obase = out + (head * P.Sq + qw0 + 4 * hh) * D;
+    const bool full = qw0 + 32 <= P.Sq;
+    const uint32_t rq_add = P.req_shift >= 33 ? (1u << (P.req_shift - 33)) : 0u;
+    const uint32_t rq_sh = static_cast<uint32_t>(P.req_shift - 32);
+    auto store_rows = [&](const v16i& acc, int8_t* op) {
+        auto put = [&](auto rq) {
+            if (full) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) op[acc_row(r, 0) * D] = static_cast<int8_t>(rq(acc[r]));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (qw0 + 4 * hh + acc_row(r, 0) < P.Sq) op[acc_row(r, 0) * D] = static_cast<int8_t>(rq(acc[r]));
+            }
+        };
+        if (P.req_shift >= 33) put([&](int32_t x) { return requantise_hi(x, P.req_mul, rq_add, rq_sh); });
+        else put([&](int32_t x) { return static_cast<int32_t>(requantise(x, P)); });
+    };
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
         const int d = 32 * db + l32;
-        const int32_t csum = lds.colsum[0][d] + lds.colsum[1][d] + lds.colsum[2][d] + lds.colsum[3][d];
+        const int32_t c128 = 128 * (lds.colsum[0][d] + lds.colsum[1][d] + lds.colsum[2][d] + lds.colsum[3][d]);
+        v16i acc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qi = qw0 + acc_row(r, hh);
-            if (qi >= P.Sq) continue;
-            out[(head * P.Sq + qi) * D + d] = requantise(o[db][r] + 128 * csum, P);
-        }
+        for (int r = 0; r < 16; ++r) acc[r] = o[db][r] + c128;
+        store_rows(acc, obase + d);
     }
 }
 
