@@ -16,7 +16,12 @@ Q + K + V + O bytes of int8 read or written once.
 Timing: W untimed calls, then K calls bracketed by synchronisation and HIP
 events recorded on the stream the library launches on (the caller's current
 stream). The same events give the kernel's average duration per launch used
-for the roofline fraction.
+for the roofline fraction. Five more blocks of K calls give the median, and
+one block cycling through copies of the inputs (more than 512 MB in all, so
+they do not stay in the caches) gives the cold-input rate.
+
+    python bench.py --calibrate peaks   # measured copy GB/s, int8 MFMA TOPS, VALU ops/s
+    python bench.py --calibrate copy    # three 256 MiB device copies (counter scaling run)
 """
 from __future__ import annotations
 
@@ -33,8 +38,17 @@ if ROOT not in sys.path:
 
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+# 32-bit VALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3e12 lane-ops/s
+# (a wave64 VALU instruction occupies its SIMD for 4 cycles)
+PEAK_VALU_TLANEOPS = 39.3
+VALU_CYCLES_PER_INSTR = 4
+N_SIMD = 1024
+CLOCK_GHZ = 2.4
 
 DEFAULT_STEPS = {"tiny": 2000, "bert": 500, "vit": 500, "llama_prefill": 50, "decode": 100}
+# untimed calls before the timed region: about 0.4 s of work, so the GPU has
+# left its idle clocks (shorter warm-ups measure the clock ramp-up)
+DEFAULT_WARMUP = {"tiny": 50000, "bert": 30000, "vit": 25000, "llama_prefill": 2000, "decode": 2000}
 BOUND = {"tiny": "mfma", "bert": "mfma", "vit": "mfma", "llama_prefill": "mfma", "decode": "hbm"}
 # kernel the library dispatches for each workload, and its source file
 KERNEL = {"tiny": ("ia_short_kernel", "ia_short.hip"), "bert": ("ia_short_kernel", "ia_short.hip"),
@@ -69,6 +83,27 @@ def measured_traffic(config: str):
         return None
     try:
         return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def measured_valu(config):
+    """SQ_INSTS_VALU per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since."""
+    kname, src = KERNEL[config]
+    path = os.path.join(ROOT, "profiles", f"valu_{kname}_{config}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line:
+                k, _, val = line.partition(":")
+                fields[k.strip()] = val.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_sha(src):
+        return None
+    try:
+        return float(fields["valu_wave_instrs_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -128,15 +163,75 @@ def cpu_baseline(w, budget_s=10.0):
     return info, results
 
 
+def calibrate(mode):
+    """Peaks measured on this GPU (mode 'peaks'), or the plain-copy run that
+    scales FETCH_SIZE / WRITE_SIZE (mode 'copy': three 256 MiB copies)."""
+    import ctypes
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if mode == "copy":
+        n = 256 << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).random_(0, 255)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_per_copy": n, "copies": 3}), flush=True)
+        return 0
+    out = {"calibration": "peaks"}
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev).random_(0, 255)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(20):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    out["copy_GBs"] = 2 * n * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    lib = ctypes.CDLL(os.path.join(ROOT, "integer_only_quantized_amd", "libintattn_probe.so"))
+    for fn in (lib.intattn_probe_mfma_i8, lib.intattn_probe_valu):
+        fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        fn.restype = ctypes.c_int
+    blocks = 2048
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    for name, fn, iters, work in (
+            ("mfma_i8_TOPS", lib.intattn_probe_mfma_i8, 20000, lambda it: blocks * 4 * 4 * it * 65536 / 1e12),
+            ("valu_Tlaneops", lib.intattn_probe_valu, 100000, lambda it: blocks * 256 * 8 * it / 1e12)):
+        if fn(blocks, 100, ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+            raise RuntimeError(f"{name}: probe launch failed")
+        torch.cuda.synchronize()
+        e0.record()
+        if fn(blocks, iters, ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+            raise RuntimeError(f"{name}: probe launch failed")
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = work(iters) / (e0.elapsed_time(e1) * 1e-3)
+    out["spec"] = {"hbm_GBs": PEAK_HBM_GBS, "mfma_i8_TOPS": PEAK_INT8_TOPS, "valu_Tlaneops": PEAK_VALU_TLANEOPS}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default="bert",
                     choices=["tiny", "bert", "vit", "llama_prefill", "decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibrate", choices=["peaks", "copy"], default=None)
+    ap.add_argument("--no-extra-timing", action="store_true",
+                    help="skip the median-of-5 and cold-input blocks")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -145,6 +240,9 @@ def main(argv=None):
               "library runs on one GPU. Run with --gpus 1.", file=sys.stderr)
         return 2
 
+    if args.calibrate:
+        return calibrate(args.calibrate)
+
     import numpy as np
     import torch
 
@@ -152,6 +250,7 @@ def main(argv=None):
     from integer_only_quantized_amd import workloads as W
 
     steps = args.steps or DEFAULT_STEPS[args.config]
+    warmup = DEFAULT_WARMUP[args.config] if args.warmup is None else args.warmup
     w = W.make_config(args.config)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -159,7 +258,7 @@ def main(argv=None):
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         ia.forward(q, k, v, w.scales, w.clip, w.causal, out=out)
     torch.cuda.synchronize(dev)
 
@@ -175,6 +274,32 @@ def main(argv=None):
     t_wall = time.perf_counter() - t_wall0
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / steps
+
+    timing = None
+    if not args.no_extra_timing:
+        def timed_block(sets):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize(dev)
+            e0.record(stream)
+            for i in range(steps):
+                qs, ks, vs, os_ = sets[i % len(sets)]
+                ia.forward(qs, ks, vs, w.scales, w.clip, w.causal, out=os_)
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            return e0.elapsed_time(e1) / steps
+        warm = [(q, k, v, out)]
+        reps = [timed_block(warm) for _ in range(5)]
+        per_set = 2 * q.numel() + 2 * k.numel()
+        # input copies totalling > 512 MB (twice the 256 MB last-level cache),
+        # at most 4096 of them (tiny inputs are launch-bound either way)
+        n_sets = 1 if per_set > (512 << 20) else min(4096, (512 << 20) // per_set + 2)
+        cold_sets = warm + [(q.clone(), k.clone(), v.clone(), torch.empty_like(out)) for _ in range(n_sets - 1)]
+        cold = timed_block(cold_sets)
+        del cold_sets
+        timing = {"repeats_ms_per_step": reps, "median_ms_per_step": sorted(reps)[2],
+                  "cold_ms_per_step": cold, "cold_input_sets": n_sets,
+                  "cold_input_bytes": n_sets * per_set}
 
     ops, nbytes, scores = algorithmic_work(w)
     sec = ms_per_step / 1e3
@@ -193,6 +318,14 @@ def main(argv=None):
     roof["per_launch"] = {"ops": ops, "bytes": nbytes, "scores": scores,
                           "avg_launch_us": ms_per_step * 1e3}
     roof["traffic"] = measured_traffic(args.config)
+    valu_instrs = measured_valu(args.config)
+    valu = None
+    if valu_instrs is not None:
+        lane_ops = valu_instrs * 64
+        achieved = lane_ops / sec / 1e12
+        valu = {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_TLANEOPS, "unit": "T lane-ops/s",
+                "frac": achieved / PEAK_VALU_TLANEOPS, "lane_ops_per_score": lane_ops / scores,
+                "source": f"profiles/valu_{KERNEL[args.config][0]}_{args.config}.txt"}
 
     cpu = None
     parity = None
@@ -213,7 +346,7 @@ def main(argv=None):
         "unit": unit,
         "n_gpus": 1,
         "steps": steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -227,6 +360,8 @@ def main(argv=None):
         "gb_per_s": gbs,
         "wall_s_timed_region": t_wall,
         "roofline": roof,
+        "valu_roofline": valu,
+        "timing": timing,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -20,6 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libintattn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+# roofline calibration kernels (pure MFMA / VALU loops), a separate library
+PROBE_LIB_PATH = os.path.join(HERE, "libintattn_probe.so")
+PROBE_SOURCES = ["peak_probe.hip"]
 BUILD_DIR = os.path.join(ROOT, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
@@ -63,11 +66,17 @@ def build(verbose: bool = True, jobs: int = 8) -> str:
         obj = os.path.join(BUILD_DIR, src.rsplit(".", 1)[0] + ".o")
         cmds.append([HIPCC] + HIP_FLAGS + HIP_EXTRA.get(src, []) + inc + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    probe_objs = []
+    for src in PROBE_SOURCES:
+        obj = os.path.join(BUILD_DIR, src.rsplit(".", 1)[0] + ".o")
+        cmds.append([HIPCC] + HIP_FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", obj])
+        probe_objs.append(obj)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         list(ex.map(_run, cmds))
-    tmp = LIB_PATH + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp])
-    os.replace(tmp, LIB_PATH)
+    for objects, path in ((objs, LIB_PATH), (probe_objs, PROBE_LIB_PATH)):
+        tmp = path + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objects + ["-o", tmp])
+        os.replace(tmp, path)
     return LIB_PATH
 
 
