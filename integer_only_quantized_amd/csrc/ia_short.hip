@@ -87,15 +87,36 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     // Load i of wave w fills LDS bytes [(w*LOADS + i) KB, +1 KB): lane l writes
     // row (1 KB offset)/D + l/CPR, stored chunk l % CPR = logical chunk
     // (l % CPR) ^ swizzle(row).
-    auto stage = [&](const int8_t* src, bool is_v) {
+    // The source offset of load blk is blk*1024 plus a per-lane constant that
+    // depends only on the parity of blk (the swizzles use the row's low bits),
+    // so the loads take a scalar base; rows past Skv (a uniform tail case)
+    // are clamped per lane.
+    uint32_t koff[2], voff[2];
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int blk = wave * LOADS + i;
-            const int row = blk * (1024 / D) + lane / CPR;
-            const int chunk = (lane % CPR) ^ (is_v ? v_swz<D>(row) : k_swz<D>(row));
-            const int srow = min(row, P.Skv - 1);
-            __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(srow) * D + 16 * chunk,
-                                             (lds_void_t*)(lds.kv + blk * 1024), 16, 0, 0);
+    for (int par = 0; par < 2; ++par) {
+        const int row = par * (1024 / D) + lane / CPR;
+        koff[par] = static_cast<uint32_t>(row * D + 16 * ((lane % CPR) ^ k_swz<D>(row)) - par * 1024);
+        voff[par] = static_cast<uint32_t>(row * D + 16 * ((lane % CPR) ^ v_swz<D>(row)) - par * 1024);
+    }
+    const bool stage_tail = L::KVBytes / D > P.Skv;     // some staged rows lie past Skv
+    auto stage = [&](const int8_t* src, bool is_v) {
+        const uint32_t* off = is_v ? voff : koff;
+        if (!stage_tail) {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int blk = wave * LOADS + i;
+                __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(blk) * 1024 + off[blk & 1],
+                                                 (lds_void_t*)(lds.kv + blk * 1024), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int blk = wave * LOADS + i;
+                const int row = blk * (1024 / D) + lane / CPR;
+                const int chunk = (lane % CPR) ^ (is_v ? v_swz<D>(row) : k_swz<D>(row));
+                __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(min(row, P.Skv - 1)) * D + 16 * chunk,
+                                                 (lds_void_t*)(lds.kv + blk * 1024), 16, 0, 0);
+            }
         }
     };
     stage(kh, false);
@@ -194,8 +215,8 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
                     const uint32_t a = FAST ? ((t[c] >> 24) & 0x7cu) : ((t[c] >> 22) & 0x1fcu);
                     e[4 * w4 + c] = lds_u32(a);
                 }
-                // FAST: 4 * slot per byte (fraction bits cleared); otherwise min(127, slot)
-                idxw[j][w4] = pack_top_bytes(t[0], t[1], t[2], t[3]) & (FAST ? 0x7c7c7c7cu : 0x7f7f7f7fu);
+                // top bytes: FAST 4 * slot + fraction; otherwise min(127, slot)
+                idxw[j][w4] = pack_top_bytes(t[0], t[1], t[2], t[3]);
                 // keep the packed word (not the four values it came from) live
                 asm volatile("" : "+v"(idxw[j][w4]));
             }
@@ -229,11 +250,27 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     lds_barrier();
 
     // ---- pass 3: P from the slot bytes, P.V on the MFMA -------------------
-    // table address of byte i of a kept slot word
+    // table address of byte i of a kept slot word: FAST: byte & 0x7c;
+    // otherwise 4 * byte (bytes are at most 127); one SDWA op either way
     auto byte_addr = [&](uint32_t w, int i) -> uint32_t {
-        const uint32_t b = i == 3 ? (w >> 24) : __builtin_amdgcn_ubfe(w, 8 * i, 8);
-        if constexpr (FAST) return b;
-        else return b << 2;
+        uint32_t a;
+        if constexpr (FAST) {
+            const uint32_t m = 0x7cu;
+            switch (i) {
+                case 0: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
+                case 1: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
+                case 2: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
+                default: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
+            }
+        } else {
+            switch (i) {
+                case 0: asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(a) : "v"(w)); break;
+                case 1: asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(a) : "v"(w)); break;
+                case 2: asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(a) : "v"(w)); break;
+                default: asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(a) : "v"(w)); break;
+            }
+        }
+        return a;
     };
     auto plookup = [&](int j, uint32_t (&pl)[16]) {
 #pragma unroll
