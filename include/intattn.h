@@ -113,13 +113,60 @@ int intattn_forward(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* o
 /* intattn_forward plus the per-row integer state of IndexSoftmax, for parity
  * checks: row_max [B,H,Sq] int32 (m_i), row_sum [B,H,Sq] uint32 (E_i), and,
  * when probs is not NULL, probs [B,H,Sq,Skv] uint8 (p_ij, 0 for masked keys).
- * row_max and row_sum are required device pointers. Runs the general kernel
- * (not the shape-specialised ones), so it is slower than intattn_forward.
- * Errors: as intattn_forward. */
+ * row_max and row_sum are required device pointers. With probs, the general
+ * kernel runs (the only one that writes P); without, the same kernel as
+ * intattn_forward. Errors: as intattn_forward. */
 int intattn_forward_debug(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
                           const intattn_shape* shape, const intattn_scales* scales,
                           float clip, int causal, void* stream,
                           int32_t* row_max, uint32_t* row_sum, uint8_t* probs);
+
+/* ---- The pipeline as separate stages (scores and P in device memory) ----
+ * The pages' "Methodology" step 1 places the cost of an INT8 pipeline in the
+ * floating-point softmax between the integer products; these entry points run
+ * the three steps as separate kernels so each can be timed, and offer the
+ * floating-point softmax as a comparator. Chained as
+ *   intattn_qk_scores -> intattn_index_softmax -> intattn_pv
+ * they give exactly intattn_forward's output. All buffers are caller-owned
+ * device memory; nothing is allocated; calls queue on stream and return.
+ * The softmax stages need Skv <= 4096 (a row is held in registers). */
+
+/* Step 3, first product: scores[b,h,i,j] = sum_d q[b,h,i,d] * k[b,h,j,d]
+ * as int32 [B,H,Sq,Skv], for every (i, j) (masks are applied by the
+ * softmax stage). q, k 16-byte aligned; scores 4-byte aligned.
+ * Errors: E_NULL, E_SHAPE, E_DIM, E_ALIGN, E_HIP. */
+int intattn_qk_scores(const int8_t* q, const int8_t* k, int32_t* scores,
+                      const intattn_shape* shape, void* stream);
+
+/* Step 2, IndexSoftmax on int32 scores [B,H,Sq,Skv] (|s| < 2^30, as any
+ * int8 product is): probs [B,H,Sq,Skv] uint8 p_ij (0 for keys that are not
+ * allowed), and optionally row_max [B,H,Sq] int32 and row_sum [B,H,Sq]
+ * uint32 (both or neither). Same integers as intattn_forward_debug.
+ * scores 4-byte aligned. Errors: E_NULL, E_SHAPE (also Skv > 4096), E_DIM,
+ * E_ALIGN, E_SCALE, E_CLIP, E_RANGE, E_HIP. */
+int intattn_index_softmax(const int32_t* scores, uint8_t* probs, int32_t* row_max,
+                          uint32_t* row_sum, const intattn_shape* shape,
+                          const intattn_scales* scales, float clip, int causal,
+                          void* stream);
+
+/* Comparator for step 2 (the dequantise-softmax-requantise loop the pages
+ * remove): y = alpha * s in float32 with alpha = float32(s_q*s_k/sqrt(D)),
+ * softmax over the allowed keys with the row max subtracted (float32), and
+ * probs = min(255, rint(255 * p)) as uint8 (0 for keys that are not
+ * allowed). Floating point is used only here. scores 4-byte aligned.
+ * Errors: E_NULL, E_SHAPE (also Skv > 4096), E_DIM, E_ALIGN, E_SCALE, E_HIP. */
+int intattn_fp_softmax(const int32_t* scores, uint8_t* probs, const intattn_shape* shape,
+                       const intattn_scales* scales, int causal, void* stream);
+
+/* Step 3, second product: out = requantise(P.V) int8 [B,H,Sq,D] from uint8
+ * probs [B,H,Sq,Skv] and int8 v, with the requantisation of intattn_forward
+ * (from s_v, s_o; clip and the other scales must be valid as for
+ * intattn_forward). With causal, key tiles past a query block's causal limit
+ * are skipped, so probs must be 0 there (as the softmax stages write them).
+ * v, out 16-byte aligned. Errors: E_NULL, E_SHAPE, E_DIM, E_ALIGN, E_SCALE,
+ * E_CLIP, E_RANGE, E_HIP. */
+int intattn_pv(const uint8_t* probs, const int8_t* v, int8_t* out, const intattn_shape* shape,
+               const intattn_scales* scales, float clip, int causal, void* stream);
 
 /* Static, NUL-terminated description of a status code. Never NULL. */
 const char* intattn_strerror(int status);

@@ -68,6 +68,15 @@ def _load():
     lib.intattn_forward_debug.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape),
                                           ctypes.POINTER(Scales), f32, i32, vp, vp, vp, vp]
     lib.intattn_forward_debug.restype = i32
+    lib.intattn_qk_scores.argtypes = [vp, vp, vp, ctypes.POINTER(Shape), vp]
+    lib.intattn_qk_scores.restype = i32
+    lib.intattn_index_softmax.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), ctypes.POINTER(Scales),
+                                          f32, i32, vp]
+    lib.intattn_index_softmax.restype = i32
+    lib.intattn_fp_softmax.argtypes = [vp, vp, ctypes.POINTER(Shape), ctypes.POINTER(Scales), i32, vp]
+    lib.intattn_fp_softmax.restype = i32
+    lib.intattn_pv.argtypes = [vp, vp, vp, ctypes.POINTER(Shape), ctypes.POINTER(Scales), f32, i32, vp]
+    lib.intattn_pv.restype = i32
     lib.intattn_strerror.argtypes = [i32]
     lib.intattn_strerror.restype = ctypes.c_char_p
     return lib
@@ -184,3 +193,103 @@ def forward_debug(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = Fa
                        debug=(rm.data_ptr(), rs.data_ptr(), pr.data_ptr() if pr is not None else None))
     _check(code, "intattn_forward_debug")
     return out, rm, rs, pr
+
+
+# ---------------------------------------------------------------------------
+# The pipeline as separate stages (scores and P in device memory)
+# ---------------------------------------------------------------------------
+def _check_t(name, t, dtype, ndim, device=None):
+    if t.dtype is not dtype or not t.is_cuda or t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-D {dtype} CUDA tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
+def qk_scores(q, k, out=None):
+    """int32 scores [B, H, Sq, Skv] = Q.K^T of int8 q [B,H,Sq,D], k [B,H,Skv,D]."""
+    import torch
+    _check_t("q", q, torch.int8, 4)
+    _check_t("k", k, torch.int8, 4, q.device)
+    B, H, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
+        raise ValueError("shape mismatch between q and k")
+    Skv = k.shape[2]
+    if out is None:
+        out = torch.empty((B, H, Sq, Skv), dtype=torch.int32, device=q.device)
+    else:
+        _check_t("out", out, torch.int32, 4, q.device)
+        if tuple(out.shape) != (B, H, Sq, Skv):
+            raise ValueError("out must be [B, H, Sq, Skv]")
+    sh, _ = _structs((B, H, Sq, Skv, D), (1.0, 1.0, 1.0, 1.0))
+    _check(_lib.intattn_qk_scores(q.data_ptr(), k.data_ptr(), out.data_ptr(), ctypes.byref(sh), _stream(q)),
+           "intattn_qk_scores")
+    return out
+
+
+def _scores_shape(scores, D):
+    B, H, Sq, Skv = scores.shape
+    return (B, H, Sq, Skv, int(D))
+
+
+def index_softmax(scores, D, scales, clip: float = DEFAULT_CLIP, causal: bool = False, probs=None,
+                  stats: bool = False):
+    """IndexSoftmax of int32 scores [B,H,Sq,Skv] -> uint8 probs (and, with
+    stats, int32 row max and uint32 row sums as an int32 view)."""
+    import torch
+    _check_t("scores", scores, torch.int32, 4)
+    shape = _scores_shape(scores, D)
+    if probs is None:
+        probs = torch.empty(scores.shape, dtype=torch.uint8, device=scores.device)
+    else:
+        _check_t("probs", probs, torch.uint8, 4, scores.device)
+        if probs.shape != scores.shape:
+            raise ValueError("probs must be shaped like scores")
+    rm = rs = None
+    if stats:
+        rm = torch.empty(scores.shape[:3], dtype=torch.int32, device=scores.device)
+        rs = torch.empty(scores.shape[:3], dtype=torch.int32, device=scores.device)
+    sh, sc = _structs(shape, scales)
+    _check(_lib.intattn_index_softmax(scores.data_ptr(), probs.data_ptr(),
+                                      rm.data_ptr() if stats else None, rs.data_ptr() if stats else None,
+                                      ctypes.byref(sh), ctypes.byref(sc), float(clip), int(bool(causal)),
+                                      _stream(scores)), "intattn_index_softmax")
+    return (probs, rm, rs) if stats else probs
+
+
+def fp_softmax(scores, D, scales, causal: bool = False, probs=None):
+    """Comparator: dequantise -> float32 softmax -> uint8 codes rint(255 p)."""
+    import torch
+    _check_t("scores", scores, torch.int32, 4)
+    shape = _scores_shape(scores, D)
+    if probs is None:
+        probs = torch.empty(scores.shape, dtype=torch.uint8, device=scores.device)
+    else:
+        _check_t("probs", probs, torch.uint8, 4, scores.device)
+        if probs.shape != scores.shape:
+            raise ValueError("probs must be shaped like scores")
+    sh, sc = _structs(shape, scales)
+    _check(_lib.intattn_fp_softmax(scores.data_ptr(), probs.data_ptr(), ctypes.byref(sh), ctypes.byref(sc),
+                                   int(bool(causal)), _stream(scores)), "intattn_fp_softmax")
+    return probs
+
+
+def pv(probs, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False, out=None):
+    """int8 out [B,H,Sq,D] = requantise(P.V) from uint8 probs and int8 v."""
+    import torch
+    _check_t("probs", probs, torch.uint8, 4)
+    _check_t("v", v, torch.int8, 4, probs.device)
+    B, H, Sq, Skv = probs.shape
+    if v.shape[0] != B or v.shape[1] != H or v.shape[2] != Skv:
+        raise ValueError("shape mismatch between probs and v")
+    D = v.shape[3]
+    if out is None:
+        out = torch.empty((B, H, Sq, D), dtype=torch.int8, device=probs.device)
+    else:
+        _check_t("out", out, torch.int8, 4, probs.device)
+        if tuple(out.shape) != (B, H, Sq, D):
+            raise ValueError("out must be [B, H, Sq, D]")
+    sh, sc = _structs((B, H, Sq, Skv, D), scales)
+    _check(_lib.intattn_pv(probs.data_ptr(), v.data_ptr(), out.data_ptr(), ctypes.byref(sh), ctypes.byref(sc),
+                           float(clip), int(bool(causal)), _stream(probs)), "intattn_pv")
+    return out
+

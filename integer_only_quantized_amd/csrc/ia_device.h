@@ -175,6 +175,11 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// LDS byte address of a __shared__ object (its offset in the workgroup's LDS).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)(const_cast<void*>(p))));
+}
+
 // 32-bit LDS load from a byte address (the kernel's LDS block starts at 0).
 __device__ __forceinline__ uint32_t lds_u32(uint32_t addr) {
     return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(static_cast<uintptr_t>(addr));

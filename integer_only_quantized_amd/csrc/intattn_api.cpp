@@ -7,7 +7,13 @@
 //   otherwise                                -> long-row kernel (tiled, 3 passes)
 // intattn_forward_debug with a probability buffer runs the general kernel,
 // which is the only one that materialises P.
+//
+// The unfused stages (intattn_qk_scores, intattn_index_softmax,
+// intattn_fp_softmax, intattn_pv) keep scores and probabilities in
+// caller-owned device buffers; chained, the integer ones give exactly the
+// result of intattn_forward.
 #include <climits>
+#include <cmath>
 #include <cstdint>
 
 #include "intattn.h"
@@ -17,14 +23,12 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int prepare(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
-            const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
-            IaKernelParams* kp) {
-    if (!q || !k || !v || !out || !shape || !scales) return INTATTN_E_NULL;
+// Shape, head size and parameter derivation shared by every entry point.
+int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
+                         IaKernelParams* kp) {
     int st = intattn_validate_shape(shape, causal);
     if (st != INTATTN_OK) return st;
     if (shape->D != 64 && shape->D != 128) return INTATTN_E_DIM;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return INTATTN_E_ALIGN;
     intattn_params prm;
     st = intattn_derive_params(shape, scales, clip, &prm);
     if (st != INTATTN_OK) return st;
@@ -41,6 +45,18 @@ int prepare(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
         kp->lut2[i] = static_cast<uint32_t>(prm.lut[2 * i]) | (static_cast<uint32_t>(prm.lut[2 * i + 1]) << 16);
     return INTATTN_OK;
 }
+
+int prepare(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
+            const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
+            IaKernelParams* kp) {
+    if (!q || !k || !v || !out || !shape || !scales) return INTATTN_E_NULL;
+    const int st = derive_kernel_params(shape, scales, clip, causal, kp);
+    if (st != INTATTN_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return INTATTN_E_ALIGN;
+    return INTATTN_OK;
+}
+
+long long rows_of(const IaKernelParams& kp) { return static_cast<long long>(kp.B) * kp.H * kp.Sq; }
 
 int dispatch(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
              const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum) {
@@ -75,4 +91,68 @@ extern "C" int intattn_forward_debug(const int8_t* q, const int8_t* k, const int
     if (probs != nullptr)
         return ia::launch_general(q, k, v, out, shape->D, kp, stream, row_max, row_sum, probs);
     return dispatch(q, k, v, out, shape->D, kp, stream, row_max, row_sum);
+}
+
+extern "C" int intattn_qk_scores(const int8_t* q, const int8_t* k, int32_t* scores, const intattn_shape* shape,
+                                 void* stream) {
+    if (!q || !k || !scores || !shape) return INTATTN_E_NULL;
+    int st = intattn_validate_shape(shape, 0);
+    if (st != INTATTN_OK) return st;
+    if (shape->D != 64 && shape->D != 128) return INTATTN_E_DIM;
+    if (!aligned16(q) || !aligned16(k) || (reinterpret_cast<uintptr_t>(scores) & 3u)) return INTATTN_E_ALIGN;
+    IaKernelParams kp{};
+    kp.B = shape->B;
+    kp.H = shape->H;
+    kp.Sq = shape->Sq;
+    kp.Skv = shape->Skv;
+    if (rows_of(kp) == 0) return INTATTN_OK;
+    return ia::launch_qk_scores(q, k, scores, shape->D, kp, stream);
+}
+
+extern "C" int intattn_index_softmax(const int32_t* scores, uint8_t* probs, int32_t* row_max, uint32_t* row_sum,
+                                     const intattn_shape* shape, const intattn_scales* scales, float clip,
+                                     int causal, void* stream) {
+    if (!scores || !probs || !shape || !scales) return INTATTN_E_NULL;
+    if ((row_max == nullptr) != (row_sum == nullptr)) return INTATTN_E_NULL;
+    if (reinterpret_cast<uintptr_t>(scores) & 3u) return INTATTN_E_ALIGN;
+    IaKernelParams kp;
+    const int st = derive_kernel_params(shape, scales, clip, causal, &kp);
+    if (st != INTATTN_OK) return st;
+    if (kp.Skv > ia::stage_max_keys()) return INTATTN_E_SHAPE;
+    if (rows_of(kp) == 0) return INTATTN_OK;
+    return ia::launch_index_softmax(scores, probs, row_max, row_sum, kp, stream);
+}
+
+extern "C" int intattn_fp_softmax(const int32_t* scores, uint8_t* probs, const intattn_shape* shape,
+                                  const intattn_scales* scales, int causal, void* stream) {
+    if (!scores || !probs || !shape || !scales) return INTATTN_E_NULL;
+    if (reinterpret_cast<uintptr_t>(scores) & 3u) return INTATTN_E_ALIGN;
+    int st = intattn_validate_shape(shape, causal);
+    if (st != INTATTN_OK) return st;
+    if (shape->D != 64 && shape->D != 128) return INTATTN_E_DIM;
+    if (!(scales->q > 0.0f) || !(scales->k > 0.0f) || !std::isfinite(scales->q) || !std::isfinite(scales->k))
+        return INTATTN_E_SCALE;
+    IaKernelParams kp{};
+    kp.B = shape->B;
+    kp.H = shape->H;
+    kp.Sq = shape->Sq;
+    kp.Skv = shape->Skv;
+    kp.causal = causal ? 1 : 0;
+    if (kp.Skv > ia::stage_max_keys()) return INTATTN_E_SHAPE;
+    if (rows_of(kp) == 0) return INTATTN_OK;
+    // dequantisation factor of a score: s_q * s_k / sqrt(D), rounded once to float32
+    const float alpha = static_cast<float>(static_cast<double>(scales->q) * static_cast<double>(scales->k) /
+                                           std::sqrt(static_cast<double>(shape->D)));
+    return ia::launch_fp_softmax(scores, probs, alpha, kp, stream);
+}
+
+extern "C" int intattn_pv(const uint8_t* probs, const int8_t* v, int8_t* out, const intattn_shape* shape,
+                          const intattn_scales* scales, float clip, int causal, void* stream) {
+    if (!probs || !v || !out || !shape || !scales) return INTATTN_E_NULL;
+    if (!aligned16(v) || !aligned16(out)) return INTATTN_E_ALIGN;
+    IaKernelParams kp;
+    const int st = derive_kernel_params(shape, scales, clip, causal, &kp);
+    if (st != INTATTN_OK) return st;
+    if (rows_of(kp) == 0) return INTATTN_OK;
+    return ia::launch_pv(probs, v, out, shape->D, kp, stream);
 }

@@ -47,4 +47,14 @@ int launch_decode(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out
 int launch_long(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
                 const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum);
 
+// Unfused pipeline stages (scores and probabilities in HBM). The softmax
+// stages hold a row in registers: Skv <= stage_max_keys().
+int stage_max_keys();
+int launch_qk_scores(const int8_t* q, const int8_t* k, int32_t* scores, int D, const IaKernelParams& kp,
+                     void* stream);
+int launch_index_softmax(const int32_t* scores, uint8_t* probs, int32_t* row_max, uint32_t* row_sum,
+                         const IaKernelParams& kp, void* stream);
+int launch_fp_softmax(const int32_t* scores, uint8_t* probs, float alpha, const IaKernelParams& kp, void* stream);
+int launch_pv(const uint8_t* probs, const int8_t* v, int8_t* out, int D, const IaKernelParams& kp, void* stream);
+
 }  // namespace ia

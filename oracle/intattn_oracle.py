@@ -197,13 +197,23 @@ def allowed_mask(Sq: int, Skv: int, causal: bool):
     return j <= i + (Skv - Sq)
 
 
-def head_forward(qh, kh, vh, prm: Params, causal: bool):
-    """One (b, h) slice. Returns out int8 [Sq, D], m int64 [Sq], E int64 [Sq],
-    P uint8 [Sq, Skv]."""
-    Sq, D = qh.shape
-    Skv = kh.shape[0]
-    # Q.K^T: exact integer contraction (float64 BLAS, exact below 2^53)
-    S = np.rint(qh.astype(np.float64) @ kh.astype(np.float64).T).astype(np.int64)
+def qk_scores(qh, kh):
+    """int32 scores S = Q.K^T of one head, [Sq, Skv] (methodology step 3:
+    the score product stays integer). Exact: float64 BLAS below 2^53."""
+    return np.rint(qh.astype(np.float64) @ kh.astype(np.float64).T).astype(np.int64)
+
+
+def index_softmax(S, prm: Params, causal: bool):
+    """IndexSoftmax of one head's int32 scores (methodology step 2).
+
+    Row max over the allowed keys, relative scores x = m - s, table slots with
+    the sparsity-aware clip, int32 row sum E of the table entries, integer
+    reciprocal R and uint8 probabilities p = (e*R + 2^22) >> 23. Keys that are
+    not allowed take the last slot (entry 0, p = 0). Returns P uint8 [Sq, Skv],
+    m int64 [Sq], E int64 [Sq].
+    """
+    S = np.asarray(S, dtype=np.int64)
+    Sq, Skv = S.shape
     allow = allowed_mask(Sq, Skv, causal)
     lo = np.iinfo(np.int64).min
     m = np.where(allow, S, lo).max(axis=1)
@@ -214,10 +224,23 @@ def head_forward(qh, kh, vh, prm: Params, causal: bool):
     E = e.sum(axis=1)
     R = reciprocal(E)
     P = normalise(e, R[:, None])
-    # P.V: exact integer contraction
-    A = np.rint(P.astype(np.float64) @ vh.astype(np.float64)).astype(np.int64)
-    out = requantise(A, prm)
-    return out, m, E, P.astype(np.uint8)
+    return P.astype(np.uint8), m, E
+
+
+def pv_requant(P, vh, prm: Params):
+    """out int8 [Sq, D] = requantise(P.V) (methodology step 3: the value
+    product stays integer; the int32 accumulator returns to int8)."""
+    A = np.rint(np.asarray(P).astype(np.float64) @ vh.astype(np.float64)).astype(np.int64)
+    return requantise(A, prm)
+
+
+def head_forward(qh, kh, vh, prm: Params, causal: bool):
+    """One (b, h) slice. Returns out int8 [Sq, D], m int64 [Sq], E int64 [Sq],
+    P uint8 [Sq, Skv]."""
+    S = qk_scores(qh, kh)
+    P, m, E = index_softmax(S, prm, causal)
+    out = pv_requant(P, vh, prm)
+    return out, m, E, P
 
 
 def check_args(q, k, v, causal):

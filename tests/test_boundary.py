@@ -6,6 +6,7 @@
 * every argument error is reported before any HIP call (so these run on a
   machine without a GPU) and with the documented code.
 """
+import ctypes
 import math
 import os
 import re
@@ -30,7 +31,8 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     names = _declared()
     assert names == sorted(["intattn_build_lut", "intattn_derive_params", "intattn_forward",
-                            "intattn_forward_debug", "intattn_strerror"])
+                            "intattn_forward_debug", "intattn_strerror", "intattn_qk_scores",
+                            "intattn_index_softmax", "intattn_fp_softmax", "intattn_pv"])
     for n in names:
         assert hasattr(B._lib, n), n
 
@@ -109,3 +111,49 @@ def test_empty_problems_are_noops():
     assert _call(shape=(2, 0, 512, 512, 64)) == 0
     assert _call(shape=(2, 3, 0, 7, 128), causal=True) == 0
     assert _call(shape=(0, 12, 512, 512, 64), debug=(0x5000, 0x6000, None)) == 0
+
+
+def _stage(fn, shape=(1, 1, 8, 8, 64), scales=(0.05, 0.05, 0.05, 0.05), clip=B.DEFAULT_CLIP, causal=False,
+           ptrs=(0x1000, 0x2000, 0x3000, 0x4000)):
+    sh = B.Shape(*shape)
+    sc = B.Scales(*scales)
+    a, b, c, d = ptrs
+    if fn == "qk":
+        return B._lib.intattn_qk_scores(a, b, c, ctypes.byref(sh), None)
+    if fn == "isoftmax":
+        return B._lib.intattn_index_softmax(a, b, c, d, ctypes.byref(sh), ctypes.byref(sc), clip, int(causal), None)
+    if fn == "fpsoftmax":
+        return B._lib.intattn_fp_softmax(a, b, ctypes.byref(sh), ctypes.byref(sc), int(causal), None)
+    return B._lib.intattn_pv(a, b, c, ctypes.byref(sh), ctypes.byref(sc), clip, int(causal), None)
+
+
+def test_stage_validation_errors_before_any_device_call():
+    E = {v: k for k, v in B.STATUS_NAMES.items()}
+    for fn in ("qk", "isoftmax", "fpsoftmax", "pv"):
+        assert _stage(fn, ptrs=(0, 0x2000, 0x3000, 0x4000)) == E["INTATTN_E_NULL"], fn
+        assert _stage(fn, shape=(1, 1, 8, 0, 64)) == E["INTATTN_E_SHAPE"], fn
+        assert _stage(fn, shape=(1, 1, 8, 8, 96)) == E["INTATTN_E_DIM"], fn
+    # alignment: q/k 16 bytes and scores 4 bytes; scores 4 bytes; v/out 16 bytes
+    assert _stage("qk", ptrs=(0x1008, 0x2000, 0x3000, 0)) == E["INTATTN_E_ALIGN"]
+    assert _stage("qk", ptrs=(0x1000, 0x2000, 0x3002, 0)) == E["INTATTN_E_ALIGN"]
+    assert _stage("isoftmax", ptrs=(0x1002, 0x2000, 0x3000, 0x4000)) == E["INTATTN_E_ALIGN"]
+    assert _stage("fpsoftmax", ptrs=(0x1001, 0x2000, 0, 0)) == E["INTATTN_E_ALIGN"]
+    assert _stage("pv", ptrs=(0x1001, 0x2008, 0x3000, 0)) == E["INTATTN_E_ALIGN"]
+    # softmax stages hold a row in registers: Skv <= 4096
+    assert _stage("isoftmax", shape=(1, 1, 8, 4097, 64)) == E["INTATTN_E_SHAPE"]
+    assert _stage("fpsoftmax", shape=(1, 1, 8, 4097, 64)) == E["INTATTN_E_SHAPE"]
+    # row statistics: both or neither
+    assert _stage("isoftmax", ptrs=(0x1000, 0x2000, 0x3000, 0)) == E["INTATTN_E_NULL"]
+    assert _stage("isoftmax", ptrs=(0x1000, 0x2000, 0, 0x4000)) == E["INTATTN_E_NULL"]
+    # parameters: as intattn_forward for the integer stages, positive finite s_q, s_k for the comparator
+    assert _stage("isoftmax", scales=(3.0, 3.0, 0.05, 0.05)) == E["INTATTN_E_RANGE"]
+    assert _stage("pv", clip=math.nan) == E["INTATTN_E_CLIP"]
+    assert _stage("fpsoftmax", scales=(0.0, 0.05, 0.05, 0.05)) == E["INTATTN_E_SCALE"]
+    assert _stage("fpsoftmax", shape=(1, 1, 9, 8, 64), causal=True) == E["INTATTN_E_SHAPE"]
+
+
+def test_stage_empty_problems_are_noops():
+    for fn in ("qk", "isoftmax", "fpsoftmax", "pv"):
+        assert _stage(fn, shape=(0, 12, 512, 512, 64), ptrs=(0x1000, 0x2000, 0x3000, 0x4000)) == 0, fn
+        assert _stage(fn, shape=(2, 3, 0, 7, 128), ptrs=(0x1000, 0x2000, 0x3000, 0x4000)) == 0, fn
+
