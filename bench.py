@@ -22,6 +22,7 @@ they do not stay in the caches) gives the cold-input rate.
 
     python bench.py --calibrate peaks   # measured copy GB/s, int8 MFMA TOPS, VALU ops/s
     python bench.py --calibrate copy    # three 256 MiB device copies (counter scaling run)
+    python bench.py --breakdown         # per-stage times of the unfused pipelines
 """
 from __future__ import annotations
 
@@ -220,6 +221,84 @@ def calibrate(mode):
     return 0
 
 
+def breakdown(config, steps=None):
+    """Per-stage times of the pipeline run as separate kernels (scores and P in
+    HBM), with the integer softmax and with the float32 comparator, beside the
+    fused call: the softmax share of each pipeline and the speedups."""
+    import torch
+
+    from integer_only_quantized_amd import _binding as ia
+    from integer_only_quantized_amd import workloads as W
+
+    w = W.make_config(config)
+    if w.Skv > 4096:
+        raise SystemExit(f"--breakdown needs Skv <= 4096 (the softmax stages hold a row in registers); "
+                         f"{config} has Skv = {w.Skv}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
+    B, H, Sq, Skv, D = w.shape
+    S = torch.empty((B, H, Sq, Skv), dtype=torch.int32, device=dev)
+    P = torch.empty((B, H, Sq, Skv), dtype=torch.uint8, device=dev)
+    C = torch.empty_like(P)
+    out = torch.empty_like(q)
+    outc = torch.empty_like(q)
+    calls = {
+        "fused": lambda: ia.forward(q, k, v, w.scales, w.clip, w.causal, out=out),
+        "qk_scores": lambda: ia.qk_scores(q, k, out=S),
+        "index_softmax": lambda: ia.index_softmax(S, D, w.scales, w.clip, w.causal, probs=P),
+        "fp_softmax": lambda: ia.fp_softmax(S, D, w.scales, w.causal, probs=C),
+        "pv": lambda: ia.pv(P, v, w.scales, w.clip, w.causal, out=outc),
+    }
+    for name in ("qk_scores", "index_softmax", "fp_softmax", "pv", "fused"):
+        calls[name]()
+    torch.cuda.synchronize(dev)
+    if not torch.equal(outc, out):
+        raise RuntimeError("the integer stages chained differ from the fused call")
+    stream = torch.cuda.current_stream(dev)
+    times = {}
+    for name, fn in calls.items():
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:      # warm-up (clock ramp)
+            fn()
+        torch.cuda.synchronize(dev)
+        n = steps or 200
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        times[name] = e0.elapsed_time(e1) / n * 1e3      # us per call
+    _, _, scores = algorithmic_work(w)
+    n_sc = B * H * Sq * Skv
+    hbm = {   # bytes each stage moves at least once
+        "qk_scores": B * H * (Sq + Skv) * D + 4 * n_sc,
+        "index_softmax": 5 * n_sc,
+        "fp_softmax": 5 * n_sc,
+        "pv": n_sc + B * H * (Skv + Sq) * D,
+    }
+    t_int = times["qk_scores"] + times["index_softmax"] + times["pv"]
+    t_fp = times["qk_scores"] + times["fp_softmax"] + times["pv"]
+    line = {
+        "breakdown": config,
+        "shape": {"B": B, "H": H, "Sq": Sq, "Skv": Skv, "D": D, "causal": w.causal},
+        "us_per_call": times,
+        "stage_GBs": {k2: hbm[k2] / (times[k2] * 1e-6) / 1e9 for k2 in hbm},
+        "stage_hbm_frac": {k2: hbm[k2] / (times[k2] * 1e-6) / 1e9 / PEAK_HBM_GBS for k2 in hbm},
+        "integer_pipeline_us": t_int,
+        "fp_pipeline_us": t_fp,
+        "softmax_share_integer_pipeline": times["index_softmax"] / t_int,
+        "softmax_share_fp_pipeline": times["fp_softmax"] / t_fp,
+        "speedup_integer_vs_fp_pipeline": t_fp / t_int,
+        "speedup_fused_vs_fp_pipeline": t_fp / times["fused"],
+        "softmax_stage_speedup": times["fp_softmax"] / times["index_softmax"],
+        "scores_allowed": scores,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +309,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calibrate", choices=["peaks", "copy"], default=None)
+    ap.add_argument("--breakdown", action="store_true",
+                    help="per-stage times of the unfused pipelines (integer and float32 softmax)")
     ap.add_argument("--no-extra-timing", action="store_true",
                     help="skip the median-of-5 and cold-input blocks")
     args = ap.parse_args(argv)
@@ -242,6 +323,8 @@ def main(argv=None):
 
     if args.calibrate:
         return calibrate(args.calibrate)
+    if args.breakdown:
+        return breakdown(args.config, args.steps)
 
     import numpy as np
     import torch

@@ -51,6 +51,10 @@ def library_path() -> str:
 
 
 def _load():
+    # torch ships its own HIP runtime: load it before this library, so the
+    # process has one runtime and torch's device memory is the library's too
+    # (a library loaded first would bring in the system's runtime instead)
+    import torch  # noqa: F401
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
             f"{_LIB_PATH} is not built; run `python -m integer_only_quantized_amd.build` "

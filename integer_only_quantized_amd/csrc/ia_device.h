@@ -76,6 +76,25 @@ __device__ __forceinline__ uint32_t slot_word_sat(int32_t y, int32_t negM4, int3
     return static_cast<uint32_t>(t);
 }
 
+// Byte address of a slot word's exp-table entry (table of u32 at LDS 0), one
+// SDWA op: FAST words (4M < 2^23) have 4 * slot + fraction in the top byte,
+// so the address is that byte & 0x7c; otherwise the top byte is
+// min(127, slot) (the word is at most 2^31 - 1) and the address is 4 * byte
+// into a 128-entry table whose entries 31..127 are zero.
+template <bool FAST>
+__device__ __forceinline__ uint32_t lut_byte_addr(uint32_t t) {
+    uint32_t a;
+    if constexpr (FAST) {
+        const uint32_t m = 0x7cu;
+        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD"
+            : "=v"(a) : "v"(t), "s"(m));
+    } else {
+        asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+            : "=v"(a) : "v"(t));
+    }
+    return a;
+}
+
 // int32 accumulator -> int8: sign(a) * min(127, (|a|*M_o + 2^(sh_o-1)) >> sh_o).
 __device__ __forceinline__ int8_t requantise(int32_t a, const IaKernelParams& P) {
     const uint32_t mag = static_cast<uint32_t>(a < 0 ? -a : a);

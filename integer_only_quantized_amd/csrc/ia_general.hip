@@ -247,6 +247,8 @@ __global__ __launch_bounds__(256) void ia_general_kernel(
 
 }  // namespace
 
+void clear_pending_hip_error() { (void)hipGetLastError(); }
+
 int launch_general(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
                    const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum,
                    uint8_t* probs) {

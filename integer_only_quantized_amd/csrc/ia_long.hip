@@ -227,12 +227,9 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     for (int r = 0; r < 16; ++r) cinit[r] = -mrow;
     const int32_t negMs = FAST ? -4 * P.idx_mul : -P.idx_mul;
     const int32_t halfs = FAST ? (1 << 25) : (1 << 23);
-    // table byte address of the slot word
-    auto lut_addr = [&](uint32_t t) -> uint32_t {
-        if constexpr (FAST) return (t >> 24) & 0x7cu;
-        else return (t >> 22) & 0x1fcu;
+    auto table_entry = [&](int32_t y) -> uint32_t {
+        return lds_u32(lut_byte_addr<FAST>(slot_word_sat(y, negMs, halfs)));
     };
-    auto table_entry = [&](int32_t y) -> uint32_t { return lds_u32(lut_addr(slot_word_sat(y, negMs, halfs))); };
     constexpr int32_t kMasked = -(1 << 23);   // y of a masked key: saturates to the last slot
 
     // ---- pass 2: row sum of the table entries ------------------------------

@@ -212,8 +212,7 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     t[c] = slot_word_sat(cur[4 * w4 + c], negMs, halfs);
-                    const uint32_t a = FAST ? ((t[c] >> 24) & 0x7cu) : ((t[c] >> 22) & 0x1fcu);
-                    e[4 * w4 + c] = lds_u32(a);
+                    e[4 * w4 + c] = lds_u32(lut_byte_addr<FAST>(t[c]));
                 }
                 // top bytes: FAST 4 * slot + fraction; otherwise min(127, slot)
                 idxw[j][w4] = pack_top_bytes(t[0], t[1], t[2], t[3]);

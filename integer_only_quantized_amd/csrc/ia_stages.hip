@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void ia_index_softmax_kernel(const int32_t* __
     for (int c = 0; c < NCH; ++c) {
         const int32_t y = 64 * c + lane < kend ? max(s[c] - m, -(1 << 23)) : -(1 << 23);
         const uint32_t t = slot_word_sat(y, negMs, halfs);
-        e[c] = lut[FAST ? ((t >> 24) & 0x7cu) >> 2 : (t >> 24)];
+        e[c] = lds_u32(lds_addr(lut) + lut_byte_addr<FAST>(t));
         E += e[c];
     }
     E = wave_sum(E);

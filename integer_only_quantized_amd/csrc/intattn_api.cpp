@@ -76,6 +76,7 @@ extern "C" int intattn_forward(const int8_t* q, const int8_t* k, const int8_t* v
     const int st = prepare(q, k, v, out, shape, scales, clip, causal, &kp);
     if (st != INTATTN_OK) return st;
     if (static_cast<long long>(kp.B) * kp.H * kp.Sq == 0) return INTATTN_OK;
+    ia::clear_pending_hip_error();
     return dispatch(q, k, v, out, shape->D, kp, stream, nullptr, nullptr);
 }
 
@@ -88,6 +89,7 @@ extern "C" int intattn_forward_debug(const int8_t* q, const int8_t* k, const int
     const int st = prepare(q, k, v, out, shape, scales, clip, causal, &kp);
     if (st != INTATTN_OK) return st;
     if (static_cast<long long>(kp.B) * kp.H * kp.Sq == 0) return INTATTN_OK;
+    ia::clear_pending_hip_error();
     if (probs != nullptr)
         return ia::launch_general(q, k, v, out, shape->D, kp, stream, row_max, row_sum, probs);
     return dispatch(q, k, v, out, shape->D, kp, stream, row_max, row_sum);
@@ -106,6 +108,7 @@ extern "C" int intattn_qk_scores(const int8_t* q, const int8_t* k, int32_t* scor
     kp.Sq = shape->Sq;
     kp.Skv = shape->Skv;
     if (rows_of(kp) == 0) return INTATTN_OK;
+    ia::clear_pending_hip_error();
     return ia::launch_qk_scores(q, k, scores, shape->D, kp, stream);
 }
 
@@ -120,6 +123,7 @@ extern "C" int intattn_index_softmax(const int32_t* scores, uint8_t* probs, int3
     if (st != INTATTN_OK) return st;
     if (kp.Skv > ia::stage_max_keys()) return INTATTN_E_SHAPE;
     if (rows_of(kp) == 0) return INTATTN_OK;
+    ia::clear_pending_hip_error();
     return ia::launch_index_softmax(scores, probs, row_max, row_sum, kp, stream);
 }
 
@@ -143,6 +147,7 @@ extern "C" int intattn_fp_softmax(const int32_t* scores, uint8_t* probs, const i
     // dequantisation factor of a score: s_q * s_k / sqrt(D), rounded once to float32
     const float alpha = static_cast<float>(static_cast<double>(scales->q) * static_cast<double>(scales->k) /
                                            std::sqrt(static_cast<double>(shape->D)));
+    ia::clear_pending_hip_error();
     return ia::launch_fp_softmax(scores, probs, alpha, kp, stream);
 }
 
@@ -154,5 +159,6 @@ extern "C" int intattn_pv(const uint8_t* probs, const int8_t* v, int8_t* out, co
     const int st = derive_kernel_params(shape, scales, clip, causal, &kp);
     if (st != INTATTN_OK) return st;
     if (rows_of(kp) == 0) return INTATTN_OK;
+    ia::clear_pending_hip_error();
     return ia::launch_pv(probs, v, out, shape->D, kp, stream);
 }

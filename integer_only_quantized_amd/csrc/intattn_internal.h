@@ -24,6 +24,10 @@ struct IaKernelParams {
 
 namespace ia {
 
+// Clears an error left pending in this thread by earlier, unrelated HIP
+// calls, so that the status read after a launch is that launch's own.
+void clear_pending_hip_error();
+
 // Each launcher queues one kernel on `stream` (a hipStream_t) and returns
 // INTATTN_OK or INTATTN_E_HIP / INTATTN_E_SHAPE. row_max / row_sum are
 // optional per-row outputs [B, H, Sq] (both NULL or both set).

@@ -58,11 +58,13 @@ extern "C" {
 // launch fails. Work: probe_mfma: 4 * iters * 65536 ops per wave;
 // probe_valu: 8 * iters multiply-adds per lane.
 int intattn_probe_mfma_i8(int blocks, int iters, int32_t* sink, void* stream) {
+    (void)hipGetLastError();   // report this launch's status only
     hipLaunchKernelGGL(probe_mfma_i8, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int intattn_probe_valu(int blocks, int iters, int32_t* sink, void* stream) {
+    (void)hipGetLastError();   // report this launch's status only
     hipLaunchKernelGGL(probe_valu, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
