@@ -55,7 +55,7 @@ struct ShortLds {
     int8_t kv[Region];                       // K, then V, then the output partials
 };
 
-template <int D, int NBH, bool FAST>
+template <int D, int NBH, bool FAST, bool SKIP>
 __global__ __launch_bounds__(256) void ia_short_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, const int8_t* __restrict__ v,
     int8_t* __restrict__ out, const IaKernelParams P, int nqb, int32_t* __restrict__ row_max,
@@ -129,6 +129,20 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     const int kend_row = P.causal ? min(P.Skv, qrow + shift + 1) : P.Skv;
     const int kend_wave = P.causal ? min(P.Skv, qw0 + shift + 1) : P.Skv;
     const int kb0 = half * NBH;                        // first key block of this wave
+    // 32-key blocks of key half h that some row of query group g attends
+    // (none for a group past Sq; causal: up to the group's last row); blocks
+    // past that are skipped in every pass (their p would all be 0). Without
+    // SKIP every block of both halves is attended by both groups.
+    auto nvalid_of = [&](int g, int h) -> int {
+        const int qa = qb * 64 + 32 * g;
+        if (qa >= P.Sq) return 0;
+        const int kmax = P.causal ? min(P.Skv, min(qa + 31, P.Sq - 1) + shift + 1) : P.Skv;
+        return min(NBH, max(0, (kmax - 32 * h * NBH + 31) / 32));
+    };
+    const int nvalid = SKIP ? nvalid_of(qg, half) : NBH;
+    // column sums shared between the two query groups (each sums every other
+    // block) only when both groups feed the same blocks in both halves
+    const bool share_cs = !SKIP || (nvalid_of(0, 0) == nvalid_of(1, 0) && nvalid_of(0, 1) == nvalid_of(1, 1));
 
     v4i qf[KS];
 #pragma unroll
@@ -170,16 +184,19 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     const v16i zero16 = v16i{};
     int32_t mrow = INT_MIN;
     {
-        v16i cur = scores(kb0, zero16);
+        v16i cur = zero16;
+        if (nvalid > 0) cur = scores(kb0, zero16);
 #pragma unroll
         for (int j = 0; j < NBH; ++j) {
-            v16i nxt;
-            if (j + 1 < NBH) nxt = scores(kb0 + j + 1, zero16);
-            mask(cur, kb0 + j, INT_MIN);
+            v16i nxt = zero16;
+            if (j + 1 < nvalid) nxt = scores(kb0 + j + 1, zero16);
+            if (j < nvalid) {
+                mask(cur, kb0 + j, INT_MIN);
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) mrow = max(max(mrow, cur[r]), cur[r + 1]);
-            // keep the reduction per block (not one cross-block tree at the end)
-            asm volatile("" : "+v"(mrow));
+                for (int r = 0; r < 16; r += 2) mrow = max(max(mrow, cur[r]), cur[r + 1]);
+                // keep the reduction per block (not one cross-block tree at the end)
+                asm volatile("" : "+v"(mrow));
+            }
             if (j + 1 < NBH) cur = nxt;
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -199,11 +216,18 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
         v16i cinit;
 #pragma unroll
         for (int r = 0; r < 16; ++r) cinit[r] = -mrow;
-        v16i cur = scores(kb0, cinit);
+        v16i cur = cinit;
+        if (nvalid > 0) cur = scores(kb0, cinit);
 #pragma unroll
         for (int j = 0; j < NBH; ++j) {
-            v16i nxt;
-            if (j + 1 < NBH) nxt = scores(kb0 + j + 1, cinit);
+            v16i nxt = cinit;
+            if (j + 1 < nvalid) nxt = scores(kb0 + j + 1, cinit);
+            if (j >= nvalid) {
+                idxw[j][0] = idxw[j][1] = idxw[j][2] = idxw[j][3] = 0;   // never read
+                if (j + 1 < NBH) cur = nxt;
+                __builtin_amdgcn_sched_barrier(0);
+                continue;
+            }
             mask(cur, kb0 + j, kMasked);
             uint32_t e[16];
 #pragma unroll
@@ -231,7 +255,10 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     lds_barrier();                       // every wave is also done with K
     stage(vh, true);                     // V replaces K
     E += lds.xe[qg][half ^ 1][l32];
-    const uint32_t R = ((255u << 23) + (E >> 1)) / E;
+    // E >= 2^15 for every row that exists (it attends at least one key); rows
+    // past Sq may have E = 0 and are never stored
+    const uint32_t Ed = SKIP ? max(E, 1u) : E;
+    const uint32_t R = ((255u << 23) + (Ed >> 1)) / Ed;
     const uint32_t R2 = 2 * R;
     if (row_max != nullptr && half == 0 && hh == 0 && qrow < P.Sq) {
         row_max[head * P.Sq + qrow] = mrow;
@@ -294,21 +321,29 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     }
     {
         uint32_t pl[16];
-        plookup(0, pl);
-        v4i pa = ppack(pl);
-        if (NBH > 1) plookup(1, pl);
+        v4i pa = v4i{0, 0, 0, 0};
+        if (nvalid > 0) {
+            plookup(0, pl);
+            pa = ppack(pl);
+        }
+        if (nvalid > 1) plookup(1, pl);
         static_for<NBH>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            v4i pnext;
-            if constexpr (j + 1 < NBH) pnext = ppack(pl);
-            if constexpr (j + 2 < NBH) plookup(j + 2, pl);
+            v4i pnext = v4i{0, 0, 0, 0};
+            if constexpr (j + 1 < NBH) {
+                if (j + 1 < nvalid) pnext = ppack(pl);
+            }
+            if constexpr (j + 2 < NBH) {
+                if (j + 2 < nvalid) plookup(j + 2, pl);
+            }
+            if (j >= nvalid) return;
             v4i vb[DB];
             tr8_operands<DB, j * 32 * D>(vaddr, vb);
 #pragma unroll
             for (int db = 0; db < DB; ++db) o[db] = mfma_i8_32x32x32(pa, vb[db], o[db]);
-            // the two query-group waves of a half see the same V blocks: each
-            // sums the columns of every other block (asm: no speculation)
-            if ((j & 1) == qg) {
+            // column sums of the V rows fed: when both query groups feed the
+            // same blocks, each sums every other block (asm: no speculation)
+            if (!share_cs || (j & 1) == qg) {
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     asm volatile("" : "+v"(cs[db]));
@@ -374,7 +409,11 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
             constexpr int j = decltype(jc)::value;
             constexpr int db = H * HDB + j;
             const int d = 32 * db + l32;
-            const int32_t c128 = 128 * (lds.xcs[0][d] + lds.xcs[1][d] + lds.xcs[2][d] + lds.xcs[3][d]);
+            // shared sums: all four waves' partials; otherwise this query
+            // group's two waves (wave = 2 * half + query group)
+            const int32_t csum = share_cs ? lds.xcs[0][d] + lds.xcs[1][d] + lds.xcs[2][d] + lds.xcs[3][d]
+                                          : lds.xcs[qg][d] + lds.xcs[2 + qg][d];
+            const int32_t c128 = 128 * csum;
             int32_t acc[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -396,12 +435,24 @@ int launch_short_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* ou
     const int nqb = (kp.Sq + 63) / 64;
     const long long blocks = static_cast<long long>(kp.B) * kp.H * nqb;
     if (blocks > INT_MAX) return INTATTN_E_SHAPE;
-    if (fast)
-        hipLaunchKernelGGL((ia_short_kernel<D, NBH, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                           stream, q, k, v, out, kp, nqb, row_max, row_sum);
+    // some 32-key block goes unattended by a whole query group: causal rows,
+    // an empty trailing query group, or a second key half shorter than NBH
+    // blocks
+    const int tail_rows = kp.Sq % 64;
+    const bool skip = kp.causal || (tail_rows != 0 && tail_rows <= 32) || kp.Skv <= 64 * NBH - 32;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (fast && skip)
+        hipLaunchKernelGGL((ia_short_kernel<D, NBH, true, true>), grid, dim3(256), 0, stream, q, k, v, out, kp,
+                           nqb, row_max, row_sum);
+    else if (fast)
+        hipLaunchKernelGGL((ia_short_kernel<D, NBH, true, false>), grid, dim3(256), 0, stream, q, k, v, out, kp,
+                           nqb, row_max, row_sum);
+    else if (skip)
+        hipLaunchKernelGGL((ia_short_kernel<D, NBH, false, true>), grid, dim3(256), 0, stream, q, k, v, out, kp,
+                           nqb, row_max, row_sum);
     else
-        hipLaunchKernelGGL((ia_short_kernel<D, NBH, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                           stream, q, k, v, out, kp, nqb, row_max, row_sum);
+        hipLaunchKernelGGL((ia_short_kernel<D, NBH, false, false>), grid, dim3(256), 0, stream, q, k, v, out, kp,
+                           nqb, row_max, row_sum);
     return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
 }
 

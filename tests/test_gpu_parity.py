@@ -83,6 +83,13 @@ EDGE = [
     (1, 2, 1, 16385, 64, True, 115, "normal"),        # one key past it: general kernel
     (4, 2, 1, 255, 128, False, 116, "channel_outliers"),
     (1, 1, 1, 5, 64, False, 117, "student_t_tail"),
+    # short-row block skipping: causal blocks past a query group's last row,
+    # empty trailing query groups, key blocks past Skv
+    (2, 2, 512, 512, 64, True, 118, "channel_outliers"),
+    (1, 2, 100, 300, 64, True, 119, "normal"),
+    (1, 2, 33, 40, 128, True, 120, "normal"),
+    (2, 1, 70, 197, 64, False, 121, "normal"),
+    (1, 1, 250, 250, 128, True, 122, "student_t_tail"),
 ]
 
 
