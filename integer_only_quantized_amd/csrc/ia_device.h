@@ -96,23 +96,27 @@ __device__ __forceinline__ uint32_t lut_byte_addr(uint32_t t) {
 }
 
 // int32 accumulator -> int8: sign(a) * min(127, (|a|*M_o + 2^(sh_o-1)) >> sh_o).
+// One signed product instead of magnitude and sign: with h = 2^(sh-1),
+// -floor((|a|M + h) / 2^sh) = floor((aM + 2^sh - 1 - h) / 2^sh) for a < 0, so
+// the result is clamp(floor((aM + h + s) / 2^sh), -127, 127) with s = a >> 31
+// (0 or -1). M_o < 2^31 and |a| < 2^31 keep |aM + h + s| < 2^63.
 __device__ __forceinline__ int8_t requantise(int32_t a, const IaKernelParams& P) {
-    const uint32_t mag = static_cast<uint32_t>(a < 0 ? -a : a);
-    const uint64_t prod = static_cast<uint64_t>(mag) * P.req_mul + (uint64_t(1) << (P.req_shift - 1));
-    uint64_t qv = prod >> P.req_shift;
-    if (qv > 127) qv = 127;
-    return static_cast<int8_t>(a < 0 ? -static_cast<int32_t>(qv) : static_cast<int32_t>(qv));
+    const int64_t x = static_cast<int64_t>(a) * static_cast<int32_t>(P.req_mul) +
+                      ((int64_t(1) << (P.req_shift - 1)) + (a >> 31));
+    const int32_t r = static_cast<int32_t>(max(min(x >> P.req_shift, int64_t(127)), int64_t(-127)));
+    return static_cast<int8_t>(r);
 }
 
-// The same for shifts sh >= 33 in 32-bit arithmetic: 2^(sh-1) is then a
-// multiple of 2^32, so with |a| * M_o = hi * 2^32 + lo,
-//   (|a| * M_o + 2^(sh-1)) >> sh = (hi + 2^(sh-33)) >> (sh-32)
-// (lo / 2^32 < 1 cannot carry an integer numerator across a multiple of
-// 2^(sh-32)); hi + 2^(sh-33) < 2^31. add = 2^(sh-33), rsh = sh - 32.
+// The same for shifts sh >= 33: h + s = (2^(sh-33) + s) * 2^32 + (s mod 2^32),
+// and floor(x / 2^sh) = floor(hi32(x) / 2^(sh-32)), hi32(x) in (-2^31, 2^31).
+// add = 2^(sh-33), rsh = sh - 32.
 __device__ __forceinline__ int32_t requantise_hi(int32_t a, uint32_t mul, uint32_t add, uint32_t rsh) {
-    const uint32_t mag = static_cast<uint32_t>(a < 0 ? -a : a);
-    const uint32_t q = min((__umulhi(mag, mul) + add) >> rsh, 127u);
-    return a < 0 ? -static_cast<int32_t>(q) : static_cast<int32_t>(q);
+    const int32_t s = a >> 31;
+    const uint64_t c = static_cast<uint64_t>(static_cast<uint32_t>(s)) |
+                       (static_cast<uint64_t>(add + static_cast<uint32_t>(s)) << 32);
+    const int64_t x = static_cast<int64_t>(a) * static_cast<int32_t>(mul) + static_cast<int64_t>(c);
+    const int32_t r = static_cast<int32_t>(static_cast<uint64_t>(x) >> 32) >> rsh;
+    return min(max(r, -127), 127);
 }
 
 // Entry k of the exp table from the packed kernel argument. The argument
@@ -175,16 +179,21 @@ __device__ __forceinline__ void wait_vmcnt_c() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// The same for a count known only at run time (wave-uniform); a constant
+// argument folds to the one s_waitcnt. Counts above 31 wait for everything.
 __device__ __forceinline__ void wait_vmcnt(int n) {
-    // s_waitcnt with only the vector-memory counter constrained (lgkm/exp at max)
+#define IA_VMCNT_CASE(N) \
+    case N: wait_vmcnt_c<N>(); break;
     switch (n) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        IA_VMCNT_CASE(0) IA_VMCNT_CASE(1) IA_VMCNT_CASE(2) IA_VMCNT_CASE(3) IA_VMCNT_CASE(4) IA_VMCNT_CASE(5)
+        IA_VMCNT_CASE(6) IA_VMCNT_CASE(7) IA_VMCNT_CASE(8) IA_VMCNT_CASE(9) IA_VMCNT_CASE(10) IA_VMCNT_CASE(11)
+        IA_VMCNT_CASE(12) IA_VMCNT_CASE(13) IA_VMCNT_CASE(14) IA_VMCNT_CASE(15) IA_VMCNT_CASE(16)
+        IA_VMCNT_CASE(17) IA_VMCNT_CASE(18) IA_VMCNT_CASE(19) IA_VMCNT_CASE(20) IA_VMCNT_CASE(21)
+        IA_VMCNT_CASE(22) IA_VMCNT_CASE(23) IA_VMCNT_CASE(24) IA_VMCNT_CASE(25) IA_VMCNT_CASE(26)
+        IA_VMCNT_CASE(27) IA_VMCNT_CASE(28) IA_VMCNT_CASE(29) IA_VMCNT_CASE(30) IA_VMCNT_CASE(31)
+        default: wait_vmcnt_c<0>(); break;
     }
+#undef IA_VMCNT_CASE
 }
 
 // Workgroup barrier: this wave's LDS operations complete, then all waves
@@ -202,6 +211,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 32-bit LDS load from a byte address (the kernel's LDS block starts at 0).
 __device__ __forceinline__ uint32_t lds_u32(uint32_t addr) {
     return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(static_cast<uintptr_t>(addr));
+}
+
+// Scheduling fence over 16 values: every load feeding them completes here,
+// together (one wait for the batch instead of one per value).
+__device__ __forceinline__ void pin16(int32_t (&a)[16]) {
+    asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
+                      "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]),
+                      "+v"(a[14]), "+v"(a[15]));
 }
 
 // P.V B operand from a row-major V block of 32 keys in LDS (rows of D bytes,

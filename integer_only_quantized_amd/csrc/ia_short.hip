@@ -41,6 +41,14 @@ namespace ia {
 namespace {
 
 constexpr int kShortLut = 128;
+// Staging of a key block: split between the two query-group waves of its key
+// half (each loads part of it; a workgroup barrier per block makes the other
+// part visible), or loaded whole by both (identical bytes; each wave waits
+// only for its own loads, no barrier). Splitting halves the L2->LDS traffic
+// of the start-up burst, which pays only for the longest full rows (measured:
+// 512 keys at d = 64); elsewhere the per-block barriers cost more.
+template <int NBH, bool SKIP>
+constexpr bool split_k_staging() { return NBH >= 8 && !SKIP; }
 
 template <int D, int NBH>
 struct ShortLds {
@@ -52,6 +60,7 @@ struct ShortLds {
     int32_t xm[2][2][32];                    // row max exchange [query group][half][row]
     uint32_t xe[2][2][32];                   // row sum exchange
     int32_t xcs[4][D];                       // column-sum partials, one per wave
+    int8_t q[2][32 * D];                     // Q rows of each query group (K-block layout)
     int8_t kv[Region];                       // K, then V, then the output partials
 };
 
@@ -65,7 +74,6 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     constexpr int DB = D / 32;
     constexpr int HDB = DB / 2;                        // output column blocks finished per wave
     constexpr int CPR = D / 16;                        // 16-byte chunks per row
-    constexpr int LOADS = L::KVBytes / 1024 / 4;       // 1 KB global->LDS loads per wave
     __shared__ __attribute__((aligned(16))) L lds;
 
     const int tid = threadIdx.x;
@@ -83,14 +91,19 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     const int8_t* kh = k + head * P.Skv * D;
     const int8_t* vh = v + head * P.Skv * D;
 
-    // ---- stage K (both halves) -------------------------------------------------
-    // Load i of wave w fills LDS bytes [(w*LOADS + i) KB, +1 KB): lane l writes
-    // row (1 KB offset)/D + l/CPR, stored chunk l % CPR = logical chunk
+    // ---- staging ---------------------------------------------------------------
+    // Each wave stages the key blocks of its own half that it reads (the two
+    // query-group waves of a half write the same bytes to the same place), so
+    // a wave waits only for its own loads, block by block, and no barrier
+    // precedes pass 1 or pass 3. Block j of half h is LPB loads of 1 KB; load
+    // i of it fills LDS KB blk = (h*NBH + j)*LPB + i: lane l writes row
+    // blk*(1024/D) + l/CPR, stored chunk l % CPR = logical chunk
     // (l % CPR) ^ swizzle(row).
     // The source offset of load blk is blk*1024 plus a per-lane constant that
     // depends only on the parity of blk (the swizzles use the row's low bits),
     // so the loads take a scalar base; rows past Skv (a uniform tail case)
     // are clamped per lane.
+    constexpr int LPB = D / 32;
     uint32_t koff[2], voff[2];
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
@@ -99,29 +112,44 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
         voff[par] = static_cast<uint32_t>(row * D + 16 * ((lane % CPR) ^ v_swz<D>(row)) - par * 1024);
     }
     const bool stage_tail = L::KVBytes / D > P.Skv;     // some staged rows lie past Skv
-    auto stage = [&](const int8_t* src, bool is_v) {
+    auto stage = [&](const int8_t* src, bool is_v, int kb_first, int nblk, bool split) {
         const uint32_t* off = is_v ? voff : koff;
+        const int i0 = split ? qg * (LPB / 2) : 0;
+        const int ni = split ? LPB / 2 : LPB;
         if (!stage_tail) {
 #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                const int blk = wave * LOADS + i;
-                __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(blk) * 1024 + off[blk & 1],
-                                                 (lds_void_t*)(lds.kv + blk * 1024), 16, 0, 0);
+            for (int j = 0; j < NBH; ++j) {
+                if (j >= nblk) break;
+#pragma unroll
+                for (int ii = 0; ii < LPB; ++ii) {
+                    if (ii >= ni) break;
+                    const int i = i0 + ii;
+                    const int blk = (kb_first + j) * LPB + i;
+                    __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(blk) * 1024 + off[blk & 1],
+                                                     (lds_void_t*)(lds.kv + blk * 1024), 16, 0, 0);
+                }
             }
+            // distinct markers keep the two paths apart (a merged last load
+            // would hide the count of loads in flight from the compiler)
+            asm volatile("; staged, no tail");
         } else {
 #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                const int blk = wave * LOADS + i;
-                const int row = blk * (1024 / D) + lane / CPR;
-                const int chunk = (lane % CPR) ^ (is_v ? v_swz<D>(row) : k_swz<D>(row));
-                __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(min(row, P.Skv - 1)) * D + 16 * chunk,
-                                                 (lds_void_t*)(lds.kv + blk * 1024), 16, 0, 0);
+            for (int j = 0; j < NBH; ++j) {
+                if (j >= nblk) break;
+#pragma unroll
+                for (int ii = 0; ii < LPB; ++ii) {
+                    if (ii >= ni) break;
+                    const int i = i0 + ii;
+                    const int blk = (kb_first + j) * LPB + i;
+                    const int row = blk * (1024 / D) + lane / CPR;
+                    const int chunk = (lane % CPR) ^ (is_v ? v_swz<D>(row) : k_swz<D>(row));
+                    __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(min(row, P.Skv - 1)) * D + 16 * chunk,
+                                                     (lds_void_t*)(lds.kv + blk * 1024), 16, 0, 0);
+                }
             }
+            asm volatile("; staged, tail rows clamped");
         }
     };
-    stage(kh, false);
-
-    if (tid < kShortLut) lds.lut[tid] = tid < 32 ? lut_entry(P, tid) : 0u;
 
     const int shift = P.Skv - P.Sq;
     const int qw0 = qb * 64 + qg * 32;
@@ -144,16 +172,53 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     // block) only when both groups feed the same blocks in both halves
     const bool share_cs = !SKIP || (nvalid_of(0, 0) == nvalid_of(1, 0) && nvalid_of(0, 1) == nvalid_of(1, 1));
 
-    v4i qf[KS];
+    // Q rows of this wave's query group, staged like a K block (both key-half
+    // waves of the group write the same bytes); rows past Sq read the last
+    // row and are computed but never stored. Q goes through LDS rather than
+    // straight into registers so that no register load is in flight behind
+    // the block-by-block waits below.
+    if (nvalid > 0) {
+        if (qw0 + 32 <= P.Sq) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        if (qrow < P.Sq)
-            qf[ks] = *reinterpret_cast<const v4i*>(qh + static_cast<size_t>(qrow) * D + 32 * ks + 16 * hh);
-        else
-            qf[ks] = v4i{0, 0, 0, 0};
+            for (int i = 0; i < LPB; ++i)
+                __builtin_amdgcn_global_load_lds(qh + static_cast<size_t>(qw0) * D + i * 1024 + koff[i & 1],
+                                                 (lds_void_t*)(&lds.q[qg][i * 1024]), 16, 0, 0);
+            asm volatile("; Q staged");
+        } else {
+#pragma unroll
+            for (int i = 0; i < LPB; ++i) {
+                const int row = i * (1024 / D) + lane / CPR;
+                const int chunk = (lane % CPR) ^ k_swz<D>(row);
+                __builtin_amdgcn_global_load_lds(qh + static_cast<size_t>(min(qw0 + row, P.Sq - 1)) * D + 16 * chunk,
+                                                 (lds_void_t*)(&lds.q[qg][i * 1024]), 16, 0, 0);
+            }
+            asm volatile("; Q staged, tail rows clamped");
+        }
     }
-    wait_vmcnt(0);
-    lds_barrier();
+    // blocks of this half that either query group reads (split staging
+    // loads these), and the most blocks any wave reads (the number of
+    // per-block barriers, the same in every wave)
+    const int nvp = SKIP ? max(nvalid_of(0, half), nvalid_of(1, half)) : NBH;
+    const int nv_max = SKIP ? max(nvp, max(nvalid_of(0, half ^ 1), nvalid_of(1, half ^ 1))) : NBH;
+    // K after Q: waiting for a K block also covers the (older) Q loads
+    constexpr bool kSplitK = split_k_staging<NBH, SKIP>();
+    stage(kh, false, kb0, kSplitK ? nvp : nvalid, kSplitK);
+    v4i qf[KS];                          // Q^T fragments, read from LDS in pass 1
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = v4i{0, 0, 0, 0};
+    if (tid < kShortLut) lds.lut[tid] = tid < 32 ? lut_entry(P, tid) : 0u;
+    // block j of this wave's half is in LDS: loads complete in issue order;
+    // whole-block staging issued nvalid blocks of LPB loads, split staging
+    // nvp blocks of LPB/2 loads, and then every wave meets at a barrier
+    // (executed for j < nv_max by all waves alike)
+    auto sync_block = [&](int j, bool split) {
+        if (!split) {
+            if (j < nvalid) wait_vmcnt((nvalid - 1 - j) * LPB);
+        } else if (j < nv_max) {
+            if (j < nvp) wait_vmcnt((nvp - 1 - j) * (LPB / 2));
+            lds_barrier();
+        }
+    };
 
     // S^T block kb (absolute) from accumulator c0
     auto scores = [&](int kb, const v16i& c0) {
@@ -185,10 +250,17 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     int32_t mrow = INT_MIN;
     {
         v16i cur = zero16;
-        if (nvalid > 0) cur = scores(kb0, zero16);
+        sync_block(0, kSplitK);
+        if (nvalid > 0) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qf[ks] = *reinterpret_cast<const v4i*>(&lds.q[qg][l32 * D + 16 * ((2 * ks + hh) ^ k_swz<D>(l32))]);
+            cur = scores(kb0, zero16);
+        }
 #pragma unroll
         for (int j = 0; j < NBH; ++j) {
             v16i nxt = zero16;
+            if (j + 1 < NBH) sync_block(j + 1, kSplitK);
             if (j + 1 < nvalid) nxt = scores(kb0 + j + 1, zero16);
             if (j < nvalid) {
                 mask(cur, kb0 + j, INT_MIN);
@@ -252,8 +324,8 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     }
     E += __shfl_xor(E, 32);
     if (hh == 0) lds.xe[qg][half][l32] = E;
-    lds_barrier();                       // every wave is also done with K
-    stage(vh, true);                     // V replaces K
+    lds_barrier();                       // every wave is also done with K (and its K loads)
+    stage(vh, true, kb0, nvalid, false);   // V replaces K (whole blocks)
     E += lds.xe[qg][half ^ 1][l32];
     // E >= 2^15 for every row that exists (it attends at least one key); rows
     // past Sq may have E = 0 and are never stored
@@ -272,8 +344,6 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
             vaddr[2 * db + rd] = static_cast<uint32_t>(offsetof(L, kv)) + static_cast<uint32_t>(kb0 * 32 * D) +
                                  tr8_lane_addr<D>(lane, db, rd);
     }
-    wait_vmcnt(0);
-    lds_barrier();
 
     // ---- pass 3: P from the slot bytes, P.V on the MFMA -------------------
     // table address of byte i of a kept slot word: FAST: byte & 0x7c;
@@ -336,6 +406,7 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
             if constexpr (j + 2 < NBH) {
                 if (j + 2 < nvalid) plookup(j + 2, pl);
             }
+            sync_block(j, false);
             if (j >= nvalid) return;
             v4i vb[DB];
             tr8_operands<DB, j * 32 * D>(vaddr, vb);
@@ -416,10 +487,11 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
             const int32_t c128 = 128 * csum;
             int32_t acc[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                acc[r] = o[db][r] + c128 + static_cast<int32_t>(lds_u32(xo_addr(1 - H, j, r)));
-                asm volatile("" : "+v"(acc[r]));    // all reads issued before the stores
-            }
+            for (int r = 0; r < 16; ++r) acc[r] = static_cast<int32_t>(lds_u32(xo_addr(1 - H, j, r)));
+            // all 16 reads in flight together, one wait (not one per read)
+            pin16(acc);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] += o[db][r] + c128;
             store_rows(acc, obase + d);
         });
     };
