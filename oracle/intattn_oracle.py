@@ -30,6 +30,19 @@ Arithmetic conventions
     sum is an integer of magnitude below 2**53 (|Q.K| <= D*127**2 and
     |P.V| <= Skv*255*127), so any summation order gives the exact integer.
 
+Variants (the pages' "Limitations & Future Work" name them; each is a
+stated reading beside the 32-entry specification above, which stays the
+default):
+  * finer tables: the section on lookup-table granularity calls the 32-entry
+    table a trade-off between accuracy and memory and says very large
+    attention heads may need finer tables. lut_size N in {32, 64, 128}: bin
+    width delta = clip/(N-1), entries for slots 0..N-2 as for N = 32, the
+    last slot N-1 the sparse tail (entry 0), idx = min(N-1, (x*M + 2^23) >> 24)
+    with M from mu = alpha/delta; everything after the table is unchanged.
+  * grouped K/V heads: kv_heads K/V heads shared by the H query heads in
+    consecutive groups of G = H/kv_heads (query head h reads K/V head h//G);
+    kv_heads = H is ordinary multi-head attention, 1 is multi-query.
+
 Parity pins: see tests/test_oracle_*.py. Every function here is pinned by a
 property, closed form, brute-force twin or exact-rational bound; none is
 "parity unpinned".
@@ -45,6 +58,7 @@ import numpy as np
 # Fixed widths of the integer encoding.
 # ---------------------------------------------------------------------------
 LUT_SIZE = 32                 # the pages: a 32-entry exp table
+LUT_SIZES = (32, 64, 128)     # the finer-table variants
 LUT_ONE = 1 << 15             # Q15: table entry for a zero relative score
 IDX_SHIFT = 24                # fixed-point fraction bits of the bin multiplier
 P_ONE = 255                   # uint8 probabilities, target row sum 255
@@ -70,7 +84,7 @@ class OracleRangeError(ValueError):
 @dataclass(frozen=True)
 class Params:
     """Integers frozen on the host before any score is computed."""
-    lut: tuple            # 32 uint16 table entries, lut[31] == 0
+    lut: tuple            # lut_size uint16 table entries, the last one 0
     idx_mul: int          # M: bin multiplier, idx = (x*M + 2^23) >> 24
     idx_shift: int        # always IDX_SHIFT
     x_clip: int           # smallest relative score x that lands in slot 31
@@ -80,6 +94,7 @@ class Params:
     delta: float          # table bin width in logit units
     mu: float             # alpha / delta
     mu_o: float           # s_v / (255 * s_o)
+    lut_size: int = LUT_SIZE  # N: table entries (slots 0..N-1)
 
 
 def _f32(x) -> float:
@@ -87,45 +102,53 @@ def _f32(x) -> float:
     return float(np.float32(x))
 
 
-def build_lut(clip: float) -> tuple:
-    """The 32-entry exp table.
+def _check_lut_size(lut_size: int) -> int:
+    if lut_size not in LUT_SIZES:
+        raise OracleRangeError("lut_size must be 32, 64 or 128")
+    return int(lut_size)
 
-    Slot k approximates exp(-k * delta) with delta = clip / 31, stored as
-    round-half-even(2^15 * exp(-k*delta)) for k < 31. Slot 31 is the sparse
-    tail and holds 0: every key clipped there drops out of the sum.
+
+def build_lut(clip: float, lut_size: int = LUT_SIZE) -> tuple:
+    """The N-entry exp table (N = 32: the pages' table).
+
+    Slot k approximates exp(-k * delta) with delta = clip / (N-1), stored as
+    round-half-even(2^15 * exp(-k*delta)) for k < N-1. Slot N-1 is the
+    sparse tail and holds 0: every key clipped there drops out of the sum.
     """
+    n = _check_lut_size(lut_size)
     c = _f32(clip)
     if not (math.isfinite(c) and c > 0.0):
         raise OracleRangeError("clip must be finite and > 0")
-    delta = c / 31.0
-    lut = [int(round(LUT_ONE * math.exp(-(float(k) * delta)))) for k in range(LUT_SIZE - 1)]
+    delta = c / float(n - 1)
+    lut = [int(round(LUT_ONE * math.exp(-(float(k) * delta)))) for k in range(n - 1)]
     lut.append(0)
     return tuple(lut)
 
 
 def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
-                  clip: float) -> Params:
+                  clip: float, lut_size: int = LUT_SIZE) -> Params:
     """Host parameter derivation.
 
     alpha = s_q*s_k/sqrt(D) folds the 1/sqrt(d) attention scale into the
     index multiplier; mu = alpha/delta converts an integer score gap into
     table slots; M = round(mu * 2^24).
     """
+    n = _check_lut_size(lut_size)
     if D < 1:
         raise OracleRangeError("D must be >= 1")
     sq, sk, sv, so, c = (_f32(s) for s in (s_q, s_k, s_v, s_o, clip))
     for s in (sq, sk, sv, so):
         if not (math.isfinite(s) and s > 0.0):
             raise OracleRangeError("scales must be finite and > 0")
-    lut = build_lut(c)
+    lut = build_lut(c, n)
     alpha = (sq * sk) / math.sqrt(float(D))
-    delta = c / 31.0
+    delta = c / float(n - 1)
     mu = alpha / delta
     if not (MU_MIN <= mu < MU_MAX):
         raise OracleRangeError("index multiplier outside [2^-16, 2^-1)")
     idx_mul = int(round(math.ldexp(mu, IDX_SHIFT)))
-    # smallest x with (x*M + 2^23) >> 24 >= 31, i.e. x*M >= 61 * 2^23
-    num = 61 << (IDX_SHIFT - 1)
+    # smallest x with (x*M + 2^23) >> 24 >= N-1, i.e. x*M >= (2N-3) * 2^23
+    num = (2 * n - 3) << (IDX_SHIFT - 1)
     x_clip = -(-num // idx_mul)
     mu_o = sv / (255.0 * so)
     m_o, e_o = math.frexp(mu_o)
@@ -138,7 +161,7 @@ def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
         raise OracleRangeError("output multiplier outside the encodable range")
     return Params(lut=lut, idx_mul=idx_mul, idx_shift=IDX_SHIFT, x_clip=x_clip,
                   req_mul=req_mul, req_shift=req_shift, alpha=alpha, delta=delta,
-                  mu=mu, mu_o=mu_o)
+                  mu=mu, mu_o=mu_o, lut_size=n)
 
 
 # ---------------------------------------------------------------------------
@@ -148,12 +171,12 @@ def slot_index(x, prm: Params):
     """Table slot of a relative score x = m - s >= 0.
 
     Uniform bins of width delta, nearest bin: idx = (x*M + 2^23) >> 24,
-    clipped to the last slot (the sparsity-aware clip).
+    clipped to the last slot N-1 (the sparsity-aware clip).
     """
     x = np.asarray(x, dtype=np.int64)
     half = np.int64(1 << (prm.idx_shift - 1))
     idx = (x * np.int64(prm.idx_mul) + half) >> np.int64(prm.idx_shift)
-    return np.minimum(idx, LUT_SIZE - 1)
+    return np.minimum(idx, prm.lut_size - 1)
 
 
 def reciprocal(E):
@@ -218,7 +241,7 @@ def index_softmax(S, prm: Params, causal: bool):
     lo = np.iinfo(np.int64).min
     m = np.where(allow, S, lo).max(axis=1)
     x = m[:, None] - S
-    idx = np.where(allow, slot_index(np.where(allow, x, 0), prm), LUT_SIZE - 1)
+    idx = np.where(allow, slot_index(np.where(allow, x, 0), prm), prm.lut_size - 1)
     lut = np.asarray(prm.lut, dtype=np.int64)
     e = lut[idx]
     E = e.sum(axis=1)
@@ -243,11 +266,14 @@ def head_forward(qh, kh, vh, prm: Params, causal: bool):
     return out, m, E, P
 
 
-def check_args(q, k, v, causal):
+def check_args(q, k, v, causal, kv_heads=None):
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise OracleRangeError("tensors must be [B, H, S, D]")
     B, H, Sq, D = q.shape
-    if k.shape[:2] != (B, H) or v.shape != k.shape or k.shape[3] != D:
+    hkv = H if kv_heads is None else int(kv_heads)
+    if hkv < 1 or H % hkv != 0:
+        raise OracleRangeError("kv_heads must divide H")
+    if k.shape[:2] != (B, hkv) or v.shape != k.shape or k.shape[3] != D:
         raise OracleRangeError("shape mismatch")
     Skv = k.shape[2]
     if Skv < 1 or Skv > SKV_MAX:
@@ -262,15 +288,19 @@ def check_args(q, k, v, causal):
     return B, H, Sq, Skv, D
 
 
-def forward(q, k, v, scales, clip=DEFAULT_CLIP, causal=False, stats=False):
-    """Full forward over [B, H, S, D] int8 tensors.
+def forward(q, k, v, scales, clip=DEFAULT_CLIP, causal=False, stats=False,
+            lut_size=LUT_SIZE, kv_heads=None):
+    """Full forward over int8 tensors q [B, H, Sq, D], k and v [B, Hkv, Skv, D].
 
-    scales = (s_q, s_k, s_v, s_o). Returns out int8 [B, H, Sq, D]; with
-    stats=True also (m int64 [B,H,Sq], E int64 [B,H,Sq], P uint8 [B,H,Sq,Skv]).
+    scales = (s_q, s_k, s_v, s_o); lut_size: table entries (32 is the pages'
+    table); kv_heads = Hkv (None: H), query head h reading K/V head
+    h // (H // Hkv). Returns out int8 [B, H, Sq, D]; with stats=True also
+    (m int64 [B,H,Sq], E int64 [B,H,Sq], P uint8 [B,H,Sq,Skv]).
     """
     q, k, v = (np.ascontiguousarray(t) for t in (q, k, v))
-    B, H, Sq, Skv, D = check_args(q, k, v, causal)
-    prm = derive_params(D, *scales, clip)
+    B, H, Sq, Skv, D = check_args(q, k, v, causal, kv_heads)
+    group = H // k.shape[1]
+    prm = derive_params(D, *scales, clip, lut_size)
     out = np.zeros((B, H, Sq, D), dtype=np.int8)
     if stats:
         M = np.zeros((B, H, Sq), dtype=np.int64)
@@ -278,7 +308,7 @@ def forward(q, k, v, scales, clip=DEFAULT_CLIP, causal=False, stats=False):
         Ps = np.zeros((B, H, Sq, Skv), dtype=np.uint8)
     for b in range(B):
         for h in range(H):
-            o, m, E, P = head_forward(q[b, h], k[b, h], v[b, h], prm, causal)
+            o, m, E, P = head_forward(q[b, h], k[b, h // group], v[b, h // group], prm, causal)
             out[b, h] = o
             if stats:
                 M[b, h], Es[b, h], Ps[b, h] = m, E, P

@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY (same rules as intattn_oracle: only tests, the
 smoke check and the benchmark's CPU-baseline leg may import it).
 
 It restates each IndexSoftmax step of the IntAttention digest pages
-(section "Methodology", step 2: clip, 32-entry table lookup, int32 sum,
+(section "Methodology", step 2: clip, table lookup (32 entries, or a finer
+table of 64 or 128), int32 sum,
 reciprocal multiply + shift; step 3: integer Q.K^T and P.V) in a different
 form from the vectorised oracle, so that a slip in either (a transposed
 operand, a wrong axis, an off-by-one in a rounding) shows up as a mismatch:
@@ -60,7 +61,7 @@ def head_forward(q, k, v, prm, causal: bool):
             if not ok:
                 e.append(0)
             else:
-                e.append(prm.lut[nearest_slot(m - s, prm.idx_mul, prm.idx_shift)])
+                e.append(prm.lut[nearest_slot(m - s, prm.idx_mul, prm.idx_shift, len(prm.lut))])
         E = sum(e)
         R = round_half_up(Fraction(255 << 23, E))  # R = floor(255*2^23/E + 1/2)
         p = [round_half_up(Fraction(ej * R, 1 << 23)) for ej in e]
