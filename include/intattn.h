@@ -121,6 +121,57 @@ int intattn_forward_debug(const int8_t* q, const int8_t* k, const int8_t* v, int
                           float clip, int causal, void* stream,
                           int32_t* row_max, uint32_t* row_sum, uint8_t* probs);
 
+/* ---- Variants: finer exp tables and grouped K/V heads ----------------------
+ * Finer tables: the pages' "Limitations & Future Work" (lookup-table
+ * granularity) call the 32-entry table a trade-off between accuracy and
+ * memory and say very large attention heads may need finer tables. With
+ * lut_size N in {32, 64, 128} every step above is unchanged except
+ *   delta = clip/(N-1), lut[k] = rint(2^15 exp(-k delta)) for k < N-1,
+ *   lut[N-1] = 0, idx = min(N-1, ((m - s)*M + 2^23) >> 24),
+ * with mu = alpha/delta (still required in [2^-16, 2^-1), so a finer table
+ * admits proportionally smaller alpha). N = 32 is the specification above.
+ * Grouped K/V heads (decoder serving: grouped-query and multi-query
+ * attention; the pages do not describe this step): k and v hold kv_heads
+ * heads, [B, kv_heads, Skv, D], and query head h reads K/V head
+ * h / (H / kv_heads); kv_heads must divide H (kv_heads = H is ordinary
+ * multi-head attention). */
+typedef struct intattn_variant {
+    int32_t lut_size;   /* exp-table entries: 32, 64 or 128; 0 means 32      */
+    int32_t kv_heads;   /* K/V heads; 0 means H                              */
+} intattn_variant;
+
+typedef struct intattn_params_ex {
+    uint16_t lut[128];  /* entries 0..lut_size-1 (entry lut_size-1 is 0);
+                           the rest 0                                        */
+    int32_t  lut_size;
+    int32_t  idx_mul;   /* M                                                 */
+    int32_t  idx_shift; /* always 24                                         */
+    int32_t  x_clip;    /* smallest m - s that lands in slot lut_size-1      */
+    int32_t  req_shift; /* sh_o, 1 .. 63                                     */
+    int64_t  req_mul;   /* M_o                                               */
+} intattn_params_ex;
+
+/* The lut_size-entry exp table (lut_out holds lut_size entries). Host only,
+ * pure. Errors: E_NULL, E_CLIP, E_RANGE (lut_size not 32, 64 or 128). */
+int intattn_build_lut_ex(float clip, int32_t lut_size, uint16_t* lut_out);
+
+/* intattn_derive_params for a lut_size-entry table. Host only, pure.
+ * Errors: E_NULL, E_SHAPE, E_SCALE, E_CLIP, E_RANGE (also lut_size). */
+int intattn_derive_params_ex(const intattn_shape* shape, const intattn_scales* scales,
+                             float clip, int32_t lut_size, intattn_params_ex* out);
+
+/* intattn_forward with a variant (NULL: lut_size 32, kv_heads H). q and out
+ * are [B, H, Sq, D]; k and v are [B, kv_heads, Skv, D]. row_max / row_sum:
+ * optional device outputs [B, H, Sq] (both NULL or both set), as in
+ * intattn_forward_debug. Every tensor pointer 16-byte aligned; allocates no
+ * device memory. Errors: those of intattn_forward, E_NULL for one of
+ * row_max / row_sum without the other, E_SHAPE for kv_heads < 0 or not
+ * dividing H, E_RANGE for lut_size. */
+int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
+                       const intattn_shape* shape, const intattn_scales* scales, float clip,
+                       int causal, const intattn_variant* variant, void* stream,
+                       int32_t* row_max, uint32_t* row_sum);
+
 /* ---- The pipeline as separate stages (scores and P in device memory) ----
  * The pages' "Methodology" step 1 places the cost of an INT8 pipeline in the
  * floating-point softmax between the integer products; these entry points run

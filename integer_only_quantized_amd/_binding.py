@@ -46,6 +46,16 @@ class Params(ctypes.Structure):
                 ("req_shift", ctypes.c_int32), ("req_mul", ctypes.c_int64)]
 
 
+class ParamsEx(ctypes.Structure):
+    _fields_ = [("lut", ctypes.c_uint16 * 128), ("lut_size", ctypes.c_int32), ("idx_mul", ctypes.c_int32),
+                ("idx_shift", ctypes.c_int32), ("x_clip", ctypes.c_int32),
+                ("req_shift", ctypes.c_int32), ("req_mul", ctypes.c_int64)]
+
+
+class Variant(ctypes.Structure):
+    _fields_ = [("lut_size", ctypes.c_int32), ("kv_heads", ctypes.c_int32)]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -72,6 +82,14 @@ def _load():
     lib.intattn_forward_debug.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape),
                                           ctypes.POINTER(Scales), f32, i32, vp, vp, vp, vp]
     lib.intattn_forward_debug.restype = i32
+    lib.intattn_build_lut_ex.argtypes = [f32, i32, ctypes.POINTER(ctypes.c_uint16)]
+    lib.intattn_build_lut_ex.restype = i32
+    lib.intattn_derive_params_ex.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Scales), f32, i32,
+                                             ctypes.POINTER(ParamsEx)]
+    lib.intattn_derive_params_ex.restype = i32
+    lib.intattn_forward_ex.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), ctypes.POINTER(Scales), f32, i32,
+                                       ctypes.POINTER(Variant), vp, vp, vp]
+    lib.intattn_forward_ex.restype = i32
     lib.intattn_qk_scores.argtypes = [vp, vp, vp, ctypes.POINTER(Shape), vp]
     lib.intattn_qk_scores.restype = i32
     lib.intattn_index_softmax.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), ctypes.POINTER(Scales),
@@ -114,6 +132,22 @@ def derive_params(D: int, scales, clip: float = DEFAULT_CLIP) -> dict:
             "x_clip": p.x_clip, "req_shift": p.req_shift, "req_mul": p.req_mul}
 
 
+def build_lut_ex(clip: float = DEFAULT_CLIP, lut_size: int = 32) -> list:
+    buf = (ctypes.c_uint16 * 128)()
+    _check(_lib.intattn_build_lut_ex(float(clip), int(lut_size), buf), "intattn_build_lut_ex")
+    return list(buf)[: int(lut_size)]
+
+
+def derive_params_ex(D: int, scales, clip: float = DEFAULT_CLIP, lut_size: int = 32) -> dict:
+    shape = Shape(1, 1, 1, 1, int(D))
+    sc = Scales(*[float(s) for s in scales])
+    p = ParamsEx()
+    _check(_lib.intattn_derive_params_ex(ctypes.byref(shape), ctypes.byref(sc), float(clip), int(lut_size),
+                                         ctypes.byref(p)), "intattn_derive_params_ex")
+    return {"lut": list(p.lut)[: p.lut_size], "lut_size": p.lut_size, "idx_mul": p.idx_mul,
+            "idx_shift": p.idx_shift, "x_clip": p.x_clip, "req_shift": p.req_shift, "req_mul": p.req_mul}
+
+
 _STRUCTS = {}
 
 
@@ -143,7 +177,7 @@ def forward_raw(q_ptr, k_ptr, v_ptr, out_ptr, shape, scales, clip, causal, strea
                                       rm, rs, pr)
 
 
-def _check_tensors(q, k, v):
+def _check_tensors(q, k, v, grouped: bool = False):
     import torch
     i8 = torch.int8
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -151,7 +185,7 @@ def _check_tensors(q, k, v):
             raise ValueError(f"{name} must be a contiguous 4-D int8 CUDA tensor [B, H, S, D]")
     B, H, Sq, D = q.shape
     ks = k.shape
-    if ks[0] != B or ks[1] != H or ks[3] != D or v.shape != ks:
+    if ks[0] != B or (ks[1] != H and not grouped) or ks[3] != D or v.shape != ks:
         raise ValueError("shape mismatch between q, k and v")
     if k.device != q.device or v.device != q.device:
         raise ValueError("q, k and v must be on the same device")
@@ -297,3 +331,27 @@ def pv(probs, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False, out=N
                            float(clip), int(bool(causal)), _stream(probs)), "intattn_pv")
     return out
 
+
+def forward_ex(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False, lut_size: int = 32,
+               stats: bool = False, out=None):
+    """intattn_forward_ex: q [B,H,Sq,D], k and v [B,Hkv,Skv,D] int8 CUDA tensors
+    (Hkv divides H; query head h reads K/V head h // (H // Hkv)), a table of
+    lut_size entries. Returns out, or (out, row_max, row_sum) with stats."""
+    import torch
+    B, H, Sq, Skv, D = _check_tensors(q, k, v, grouped=True)
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype is not torch.int8 or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError("out must be a contiguous int8 tensor shaped like q, on q's device")
+    var = Variant(int(lut_size), int(k.shape[1]))
+    sh, sc = _structs((B, H, Sq, Skv, D), scales)
+    rm = rs = None
+    if stats:
+        rm = torch.empty((B, H, Sq), dtype=torch.int32, device=q.device)
+        rs = torch.empty((B, H, Sq), dtype=torch.int32, device=q.device)
+    code = _lib.intattn_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ctypes.byref(sh),
+                                   ctypes.byref(sc), float(clip), int(bool(causal)), ctypes.byref(var), _stream(q),
+                                   rm.data_ptr() if stats else None, rs.data_ptr() if stats else None)
+    _check(code, "intattn_forward_ex")
+    return (out, rm, rs) if stats else out

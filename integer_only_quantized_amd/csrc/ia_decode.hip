@@ -18,7 +18,7 @@ constexpr int kDecodeMaxKeys = 16384;
 //      the D/16 lanes of a row (DPP), scores kept in LDS (int32 per key);
 //   B: row max (wave reduction + LDS);
 //   C: slots, table lookups and row sum; the scores' LDS words are reused
-//      for the slots; then p_j for every key (one 32-entry table per row);
+//      for the slots; then p_j for every key (one table per row, N <= 128);
 //   D: P.V: each lane transposes its 4 keys x 16 value columns (v_perm) and
 //      accumulates udot4(p, v + 128) (adding 128 to a signed byte = XOR 0x80),
 //      so a_d = sum_j p_j v_jd = acc_d - 128 * sum_j p_j; lanes and waves are
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
     extern __shared__ __attribute__((aligned(16))) int32_t dsm[];
     int32_t* s_score = dsm;                                     // skv_pad ints (scores, then slots)
     uint8_t* s_p = reinterpret_cast<uint8_t*>(dsm + skv_pad);   // skv_pad bytes
-    __shared__ uint32_t s_lut[32];
+    __shared__ uint16_t s_lut[kIaMaxLut];     // exp table (N <= 128 entries, rest 0)
     __shared__ int32_t s_red[4][D];
     __shared__ int32_t s_scal[8];
 
@@ -47,11 +47,15 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
     const int wave = tid >> 6;
     const int c = lane % CPR;                   // 16-byte column chunk
     const int g = lane / CPR;                   // key group within the wave
-    const size_t head = blockIdx.x;
-    const int8_t* kh = k + head * P.Skv * D;
-    const int8_t* vh = v + head * P.Skv * D;
+    // grouped K/V heads: the query heads of one K/V head run on the same XCD
+    // (consecutive logical blocks), so its K and V stream once into that L2
+    const int bid = P.kv_group > 1 ? xcd_local_block(blockIdx.x, gridDim.x) : static_cast<int>(blockIdx.x);
+    const size_t head = static_cast<size_t>(bid);
+    const size_t kvhead = static_cast<size_t>(bid / P.kv_group);
+    const int8_t* kh = k + kvhead * P.Skv * D;
+    const int8_t* vh = v + kvhead * P.Skv * D;
     const v4i qv = *reinterpret_cast<const v4i*>(q + head * D + 16 * c);
-    if (tid < 32) s_lut[tid] = lut_entry(P, tid);
+    if (wave == 0) fill_lut_u16(P, s_lut, lane);
 
     // ---- A: scores ---------------------------------------------------------
     int32_t tmax = INT_MIN;

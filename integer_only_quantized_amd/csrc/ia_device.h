@@ -65,32 +65,65 @@ __device__ __forceinline__ uint32_t slot_of(int32_t s, int32_t lo, uint32_t C, i
     return (C + static_cast<uint32_t>(__mul24(sp, negM))) >> 24;
 }
 
-// Saturating slot word: with y = s - m <= 0 and negM4 = -4M (|4M| < 2^23),
-// t = sat_int32(y * negM4 + 2^25) has the slot min(31, (x*M + 2^23) >> 24)
-// in bits 26..30 (byte 3 = 4 * slot + two fraction bits): scaling numerator
-// and shift by 4 keeps the quotient, the value is below 2^31 whenever the
-// slot is below 31, and saturation to 2^31 - 1 lands exactly in slot 31.
-__device__ __forceinline__ uint32_t slot_word_sat(int32_t y, int32_t negM4, int32_t half4) {
+// Saturating slot word for a table of N entries: with y = s - m <= 0, a
+// scale k (4, 2 or 1, with k <= 128/N and kM < 2^23; the layouts below) and
+// negMk = -kM, halfk = k * 2^23, t = sat_int32(y * negMk + halfk) =
+// sat(k (x M + 2^23)) has top byte floor(k (x M + 2^23) / 2^24), whose
+// quotient by k is the raw slot (x*M + 2^23) >> 24: scaling numerator and
+// shift by k keeps the quotient. The value is below 2^31 whenever the raw
+// slot is below 128/k, and saturation to 2^31 - 1 gives byte 127, i.e. slot
+// 127/k >= N - 1.
+__device__ __forceinline__ uint32_t slot_word_sat(int32_t y, int32_t negMk, int32_t halfk) {
     int32_t t;
-    asm("v_mad_i32_i24 %0, %1, %2, %3 clamp" : "=v"(t) : "v"(y), "s"(negM4), "v"(half4));
+    asm("v_mad_i32_i24 %0, %1, %2, %3 clamp" : "=v"(t) : "v"(y), "s"(negMk), "v"(halfk));
     return static_cast<uint32_t>(t);
 }
 
-// Byte address of a slot word's exp-table entry (table of u32 at LDS 0), one
-// SDWA op: FAST words (4M < 2^23) have 4 * slot + fraction in the top byte,
-// so the address is that byte & 0x7c; otherwise the top byte is
-// min(127, slot) (the word is at most 2^31 - 1) and the address is 4 * byte
-// into a 128-entry table whose entries 31..127 are zero.
-template <bool FAST>
+// Exp-table layouts in LDS (at byte address 0), chosen by the slot scale
+// KM = k, each bank-conflict free on the 64-bank LDS (lanes that read
+// different slots never meet in one bank) and addressed from a top byte in
+// one SDWA op:
+//   KM = 4 (N = 32, 4M < 2^23): u32[32], byte = 4 slot + fraction, address
+//          byte & 0x7c;
+//   KM = 2 (N <= 64, 2M < 2^23): u16[128], byte = 2 slot + fraction,
+//          address byte & 0x7e;
+//   KM = 1: u16[128], byte = slot, address 2 * byte.
+// u16 entries past slot N - 1 are 0 (the clipped tail); a saturated byte
+// (127) always lands on such an entry or on slot N - 1.
+template <int KM>
 __device__ __forceinline__ uint32_t lut_byte_addr(uint32_t t) {
     uint32_t a;
-    if constexpr (FAST) {
-        const uint32_t m = 0x7cu;
+    if constexpr (KM == 1) {
+        asm("v_lshlrev_b32_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+            : "=v"(a) : "v"(t));
+    } else {
+        const uint32_t m = KM == 4 ? 0x7cu : 0x7eu;
         asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD"
             : "=v"(a) : "v"(t), "s"(m));
+    }
+    return a;
+}
+
+// Byte address of the table entry for byte i of a packed word of top bytes
+// (the same mapping as lut_byte_addr), one SDWA op.
+template <int KM>
+__device__ __forceinline__ uint32_t lut_byte_addr_of(uint32_t w, int i) {
+    uint32_t a;
+    if constexpr (KM == 1) {
+        switch (i) {
+            case 0: asm("v_lshlrev_b32_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(a) : "v"(w)); break;
+            case 1: asm("v_lshlrev_b32_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(a) : "v"(w)); break;
+            case 2: asm("v_lshlrev_b32_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(a) : "v"(w)); break;
+            default: asm("v_lshlrev_b32_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(a) : "v"(w)); break;
+        }
     } else {
-        asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
-            : "=v"(a) : "v"(t));
+        const uint32_t m = KM == 4 ? 0x7cu : 0x7eu;
+        switch (i) {
+            case 0: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
+            case 1: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
+            case 2: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
+            default: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
+        }
     }
     return a;
 }
@@ -119,22 +152,6 @@ __device__ __forceinline__ int32_t requantise_hi(int32_t a, uint32_t mul, uint32
     return min(max(r, -127), 127);
 }
 
-// Entry k of the exp table from the packed kernel argument. The argument
-// words are wave-uniform (scalar registers); selecting among them keeps a
-// per-lane k from turning into a vector load of the argument segment (whose
-// wait would also cover any loads issued before it).
-__device__ __forceinline__ uint32_t lut_entry(const IaKernelParams& P, int k) {
-    const int w = k >> 1;
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        uint32_t wi = P.lut2[i];
-        asm("" : "+s"(wi));             // a register value, not an argument-segment address
-        word = (w == i) ? wi : word;
-    }
-    return (word >> (16 * (k & 1))) & 0xffffu;
-}
-
 __device__ __forceinline__ int32_t dpp_xor1(int32_t x) { return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true); }
 __device__ __forceinline__ int32_t dpp_xor2(int32_t x) { return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true); }
 __device__ __forceinline__ int32_t dpp_half_mirror(int32_t x) { return __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true); }
@@ -149,6 +166,61 @@ template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
+
+// The packed exp table as one register of the wave: lane i holds argument
+// word i (entries 2i and 2i+1). The argument words are wave-uniform (scalar
+// registers); writing them lane by lane keeps a per-lane index from turning
+// into a vector load of the argument segment (whose wait would also cover any
+// loads issued before it).
+template <int NW = kIaMaxLut / 2>
+__device__ __forceinline__ uint32_t lut_words(const IaKernelParams& P) {
+    static_assert(NW % 16 == 0 && NW <= kIaMaxLut / 2, "words come in groups of 16");
+    uint32_t all = 0;
+    // the lane number must be an inline constant (one scalar operand per VOP3)
+#define IA_WL(i) asm volatile("v_writelane_b32 %0, %1, " #i : "+v"(all) : "s"(P.lut2[i]));
+    IA_WL(0) IA_WL(1) IA_WL(2) IA_WL(3) IA_WL(4) IA_WL(5) IA_WL(6) IA_WL(7)
+    IA_WL(8) IA_WL(9) IA_WL(10) IA_WL(11) IA_WL(12) IA_WL(13) IA_WL(14) IA_WL(15)
+    if constexpr (NW > 16) {
+        IA_WL(16) IA_WL(17) IA_WL(18) IA_WL(19) IA_WL(20) IA_WL(21) IA_WL(22) IA_WL(23)
+        IA_WL(24) IA_WL(25) IA_WL(26) IA_WL(27) IA_WL(28) IA_WL(29) IA_WL(30) IA_WL(31)
+    }
+    if constexpr (NW > 32) {
+        IA_WL(32) IA_WL(33) IA_WL(34) IA_WL(35) IA_WL(36) IA_WL(37) IA_WL(38) IA_WL(39)
+        IA_WL(40) IA_WL(41) IA_WL(42) IA_WL(43) IA_WL(44) IA_WL(45) IA_WL(46) IA_WL(47)
+        IA_WL(48) IA_WL(49) IA_WL(50) IA_WL(51) IA_WL(52) IA_WL(53) IA_WL(54) IA_WL(55)
+        IA_WL(56) IA_WL(57) IA_WL(58) IA_WL(59) IA_WL(60) IA_WL(61) IA_WL(62) IA_WL(63)
+    }
+#undef IA_WL
+    return all;
+}
+
+// Exp-table entry idx (0..127) from lut_words: lut[idx] for idx < N, else 0.
+// A cross-lane read: every lane of the wave must be active.
+__device__ __forceinline__ uint32_t lut_value(const IaKernelParams& P, uint32_t words, int idx) {
+    const uint32_t w = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute((idx >> 1) << 2, static_cast<int>(words)));
+    const uint32_t e = (w >> (16 * (idx & 1))) & 0xffffu;
+    return idx < P.lut_size ? e : 0u;
+}
+
+// Fills the u16[128] exp table at t (LDS) from one whole wave.
+__device__ __forceinline__ void fill_lut_u16(const IaKernelParams& P, uint16_t* t, int lane) {
+    const uint32_t words = lut_words(P);
+    t[lane] = static_cast<uint16_t>(lut_value(P, words, lane));
+    t[64 + lane] = static_cast<uint16_t>(lut_value(P, words, 64 + lane));
+}
+
+// Fills the exp table of layout KM (see lut_byte_addr) at LDS t (256 bytes)
+// from one whole wave.
+template <int KM>
+__device__ __forceinline__ void fill_lut_table(const IaKernelParams& P, void* t, int lane) {
+    if constexpr (KM == 4) {
+        const uint32_t v = lut_value(P, lut_words<16>(P), lane & 31);   // N = 32: words 0..15
+        if (lane < 32) static_cast<uint32_t*>(t)[lane] = v;
+    } else {
+        fill_lut_u16(P, static_cast<uint16_t*>(t), lane);
+    }
+}
+
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -211,6 +283,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 32-bit LDS load from a byte address (the kernel's LDS block starts at 0).
 __device__ __forceinline__ uint32_t lds_u32(uint32_t addr) {
     return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(static_cast<uintptr_t>(addr));
+}
+
+// 16-bit LDS load (zero-extended) from a byte address.
+__device__ __forceinline__ uint32_t lds_u16(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(static_cast<uintptr_t>(addr));
+}
+
+// Table entry at a byte address produced by lut_byte_addr<KM>.
+template <int KM>
+__device__ __forceinline__ uint32_t lut_load(uint32_t addr) {
+    if constexpr (KM == 4) return lds_u32(addr);
+    else return lds_u16(addr);
 }
 
 // Scheduling fence over 16 values: every load feeding them completes here,

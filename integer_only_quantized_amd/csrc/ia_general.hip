@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void ia_general_kernel(
 
     __shared__ __attribute__((aligned(16))) int8_t sk[kKeyTile * KStride];
     __shared__ __attribute__((aligned(16))) int8_t svt[D * kVtStride];
-    __shared__ uint16_t slut[32];
+    __shared__ uint16_t slut[kIaMaxLut];      // exp table (N <= 128 entries, rest 0)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -62,10 +62,11 @@ __global__ __launch_bounds__(256) void ia_general_kernel(
     const int b = bid / P.H;
     const size_t head = static_cast<size_t>(b) * P.H + h;
     const int8_t* qh = q + head * P.Sq * D;
-    const int8_t* kh = k + head * P.Skv * D;
-    const int8_t* vh = v + head * P.Skv * D;
+    const size_t kvhead = static_cast<size_t>(b) * (P.H / P.kv_group) + h / P.kv_group;   // grouped K/V heads
+    const int8_t* kh = k + kvhead * P.Skv * D;
+    const int8_t* vh = v + kvhead * P.Skv * D;
 
-    if (tid < 32) slut[tid] = static_cast<uint16_t>(P.lut2[tid >> 1] >> (16 * (tid & 1)));
+    if (wave == 0) fill_lut_u16(P, slut, lane);
 
     const int shift = P.Skv - P.Sq;                  // bottom-right causal alignment
     const int q0 = qb * kQBlock;

@@ -34,11 +34,12 @@
 //     their values cancel: sum (p - 128) v + 128 sum v = sum p v;
 //   * causal workgroups are dispatched heaviest first, and when the head
 //     count allows, every XCD owns a fixed subset of heads (L2 locality).
-// Slot word, y = s - m in [-2^23, 0]:
-//   4M < 2^23: t = sat(y * -4M + 2^25); byte 3 = 4 * slot + fraction, and
-//              saturation lands in slot 31 (table address: byte 3 & 0x7c);
-//   otherwise: t = sat(y * -M + 2^23); byte 3 = min(127, raw slot), and the
-//              table has 128 entries with entries 31..127 equal to zero.
+// Slot word, y = s - m in [-2^23, 0], for a table of N entries (32, or a
+// finer 64 or 128): t = sat(y * -kM + k * 2^23) with k = 4 (N = 32,
+// 4M < 2^23), 2 (N <= 64, 2M < 2^23) or 1; byte 3 is k * slot + fraction
+// bits (127 when saturated), and the table layout KM = k in LDS is
+// addressed from it in one SDWA op (u32[32]: byte & 0x7c; u16[128]:
+// byte & 0x7e or 2 * byte).
 #include <type_traits>
 
 #include "ia_device.h"
@@ -55,13 +56,13 @@ constexpr int kLutEntries = 128;
 template <int D>
 struct LongLds {
     static constexpr int TB = kLongTile * D;        // bytes per K or V tile
-    uint32_t lut[kLutEntries];                      // first member: LDS byte address 0
+    uint32_t lut[kLutEntries / 2];                  // exp table (layout KM); first member: LDS address 0
     int32_t colsum[kLongWaves][D];
     int8_t k[kStages][TB];
     int8_t v[kStages][TB];
 };
 
-template <int D, bool FAST>
+template <int D, int KM>
 __global__ __launch_bounds__(256) void ia_long_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, const int8_t* __restrict__ v,
     int8_t* __restrict__ out, const IaKernelParams P, int nqb, int32_t* __restrict__ row_max,
@@ -98,8 +99,9 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     }
     const size_t head = static_cast<size_t>(head_i);
     const int8_t* qh = q + head * P.Sq * D;
-    const int8_t* kh = k + head * P.Skv * D;
-    const int8_t* vh = v + head * P.Skv * D;
+    const size_t kvhead = static_cast<size_t>(head_i / P.kv_group);   // grouped K/V heads
+    const int8_t* kh = k + kvhead * P.Skv * D;
+    const int8_t* vh = v + kvhead * P.Skv * D;
 
     const int shift = P.Skv - P.Sq;
     const int q0 = qb * kLongRows;
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     const int kend_wg = P.causal ? min(P.Skv, qlast + shift + 1) : P.Skv;
     const int ntiles = (kend_wg + kLongTile - 1) / kLongTile;
 
-    if (tid < kLutEntries) lds.lut[tid] = tid < 32 ? lut_entry(P, tid) : 0u;
+    if (wave == 0) fill_lut_table<KM>(P, lds.lut, lane);
 
     v4i qf[KS];
 #pragma unroll
@@ -225,10 +227,10 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     v16i cinit;
 #pragma unroll
     for (int r = 0; r < 16; ++r) cinit[r] = -mrow;
-    const int32_t negMs = FAST ? -4 * P.idx_mul : -P.idx_mul;
-    const int32_t halfs = FAST ? (1 << 25) : (1 << 23);
+    const int32_t negMs = -P.slot_k * P.idx_mul;
+    const int32_t halfs = P.slot_k << 23;
     auto table_entry = [&](int32_t y) -> uint32_t {
-        return lds_u32(lut_byte_addr<FAST>(slot_word_sat(y, negMs, halfs)));
+        return lut_load<KM>(lut_byte_addr<KM>(slot_word_sat(y, negMs, halfs)));
     };
     constexpr int32_t kMasked = -(1 << 23);   // y of a masked key: saturates to the last slot
 
@@ -337,18 +339,18 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     }
 }
 
-template <int D, bool FAST>
+template <int D, int KM>
 int launch_long_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, const IaKernelParams& kp,
                   hipStream_t s, int nqb, unsigned blocks, int32_t* row_max, uint32_t* row_sum) {
     static bool attr_set = false;
     const size_t shm = sizeof(LongLds<D>);
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_long_kernel<D, FAST>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_long_kernel<D, KM>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)) != hipSuccess)
             return INTATTN_E_HIP;
         attr_set = true;
     }
-    hipLaunchKernelGGL((ia_long_kernel<D, FAST>), dim3(blocks), dim3(256), shm, s, q, k, v, out, kp, nqb,
+    hipLaunchKernelGGL((ia_long_kernel<D, KM>), dim3(blocks), dim3(256), shm, s, q, k, v, out, kp, nqb,
                        row_max, row_sum);
     return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
 }
@@ -362,12 +364,14 @@ int launch_long(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, 
     if (blocks > INT_MAX) return INTATTN_E_SHAPE;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const unsigned nb = static_cast<unsigned>(blocks);
-    const bool fast = kp.idx_mul < (1 << 21);
-    if (D == 64)
-        return fast ? launch_long_t<64, true>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum)
-                    : launch_long_t<64, false>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
-    return fast ? launch_long_t<128, true>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum)
-                : launch_long_t<128, false>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
+    if (D == 64) {
+        if (kp.slot_k == 4) return launch_long_t<64, 4>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
+        if (kp.slot_k == 2) return launch_long_t<64, 2>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
+        return launch_long_t<64, 1>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
+    }
+    if (kp.slot_k == 4) return launch_long_t<128, 4>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
+    if (kp.slot_k == 2) return launch_long_t<128, 2>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
+    return launch_long_t<128, 1>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
 }
 
 }  // namespace ia

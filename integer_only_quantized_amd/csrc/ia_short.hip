@@ -29,12 +29,14 @@
 //   combine: each wave sends the output columns the other half's wave
 //            finishes through LDS, adds the partials it receives,
 //            requantises and stores its own columns.
-// Slot word, y = s - m in [-2^23, 0]:
-//   4M < 2^23: t = sat(y * -4M + 2^25); top byte = 4 * slot + fraction, and
-//              saturation lands in slot 31 (table address: byte & 0x7c);
-//   otherwise: t = sat(y * -M + 2^23); top byte = min(127, raw slot), and the
-//              table has 128 entries with entries 31..127 equal to zero
-//              (table address: 4 * byte).
+// Slot word, y = s - m in [-2^23, 0], for a table of N entries (32, or a
+// finer 64 or 128): t = sat(y * -kM + k * 2^23) with k = 4 (N = 32,
+// 4M < 2^23), 2 (N <= 64, 2M < 2^23) or 1; its top byte is k * slot +
+// fraction bits (127 when saturated), and the table layout KM = k in LDS is
+// addressed from that byte in one SDWA op (u32[32]: byte & 0x7c; u16[128]:
+// byte & 0x7e or 2 * byte).
+#include <type_traits>
+
 #include "ia_device.h"
 
 namespace ia {
@@ -56,7 +58,7 @@ struct ShortLds {
     static constexpr int KVBytes = 2 * NBH * 32 * D;                 // K (later V) of both halves
     static constexpr int XOBytes = 4 * (DB / 2) * 16 * 64 * 4;       // output partials, 4 waves
     static constexpr int Region = KVBytes > XOBytes ? KVBytes : XOBytes;
-    uint32_t lut[kShortLut];                 // first member: LDS byte address 0
+    uint32_t lut[kIaMaxLut / 2];             // exp table (layout KM); first member: LDS address 0
     int32_t xm[2][2][32];                    // row max exchange [query group][half][row]
     uint32_t xe[2][2][32];                   // row sum exchange
     int32_t xcs[4][D];                       // column-sum partials, one per wave
@@ -64,7 +66,7 @@ struct ShortLds {
     int8_t kv[Region];                       // K, then V, then the output partials
 };
 
-template <int D, int NBH, bool FAST, bool SKIP>
+template <int D, int NBH, bool SKIP, int KM>
 __global__ __launch_bounds__(256) void ia_short_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, const int8_t* __restrict__ v,
     int8_t* __restrict__ out, const IaKernelParams P, int nqb, int32_t* __restrict__ row_max,
@@ -88,8 +90,9 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     const int qb = bid % nqb;
     const size_t head = static_cast<size_t>(bid / nqb);
     const int8_t* qh = q + head * P.Sq * D;
-    const int8_t* kh = k + head * P.Skv * D;
-    const int8_t* vh = v + head * P.Skv * D;
+    const size_t kvhead = static_cast<size_t>(static_cast<int>(head) / P.kv_group);   // grouped K/V heads
+    const int8_t* kh = k + kvhead * P.Skv * D;
+    const int8_t* vh = v + kvhead * P.Skv * D;
 
     // ---- staging ---------------------------------------------------------------
     // Each wave stages the key blocks of its own half that it reads (the two
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     v4i qf[KS];                          // Q^T fragments, read from LDS in pass 1
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = v4i{0, 0, 0, 0};
-    if (tid < kShortLut) lds.lut[tid] = tid < 32 ? lut_entry(P, tid) : 0u;
+    if (wave == 0) fill_lut_table<KM>(P, lds.lut, lane);
     // block j of this wave's half is in LDS: loads complete in issue order;
     // whole-block staging issued nvalid blocks of LPB loads, split staging
     // nvp blocks of LPB/2 loads, and then every wave meets at a barrier
@@ -279,8 +282,8 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     mrow = max(mrow, lds.xm[qg][half ^ 1][l32]);
 
     // ---- pass 2: slots, table entries, row sum; slot bytes kept ------------
-    const int32_t negMs = FAST ? -4 * P.idx_mul : -P.idx_mul;
-    const int32_t halfs = FAST ? (1 << 25) : (1 << 23);
+    const int32_t negMs = -P.slot_k * P.idx_mul;
+    const int32_t halfs = P.slot_k << 23;
     constexpr int32_t kMasked = -(1 << 23);   // y of a masked key: saturates to the last slot
     uint32_t idxw[NBH][4];
     uint32_t E = 0;
@@ -308,9 +311,9 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     t[c] = slot_word_sat(cur[4 * w4 + c], negMs, halfs);
-                    e[4 * w4 + c] = lds_u32(lut_byte_addr<FAST>(t[c]));
+                    e[4 * w4 + c] = lut_load<KM>(lut_byte_addr<KM>(t[c]));
                 }
-                // top bytes: FAST 4 * slot + fraction; otherwise min(127, slot)
+                // top bytes: k * slot + fraction bits (127 when saturated)
                 idxw[j][w4] = pack_top_bytes(t[0], t[1], t[2], t[3]);
                 // keep the packed word (not the four values it came from) live
                 asm volatile("" : "+v"(idxw[j][w4]));
@@ -346,33 +349,11 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     }
 
     // ---- pass 3: P from the slot bytes, P.V on the MFMA -------------------
-    // table address of byte i of a kept slot word: FAST: byte & 0x7c;
-    // otherwise 4 * byte (bytes are at most 127); one SDWA op either way
-    auto byte_addr = [&](uint32_t w, int i) -> uint32_t {
-        uint32_t a;
-        if constexpr (FAST) {
-            const uint32_t m = 0x7cu;
-            switch (i) {
-                case 0: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
-                case 1: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
-                case 2: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
-                default: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
-            }
-        } else {
-            switch (i) {
-                case 0: asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(a) : "v"(w)); break;
-                case 1: asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(a) : "v"(w)); break;
-                case 2: asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(a) : "v"(w)); break;
-                default: asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(a) : "v"(w)); break;
-            }
-        }
-        return a;
-    };
     auto plookup = [&](int j, uint32_t (&pl)[16]) {
 #pragma unroll
         for (int w4 = 0; w4 < 4; ++w4)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pl[4 * w4 + i] = lds_u32(byte_addr(idxw[j][w4], i));
+            for (int i = 0; i < 4; ++i) pl[4 * w4 + i] = lut_load<KM>(lut_byte_addr_of<KM>(idxw[j][w4], i));
     };
     auto ppack = [&](const uint32_t (&pl)[16]) {
         v4i pa;
@@ -502,8 +483,6 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
 template <int D, int NBH>
 int launch_short_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
                    const IaKernelParams& kp, hipStream_t stream, int32_t* row_max, uint32_t* row_sum) {
-    // the saturating slot form needs 4*M to fit the 24-bit multiplier operand
-    const bool fast = kp.idx_mul < (1 << 21);
     const int nqb = (kp.Sq + 63) / 64;
     const long long blocks = static_cast<long long>(kp.B) * kp.H * nqb;
     if (blocks > INT_MAX) return INTATTN_E_SHAPE;
@@ -513,18 +492,18 @@ int launch_short_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* ou
     const int tail_rows = kp.Sq % 64;
     const bool skip = kp.causal || (tail_rows != 0 && tail_rows <= 32) || kp.Skv <= 64 * NBH - 32;
     const dim3 grid(static_cast<unsigned>(blocks));
-    if (fast && skip)
-        hipLaunchKernelGGL((ia_short_kernel<D, NBH, true, true>), grid, dim3(256), 0, stream, q, k, v, out, kp,
-                           nqb, row_max, row_sum);
-    else if (fast)
-        hipLaunchKernelGGL((ia_short_kernel<D, NBH, true, false>), grid, dim3(256), 0, stream, q, k, v, out, kp,
-                           nqb, row_max, row_sum);
-    else if (skip)
-        hipLaunchKernelGGL((ia_short_kernel<D, NBH, false, true>), grid, dim3(256), 0, stream, q, k, v, out, kp,
-                           nqb, row_max, row_sum);
-    else
-        hipLaunchKernelGGL((ia_short_kernel<D, NBH, false, false>), grid, dim3(256), 0, stream, q, k, v, out, kp,
-                           nqb, row_max, row_sum);
+    auto go = [&](auto skip_c, auto km_c) {
+        hipLaunchKernelGGL((ia_short_kernel<D, NBH, decltype(skip_c)::value, decltype(km_c)::value>), grid,
+                           dim3(256), 0, stream, q, k, v, out, kp, nqb, row_max, row_sum);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    using K4 = std::integral_constant<int, 4>;
+    using K2 = std::integral_constant<int, 2>;
+    using K1 = std::integral_constant<int, 1>;
+    if (kp.slot_k == 4) skip ? go(T{}, K4{}) : go(F{}, K4{});
+    else if (kp.slot_k == 2) skip ? go(T{}, K2{}) : go(F{}, K2{});
+    else skip ? go(T{}, K1{}) : go(F{}, K1{});
     return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
 }
 

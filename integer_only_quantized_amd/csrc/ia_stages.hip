@@ -103,15 +103,15 @@ __device__ __forceinline__ float wave_sumf(float x) {
 // allowed key below -x_clip reaches in the last slot anyway), table entries,
 // row sum E, R = floor((255*2^23 + floor(E/2)) / E), p = top byte of
 // e*2R + 2^23. Scores must satisfy |s| < 2^30 (true for Q.K^T of int8).
-template <int NCH, bool FAST>
+template <int NCH, int KM>
 __global__ __launch_bounds__(256) void ia_index_softmax_kernel(const int32_t* __restrict__ scores,
                                                                uint8_t* __restrict__ probs,
                                                                int32_t* __restrict__ row_max,
                                                                uint32_t* __restrict__ row_sum,
                                                                const IaKernelParams P, long long rows) {
-    __shared__ uint32_t lut[128];
+    __shared__ uint32_t lut[kIaMaxLut / 2];    // exp table, layout KM
     const int tid = threadIdx.x;
-    if (tid < 128) lut[tid] = tid < 32 ? lut_entry(P, tid) : 0u;
+    if (tid < 64) fill_lut_table<KM>(P, lut, tid);   // wave 0, whole
     __syncthreads();
     const int lane = tid & 63;
     const long long row = static_cast<long long>(blockIdx.x) * 4 + (tid >> 6);
@@ -133,15 +133,15 @@ __global__ __launch_bounds__(256) void ia_index_softmax_kernel(const int32_t* __
         if (64 * c + lane < kend) m = max(m, s[c]);
     m = wave_max(m);
 
-    const int32_t negMs = FAST ? -4 * P.idx_mul : -P.idx_mul;
-    const int32_t halfs = FAST ? (1 << 25) : (1 << 23);
+    const int32_t negMs = -P.slot_k * P.idx_mul;
+    const int32_t halfs = P.slot_k << 23;
     uint32_t e[NCH];
     uint32_t E = 0;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int32_t y = 64 * c + lane < kend ? max(s[c] - m, -(1 << 23)) : -(1 << 23);
         const uint32_t t = slot_word_sat(y, negMs, halfs);
-        e[c] = lds_u32(lds_addr(lut) + lut_byte_addr<FAST>(t));
+        e[c] = lut_load<KM>(lds_addr(lut) + lut_byte_addr<KM>(t));
         E += e[c];
     }
     E = wave_sum(E);
@@ -359,11 +359,14 @@ int launch_isoftmax_n(int nch, const int32_t* scores, uint8_t* probs, int32_t* r
     } else {
         if (nch != NCH)
             return launch_isoftmax_n<NCH * 2>(nch, scores, probs, row_max, row_sum, kp, s, rows, blocks);
-        if (kp.idx_mul < (1 << 21))
-            hipLaunchKernelGGL((ia_index_softmax_kernel<NCH, true>), dim3(blocks), dim3(256), 0, s, scores, probs,
+        if (kp.slot_k == 4)
+            hipLaunchKernelGGL((ia_index_softmax_kernel<NCH, 4>), dim3(blocks), dim3(256), 0, s, scores, probs,
+                               row_max, row_sum, kp, rows);
+        else if (kp.slot_k == 2)
+            hipLaunchKernelGGL((ia_index_softmax_kernel<NCH, 2>), dim3(blocks), dim3(256), 0, s, scores, probs,
                                row_max, row_sum, kp, rows);
         else
-            hipLaunchKernelGGL((ia_index_softmax_kernel<NCH, false>), dim3(blocks), dim3(256), 0, s, scores, probs,
+            hipLaunchKernelGGL((ia_index_softmax_kernel<NCH, 1>), dim3(blocks), dim3(256), 0, s, scores, probs,
                                row_max, row_sum, kp, rows);
         return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
     }

@@ -1,7 +1,8 @@
 // C-ABI entry points of the integer attention library: argument checks,
 // host parameter derivation and the choice of device kernel.
 //
-// Kernel choice (all bit-identical to the specification in include/intattn.h):
+// Kernel choice (all bit-identical to the specification in include/intattn.h,
+// for every table size and K/V head grouping):
 //   Sq == 1 and Skv <= 16384                -> decode kernel (HBM streaming)
 //   Skv <= 512 (d = 64) or 256 (d = 128)      -> short-row kernel (K/V in LDS)
 //   otherwise                                -> long-row kernel (tiled, 3 passes)
@@ -24,33 +25,50 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Shape, head size and parameter derivation shared by every entry point.
+// lut_size: 32, 64 or 128; kv_heads: K/V heads (0: H), dividing H.
 int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
-                         IaKernelParams* kp) {
+                         IaKernelParams* kp, int lut_size = 32, int kv_heads = 0) {
     int st = intattn_validate_shape(shape, causal);
     if (st != INTATTN_OK) return st;
     if (shape->D != 64 && shape->D != 128) return INTATTN_E_DIM;
-    intattn_params prm;
-    st = intattn_derive_params(shape, scales, clip, &prm);
+    if (kv_heads < 0) return INTATTN_E_SHAPE;
+    const int hkv = kv_heads == 0 ? shape->H : kv_heads;
+    if (shape->H > 0 && (hkv < 1 || shape->H % hkv != 0)) return INTATTN_E_SHAPE;
+    uint16_t lut[kIaMaxLut] = {};
+    int32_t idx_mul = 0, x_clip = 0, req_shift = 0;
+    int64_t req_mul = 0;
+    st = intattn_derive_core(shape, scales, clip, lut_size, lut, &idx_mul, &x_clip, &req_shift, &req_mul);
     if (st != INTATTN_OK) return st;
     kp->B = shape->B;
     kp->H = shape->H;
     kp->Sq = shape->Sq;
     kp->Skv = shape->Skv;
     kp->causal = causal ? 1 : 0;
-    kp->idx_mul = prm.idx_mul;
-    kp->x_clip = prm.x_clip;
-    kp->req_shift = prm.req_shift;
-    kp->req_mul = static_cast<uint32_t>(prm.req_mul);
-    for (int i = 0; i < 16; ++i)
-        kp->lut2[i] = static_cast<uint32_t>(prm.lut[2 * i]) | (static_cast<uint32_t>(prm.lut[2 * i + 1]) << 16);
+    kp->idx_mul = idx_mul;
+    kp->x_clip = x_clip;
+    kp->req_shift = req_shift;
+    kp->req_mul = static_cast<uint32_t>(req_mul);
+    kp->lut_size = lut_size;
+    // slot word t = sat(y * -kM + k * 2^23): the largest k in {4, 2, 1} with
+    // k <= 128/N (the byte holds k * (N - 1) + k - 1) and kM within the
+    // 24-bit signed operand; k = 4 only for the 32-entry table
+    const int64_t m = idx_mul;
+    int k = 1;
+    if (lut_size == 32 && 4 * m < (int64_t(1) << 23)) k = 4;
+    else if (lut_size <= 64 && 2 * m < (int64_t(1) << 23)) k = 2;
+    kp->slot_k = k;
+    kp->slot_k_log2 = k == 4 ? 2 : k - 1;
+    kp->kv_group = shape->H > 0 ? shape->H / hkv : 1;
+    for (int i = 0; i < kIaMaxLut / 2; ++i)
+        kp->lut2[i] = static_cast<uint32_t>(lut[2 * i]) | (static_cast<uint32_t>(lut[2 * i + 1]) << 16);
     return INTATTN_OK;
 }
 
 int prepare(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
             const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
-            IaKernelParams* kp) {
+            IaKernelParams* kp, int lut_size = 32, int kv_heads = 0) {
     if (!q || !k || !v || !out || !shape || !scales) return INTATTN_E_NULL;
-    const int st = derive_kernel_params(shape, scales, clip, causal, kp);
+    const int st = derive_kernel_params(shape, scales, clip, causal, kp, lut_size, kv_heads);
     if (st != INTATTN_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return INTATTN_E_ALIGN;
     return INTATTN_OK;
@@ -95,6 +113,21 @@ extern "C" int intattn_forward_debug(const int8_t* q, const int8_t* k, const int
     return dispatch(q, k, v, out, shape->D, kp, stream, row_max, row_sum);
 }
 
+extern "C" int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
+                                  const intattn_shape* shape, const intattn_scales* scales, float clip,
+                                  int causal, const intattn_variant* variant, void* stream, int32_t* row_max,
+                                  uint32_t* row_sum) {
+    if ((row_max == nullptr) != (row_sum == nullptr)) return INTATTN_E_NULL;
+    const int lut_size = variant && variant->lut_size != 0 ? variant->lut_size : 32;
+    const int kv_heads = variant ? variant->kv_heads : 0;
+    IaKernelParams kp;
+    const int st = prepare(q, k, v, out, shape, scales, clip, causal, &kp, lut_size, kv_heads);
+    if (st != INTATTN_OK) return st;
+    if (rows_of(kp) == 0) return INTATTN_OK;
+    ia::clear_pending_hip_error();
+    return dispatch(q, k, v, out, shape->D, kp, stream, row_max, row_sum);
+}
+
 extern "C" int intattn_qk_scores(const int8_t* q, const int8_t* k, int32_t* scores, const intattn_shape* shape,
                                  void* stream) {
     if (!q || !k || !scores || !shape) return INTATTN_E_NULL;
@@ -107,6 +140,7 @@ extern "C" int intattn_qk_scores(const int8_t* q, const int8_t* k, int32_t* scor
     kp.H = shape->H;
     kp.Sq = shape->Sq;
     kp.Skv = shape->Skv;
+    kp.kv_group = 1;
     if (rows_of(kp) == 0) return INTATTN_OK;
     ia::clear_pending_hip_error();
     return ia::launch_qk_scores(q, k, scores, shape->D, kp, stream);
@@ -142,6 +176,7 @@ extern "C" int intattn_fp_softmax(const int32_t* scores, uint8_t* probs, const i
     kp.Sq = shape->Sq;
     kp.Skv = shape->Skv;
     kp.causal = causal ? 1 : 0;
+    kp.kv_group = 1;
     if (kp.Skv > ia::stage_max_keys()) return INTATTN_E_SHAPE;
     if (rows_of(kp) == 0) return INTATTN_OK;
     // dequantisation factor of a score: s_q * s_k / sqrt(D), rounded once to float32

@@ -4,7 +4,9 @@
 // The pages (IntAttention digest, "Methodology" step 2) describe a 32-entry
 // exp table indexed by the clipped integer score and an integer reciprocal
 // normalisation; the widths below are this library's fixed reading of them
-// (stated in include/intattn.h). All arithmetic is IEEE binary64 from float32
+// (stated in include/intattn.h). Finer tables of 64 or 128 entries (the
+// pages' "Limitations & Future Work", lookup-table granularity) change only
+// the bin width clip/(N-1) and the table. All arithmetic is IEEE binary64 from float32
 // inputs with correctly rounded operations only; the file is compiled with
 // -ffp-contract=off so no multiply-add is fused, and rint() (round half to
 // even in the default rounding mode) is the only rounding used.
@@ -37,13 +39,16 @@ struct NearestRounding {
     }
 };
 
-void fill_lut(double clip, uint16_t* lut) {
-    const double delta = clip / 31.0;
-    for (int k = 0; k < kLutSize - 1; ++k) {
+bool valid_lut_size(int n) { return n == 32 || n == 64 || n == 128; }
+
+// Entries k < n-1: rint(2^15 exp(-k clip/(n-1))); entry n-1: 0 (the sparse tail).
+void fill_lut(double clip, int n, uint16_t* lut) {
+    const double delta = clip / static_cast<double>(n - 1);
+    for (int k = 0; k < n - 1; ++k) {
         const double v = std::rint(kLutOne * std::exp(-(static_cast<double>(k) * delta)));
         lut[k] = static_cast<uint16_t>(v);
     }
-    lut[kLutSize - 1] = 0;
+    lut[n - 1] = 0;
 }
 
 }  // namespace
@@ -52,7 +57,16 @@ extern "C" int intattn_build_lut(float clip, uint16_t lut_out[32]) {
     if (!lut_out) return INTATTN_E_NULL;
     if (!finite_positive(clip)) return INTATTN_E_CLIP;
     NearestRounding guard;
-    fill_lut(static_cast<double>(clip), lut_out);
+    fill_lut(static_cast<double>(clip), kLutSize, lut_out);
+    return INTATTN_OK;
+}
+
+extern "C" int intattn_build_lut_ex(float clip, int32_t lut_size, uint16_t* lut_out) {
+    if (!lut_out) return INTATTN_E_NULL;
+    if (!valid_lut_size(lut_size)) return INTATTN_E_RANGE;
+    if (!finite_positive(clip)) return INTATTN_E_CLIP;
+    NearestRounding guard;
+    fill_lut(static_cast<double>(clip), lut_size, lut_out);
     return INTATTN_OK;
 }
 
@@ -69,9 +83,10 @@ int intattn_validate_shape(const intattn_shape* s, int causal) {
     return INTATTN_OK;
 }
 
-extern "C" int intattn_derive_params(const intattn_shape* shape, const intattn_scales* sc,
-                                     float clip, intattn_params* out) {
-    if (!shape || !sc || !out) return INTATTN_E_NULL;
+int intattn_derive_core(const intattn_shape* shape, const intattn_scales* sc, float clip, int lut_size,
+                        uint16_t* lut, int32_t* idx_mul, int32_t* x_clip, int32_t* req_shift, int64_t* req_mul) {
+    if (!shape || !sc || !lut || !idx_mul || !x_clip || !req_shift || !req_mul) return INTATTN_E_NULL;
+    if (!valid_lut_size(lut_size)) return INTATTN_E_RANGE;
     if (shape->D < 1) return INTATTN_E_SHAPE;
     if (!finite_positive(sc->q) || !finite_positive(sc->k) || !finite_positive(sc->v) ||
         !finite_positive(sc->o))
@@ -79,20 +94,17 @@ extern "C" int intattn_derive_params(const intattn_shape* shape, const intattn_s
     if (!finite_positive(clip)) return INTATTN_E_CLIP;
     NearestRounding guard;
 
+    const int n = lut_size;
     const double c = static_cast<double>(clip);
     const double alpha = (static_cast<double>(sc->q) * static_cast<double>(sc->k)) /
                          std::sqrt(static_cast<double>(shape->D));
-    const double delta = c / 31.0;
+    const double delta = c / static_cast<double>(n - 1);
     const double mu = alpha / delta;
     if (!(mu >= std::ldexp(1.0, -16) && mu < 0.5)) return INTATTN_E_RANGE;
 
-    intattn_params p{};
-    fill_lut(c, p.lut);
     const int64_t M = static_cast<int64_t>(std::rint(std::ldexp(mu, kIdxShift)));
-    p.idx_mul = static_cast<int32_t>(M);
-    p.idx_shift = kIdxShift;
-    const int64_t num = int64_t(61) << (kIdxShift - 1);  // x*M >= 61*2^23  <=>  slot >= 31
-    p.x_clip = static_cast<int32_t>((num + M - 1) / M);
+    // x*M >= (2n-3)*2^23  <=>  slot >= n-1
+    const int64_t num = int64_t(2 * n - 3) << (kIdxShift - 1);
 
     const double mu_o = static_cast<double>(sc->v) / (255.0 * static_cast<double>(sc->o));
     int e_o = 0;
@@ -104,8 +116,36 @@ extern "C" int intattn_derive_params(const intattn_shape* shape, const intattn_s
     }
     const int sh_o = kReqFrac - e_o;
     if (sh_o < 1 || sh_o > 63) return INTATTN_E_RANGE;
-    p.req_mul = Mo;
-    p.req_shift = sh_o;
+
+    fill_lut(c, n, lut);
+    *idx_mul = static_cast<int32_t>(M);
+    *x_clip = static_cast<int32_t>((num + M - 1) / M);
+    *req_shift = sh_o;
+    *req_mul = Mo;
+    return INTATTN_OK;
+}
+
+extern "C" int intattn_derive_params(const intattn_shape* shape, const intattn_scales* sc,
+                                     float clip, intattn_params* out) {
+    if (!shape || !sc || !out) return INTATTN_E_NULL;
+    intattn_params p{};
+    const int st = intattn_derive_core(shape, sc, clip, kLutSize, p.lut, &p.idx_mul, &p.x_clip, &p.req_shift,
+                                       &p.req_mul);
+    if (st != INTATTN_OK) return st;
+    p.idx_shift = kIdxShift;
+    *out = p;
+    return INTATTN_OK;
+}
+
+extern "C" int intattn_derive_params_ex(const intattn_shape* shape, const intattn_scales* sc, float clip,
+                                        int32_t lut_size, intattn_params_ex* out) {
+    if (!shape || !sc || !out) return INTATTN_E_NULL;
+    intattn_params_ex p{};
+    const int st = intattn_derive_core(shape, sc, clip, lut_size, p.lut, &p.idx_mul, &p.x_clip, &p.req_shift,
+                                       &p.req_mul);
+    if (st != INTATTN_OK) return st;
+    p.lut_size = lut_size;
+    p.idx_shift = kIdxShift;
     *out = p;
     return INTATTN_OK;
 }

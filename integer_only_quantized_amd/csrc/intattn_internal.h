@@ -10,17 +10,32 @@
 // Shape checks common to every entry point (no device access).
 int intattn_validate_shape(const intattn_shape* s, int causal);
 
+// Largest exp table of the variants (32 is the pages' table).
+constexpr int kIaMaxLut = 128;
+
 // Everything a kernel needs besides the tensor pointers, passed by value so
 // that it lands in kernel-argument (scalar) registers.
 struct IaKernelParams {
     int32_t B, H, Sq, Skv;
     int32_t causal;
     int32_t idx_mul;     // M, < 2^23
-    int32_t x_clip;      // smallest relative score that lands in slot 31
+    int32_t x_clip;      // smallest relative score that lands in the last slot
     int32_t req_shift;   // sh_o, 1..63
     uint32_t req_mul;    // M_o, in [2^30, 2^31)
-    uint32_t lut2[16];   // exp table, entries 2i and 2i+1 packed lo/hi
+    int32_t lut_size;    // N: 32, 64 or 128 entries; entry N-1 is 0
+    int32_t slot_k;      // slot-word scale k and table layout: 4 (N = 32, 4M < 2^23),
+                         // 2 (N <= 64, 2M < 2^23) or 1
+    int32_t slot_k_log2; // log2(k)
+    int32_t kv_group;    // query heads per K/V head (1: one K/V head each)
+    uint32_t lut2[kIaMaxLut / 2];   // exp table, entries 2i and 2i+1 packed lo/hi
 };
+
+// Host derivation of every integer the kernels receive, for a table of
+// lut_size entries (32, 64 or 128): the exp table, M, the clip point and the
+// requantisation pair. Errors as intattn_derive_params (E_RANGE also for an
+// unsupported lut_size).
+int intattn_derive_core(const intattn_shape* shape, const intattn_scales* sc, float clip, int lut_size,
+                        uint16_t* lut, int32_t* idx_mul, int32_t* x_clip, int32_t* req_shift, int64_t* req_mul);
 
 namespace ia {
 

@@ -32,7 +32,8 @@ def test_library_exports_every_declared_symbol():
     names = _declared()
     assert names == sorted(["intattn_build_lut", "intattn_derive_params", "intattn_forward",
                             "intattn_forward_debug", "intattn_strerror", "intattn_qk_scores",
-                            "intattn_index_softmax", "intattn_fp_softmax", "intattn_pv"])
+                            "intattn_index_softmax", "intattn_fp_softmax", "intattn_pv",
+                            "intattn_build_lut_ex", "intattn_derive_params_ex", "intattn_forward_ex"])
     for n in names:
         assert hasattr(B._lib, n), n
 
@@ -74,6 +75,58 @@ def test_params_equal_oracle_sweep():
             assert got["req_shift"] == ref.req_shift
             n += 1
     assert n > 500
+
+
+@pytest.mark.parametrize("n", [32, 64, 128])
+@pytest.mark.parametrize("clip", CLIPS[:6])
+def test_fine_lut_equals_oracle(n, clip):
+    assert B.build_lut_ex(clip, n) == list(O.build_lut(clip, n))
+
+
+@pytest.mark.parametrize("n", [64, 128])
+def test_fine_params_equal_oracle_sweep(n):
+    rng = np.random.default_rng(n)
+    checked = 0
+    for D in (16, 64, 128):
+        for _ in range(250):
+            sq, sk, sv, so = (float(np.float32(10 ** rng.uniform(-3.5, 0.3))) for _ in range(4))
+            clip = float(np.float32(rng.uniform(0.5, 12.0)))
+            try:
+                ref = O.derive_params(D, sq, sk, sv, so, clip, n)
+            except O.OracleRangeError:
+                with pytest.raises(B.IntAttnError) as ei:
+                    B.derive_params_ex(D, (sq, sk, sv, so), clip, n)
+                assert ei.value.code == -6
+                continue
+            got = B.derive_params_ex(D, (sq, sk, sv, so), clip, n)
+            assert got["lut"] == list(ref.lut) and got["lut_size"] == n
+            assert (got["idx_mul"], got["x_clip"]) == (ref.idx_mul, ref.x_clip)
+            assert (got["req_mul"], got["req_shift"]) == (ref.req_mul, ref.req_shift)
+            checked += 1
+    assert checked > 300
+
+
+def test_variant_validation_before_any_device_call():
+    E = {v: k for k, v in B.STATUS_NAMES.items()}
+    sh = B.Shape(1, 4, 8, 8, 64)
+    sc = B.Scales(0.05, 0.05, 0.05, 0.05)
+    rm = ctypes.c_void_p(0x5000)
+
+    def call(lut_size, kv_heads, row_max=None, row_sum=None):
+        var = B.Variant(lut_size, kv_heads)
+        return B._lib.intattn_forward_ex(0x1000, 0x2000, 0x3000, 0x4000, ctypes.byref(sh), ctypes.byref(sc),
+                                         O.DEFAULT_CLIP, 0, ctypes.byref(var), None, row_max, row_sum)
+    for bad in (16, 33, 96, 256, -32):
+        assert call(bad, 0) == E["INTATTN_E_RANGE"]
+    for bad in (3, 5, 8, -1):
+        assert call(32, bad) == E["INTATTN_E_SHAPE"]
+    assert call(64, 2, row_max=rm) == E["INTATTN_E_NULL"]
+    assert B._lib.intattn_build_lut_ex(O.DEFAULT_CLIP, 48, None) == E["INTATTN_E_NULL"]
+    buf = (ctypes.c_uint16 * 128)()
+    assert B._lib.intattn_build_lut_ex(O.DEFAULT_CLIP, 48, buf) == E["INTATTN_E_RANGE"]
+    # a 128-entry table raises mu fourfold over 32 entries: scales that fit 32 entries may not fit 128
+    assert B._lib.intattn_derive_params_ex(ctypes.byref(B.Shape(1, 1, 1, 1, 128)), ctypes.byref(B.Scales(0.8, 0.64, 0.4, 0.05)),
+                                           O.DEFAULT_CLIP, 128, ctypes.byref(B.ParamsEx())) == E["INTATTN_E_RANGE"]
 
 
 def _call(shape=(1, 1, 8, 8, 64), scales=(0.05, 0.05, 0.05, 0.05), clip=O.DEFAULT_CLIP,

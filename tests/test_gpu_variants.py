@@ -1,0 +1,132 @@
+"""GPU parity of the variants through intattn_forward_ex: finer exp tables (64
+and 128 entries) and grouped K/V heads (grouped-query / multi-query).
+
+Bar: bit-exact against the oracle (out, row max, row sum) on every kernel
+family: short rows (K/V of a head in LDS), long rows (tiled, three passes),
+decode (one query row), each with the slot-word scale k the host picks
+(4, 2 or 1 as the multiplier grows).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import intattn_oracle as O
+from integer_only_quantized_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+IA = pytest.importorskip("integer_only_quantized_amd._binding")
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _eq(name, got, ref):
+    got, ref = np.asarray(got), np.asarray(ref)
+    if not np.array_equal(got, ref):
+        bad = np.argwhere(got != ref)
+        raise AssertionError(f"{name}: {len(bad)} of {ref.size} differ; first at {bad[0].tolist()}: "
+                             f"got {got[tuple(bad[0])]} want {ref[tuple(bad[0])]}")
+
+
+def _run(q, k, v, scales, causal, lut_size, label):
+    H, Hkv = q.shape[1], k.shape[1]
+    _say(f"case {label} q={q.shape} kv={k.shape} causal={causal} lut={lut_size}")
+    out, rm, rs = IA.forward_ex(_dev(q), _dev(k), _dev(v), scales, O.DEFAULT_CLIP, causal, lut_size, stats=True)
+    torch.cuda.synchronize()
+    ref, m, E, _ = O.forward(q, k, v, scales, O.DEFAULT_CLIP, causal, stats=True, lut_size=lut_size,
+                             kv_heads=Hkv)
+    _eq(f"{label} out", out.cpu().numpy(), ref)
+    _eq(f"{label} row_max", rm.cpu().numpy(), m)
+    _eq(f"{label} row_sum", rs.cpu().numpy().view(np.uint32), E)
+    return ref
+
+
+FINE_CASES = [
+    # (B, H, Sq, Skv, D, causal, seed, kind): short, long, decode; ragged tails
+    (2, 2, 128, 128, 64, False, 400, "normal"),
+    (1, 2, 197, 197, 64, False, 401, "channel_outliers"),
+    (1, 2, 100, 256, 128, True, 402, "student_t_tail"),
+    (1, 2, 300, 700, 64, True, 403, "normal"),
+    (1, 2, 257, 600, 128, False, 404, "channel_outliers"),
+    (4, 2, 1, 3000, 128, False, 405, "normal"),
+    (2, 2, 1, 513, 64, False, 406, "student_t_tail"),
+]
+
+
+@pytest.mark.parametrize("n", [64, 128])
+@pytest.mark.parametrize("B,H,Sq,Skv,D,causal,seed,kind", FINE_CASES)
+def test_fine_table_bit_exact(n, B, H, Sq, Skv, D, causal, seed, kind):
+    w = W.make_random(B, H, Sq, Skv, D, causal, seed, kind, name="fine")
+    _run(w.q, w.k, w.v, w.scales, causal, n, f"fine{n}")
+
+
+def test_table_32_through_forward_ex_equals_forward():
+    w = W.make_random(2, 2, 150, 300, 64, True, 407, "normal", name="ex32")
+    out = _run(w.q, w.k, w.v, w.scales, True, 32, "ex32")
+    got = IA.forward(_dev(w.q), _dev(w.k), _dev(w.v), w.scales, w.clip, True).cpu().numpy()
+    _eq("forward == forward_ex", got, out)
+
+
+SCALE_K_CASES = [
+    # (lut_size, scale, k the host picks): the saturating slot word scaled by
+    # the largest k with k*M < 2^23 (4 -> 2 -> 1 as mu grows)
+    (32, 0.5, 2), (32, 0.7, 1), (64, 0.35, 2), (64, 0.5, 1), (128, 0.3, 1),
+]
+
+
+@pytest.mark.parametrize("n,scale,kexp", SCALE_K_CASES)
+@pytest.mark.parametrize("Sq,Skv,D,causal", [(40, 200, 64, False), (130, 700, 64, True), (1, 900, 64, False)])
+def test_slot_scale_choices(n, scale, kexp, Sq, Skv, D, causal):
+    rng = np.random.default_rng(int(scale * 100) + n + Skv)
+    q = rng.integers(-8, 9, (1, 2, Sq, D)).astype(np.int8)
+    k = rng.integers(-8, 9, (1, 2, Skv, D)).astype(np.int8)
+    v = rng.integers(-127, 128, (1, 2, Skv, D)).astype(np.int8)
+    scales = (scale, scale, 0.01, 0.01)
+    prm = O.derive_params(D, *scales, O.DEFAULT_CLIP, n)
+    kk = 128 // n
+    while kk > 1 and kk * prm.idx_mul >= 2 ** 23:
+        kk //= 2
+    assert kk == kexp
+    _run(q, k, v, scales, causal, n, f"k{kexp}_n{n}")
+
+
+GQA_CASES = [
+    # (B, H, Hkv, Sq, Skv, D, causal, lut): grouped-query and multi-query
+    (2, 8, 2, 128, 128, 64, False, 32),
+    (1, 8, 1, 200, 256, 128, True, 32),
+    (1, 4, 2, 300, 1000, 128, True, 64),
+    (1, 6, 3, 257, 600, 64, False, 128),
+    (4, 32, 8, 1, 2048, 128, False, 32),
+    (2, 8, 1, 1, 777, 64, False, 128),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,Sq,Skv,D,causal,lut", GQA_CASES)
+def test_grouped_kv_heads_bit_exact(B, H, Hkv, Sq, Skv, D, causal, lut):
+    w = W.make_random(B, H, Sq, Skv, D, causal, 500 + H + Hkv + Skv, "normal", name="gqa")
+    # K/V with Hkv heads (the first Hkv of the generated ones)
+    k = np.ascontiguousarray(w.k[:, :Hkv])
+    v = np.ascontiguousarray(w.v[:, :Hkv])
+    _run(w.q, k, v, w.scales, causal, lut, f"gqa{H}x{Hkv}")
+
+
+def test_bert_size_fine_table_sampled():
+    """BERT shape (8 x 12 x 512 x 64) with 128 entries: the launch the
+    variant benchmark times, every row of three heads compared."""
+    w = W.make_config("bert")
+    _say("case bert lut=128")
+    out, rm, rs = IA.forward_ex(_dev(w.q), _dev(w.k), _dev(w.v), w.scales, w.clip, False, 128, stats=True)
+    torch.cuda.synchronize()
+    out, rm, rs = out.cpu().numpy(), rm.cpu().numpy(), rs.cpu().numpy().view(np.uint32)
+    prm = O.derive_params(w.D, *w.scales, w.clip, 128)
+    for b, h in [(0, 0), (3, 7), (7, 11)]:
+        ref, m, E, _ = O.head_forward(w.q[b, h], w.k[b, h], w.v[b, h], prm, False)
+        _eq(f"bert128 out {b},{h}", out[b, h], ref)
+        _eq(f"bert128 m {b},{h}", rm[b, h], m)
+        _eq(f"bert128 E {b},{h}", rs[b, h], E)
