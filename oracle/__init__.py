@@ -9,3 +9,4 @@ from .intattn_oracle import (  # noqa: F401
     pv_requant, qk_scores, reciprocal, requantise, slot_index,
 )
 from .fp_baseline import dequant_alpha, fp_softmax_codes  # noqa: F401
+from .kv_cache import kv_append, quantise_f32  # noqa: F401
