@@ -136,8 +136,11 @@ int intattn_forward_debug(const int8_t* q, const int8_t* k, const int8_t* v, int
  * h / (H / kv_heads); kv_heads must divide H (kv_heads = H is ordinary
  * multi-head attention). */
 typedef struct intattn_variant {
-    int32_t lut_size;   /* exp-table entries: 32, 64 or 128; 0 means 32      */
-    int32_t kv_heads;   /* K/V heads; 0 means H                              */
+    int32_t lut_size;    /* exp-table entries: 32, 64 or 128; 0 means 32     */
+    int32_t kv_heads;    /* K/V heads; 0 means H                             */
+    int32_t kv_capacity; /* rows per K/V head in memory, >= Skv (a K/V cache
+                            of that capacity whose first Skv rows are
+                            attended); 0 means Skv                           */
 } intattn_variant;
 
 typedef struct intattn_params_ex {
@@ -160,17 +163,36 @@ int intattn_build_lut_ex(float clip, int32_t lut_size, uint16_t* lut_out);
 int intattn_derive_params_ex(const intattn_shape* shape, const intattn_scales* scales,
                              float clip, int32_t lut_size, intattn_params_ex* out);
 
-/* intattn_forward with a variant (NULL: lut_size 32, kv_heads H). q and out
- * are [B, H, Sq, D]; k and v are [B, kv_heads, Skv, D]. row_max / row_sum:
+/* intattn_forward with a variant (NULL: lut_size 32, kv_heads H, no cache
+ * padding). q and out are [B, H, Sq, D]; k and v are [B, kv_heads,
+ * kv_capacity, D], of which rows 0..Skv-1 of each head are read. row_max / row_sum:
  * optional device outputs [B, H, Sq] (both NULL or both set), as in
  * intattn_forward_debug. Every tensor pointer 16-byte aligned; allocates no
  * device memory. Errors: those of intattn_forward, E_NULL for one of
  * row_max / row_sum without the other, E_SHAPE for kv_heads < 0 or not
- * dividing H, E_RANGE for lut_size. */
+ * dividing H or for 0 < kv_capacity < Skv, E_RANGE for lut_size. */
 int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
                        const intattn_shape* shape, const intattn_scales* scales, float clip,
                        int causal, const intattn_variant* variant, void* stream,
                        int32_t* row_max, uint32_t* row_sum);
+
+/* Decode-step cache update (the step before attention in a decoder's decode
+ * step; the pages do not describe it): the keys and values of T new tokens,
+ * k_new and v_new float32 [B, kv_heads, T, D] in device memory, are coded to
+ * int8 and written to rows pos .. pos+T-1 of the caches k_cache and v_cache,
+ * int8 [B, kv_heads, capacity, D] in device memory; no other byte of the
+ * caches changes. Code of a value x under the cache's per-tensor scale s
+ * (s_k for keys, s_v for values): clip(rint(x / s), -127, 127), with x / s
+ * the IEEE float32 quotient (round to nearest, ties to even), rint rounding
+ * ties to even, NaN coded as 0 and +-inf as +-127 (the inputs' quantisation
+ * rule). The caches then feed intattn_forward_ex with kv_capacity =
+ * capacity and Skv = pos + T. All pointers 16-byte aligned; D 64 or 128;
+ * 0 <= pos, pos + T <= capacity <= 65535. Asynchronous on stream; allocates
+ * nothing. Errors: E_NULL, E_SHAPE, E_DIM, E_SCALE (s_k or s_v not finite
+ * and > 0), E_ALIGN, E_HIP. */
+int intattn_kv_append(const float* k_new, const float* v_new, int8_t* k_cache, int8_t* v_cache,
+                      int32_t B, int32_t kv_heads, int32_t T, int32_t D, int32_t capacity, int32_t pos,
+                      float s_k, float s_v, void* stream);
 
 /* ---- The pipeline as separate stages (scores and P in device memory) ----
  * The pages' "Methodology" step 1 places the cost of an INT8 pipeline in the

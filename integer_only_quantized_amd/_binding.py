@@ -53,7 +53,7 @@ class ParamsEx(ctypes.Structure):
 
 
 class Variant(ctypes.Structure):
-    _fields_ = [("lut_size", ctypes.c_int32), ("kv_heads", ctypes.c_int32)]
+    _fields_ = [("lut_size", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("kv_capacity", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -90,6 +90,8 @@ def _load():
     lib.intattn_forward_ex.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), ctypes.POINTER(Scales), f32, i32,
                                        ctypes.POINTER(Variant), vp, vp, vp]
     lib.intattn_forward_ex.restype = i32
+    lib.intattn_kv_append.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp]
+    lib.intattn_kv_append.restype = i32
     lib.intattn_qk_scores.argtypes = [vp, vp, vp, ctypes.POINTER(Shape), vp]
     lib.intattn_qk_scores.restype = i32
     lib.intattn_index_softmax.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), ctypes.POINTER(Scales),
@@ -333,19 +335,22 @@ def pv(probs, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False, out=N
 
 
 def forward_ex(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False, lut_size: int = 32,
-               stats: bool = False, out=None):
-    """intattn_forward_ex: q [B,H,Sq,D], k and v [B,Hkv,Skv,D] int8 CUDA tensors
-    (Hkv divides H; query head h reads K/V head h // (H // Hkv)), a table of
-    lut_size entries. Returns out, or (out, row_max, row_sum) with stats."""
+               stats: bool = False, out=None, skv: int = None):
+    """intattn_forward_ex: q [B,H,Sq,D], k and v [B,Hkv,C,D] int8 CUDA tensors
+    (Hkv divides H; query head h reads K/V head h // (H // Hkv)); the first
+    skv rows of each K/V head are attended (default all C: a cache of capacity
+    C holding skv tokens); a table of lut_size entries. Returns out, or
+    (out, row_max, row_sum) with stats."""
     import torch
-    B, H, Sq, Skv, D = _check_tensors(q, k, v, grouped=True)
+    B, H, Sq, C, D = _check_tensors(q, k, v, grouped=True)
+    skv = C if skv is None else int(skv)
     if out is None:
         out = torch.empty_like(q)
     elif (out.shape != q.shape or out.dtype is not torch.int8 or not out.is_contiguous()
           or out.device != q.device):
         raise ValueError("out must be a contiguous int8 tensor shaped like q, on q's device")
-    var = Variant(int(lut_size), int(k.shape[1]))
-    sh, sc = _structs((B, H, Sq, Skv, D), scales)
+    var = Variant(int(lut_size), int(k.shape[1]), int(C))
+    sh, sc = _structs((B, H, Sq, skv, D), scales)
     rm = rs = None
     if stats:
         rm = torch.empty((B, H, Sq), dtype=torch.int32, device=q.device)
@@ -355,3 +360,21 @@ def forward_ex(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False
                                    rm.data_ptr() if stats else None, rs.data_ptr() if stats else None)
     _check(code, "intattn_forward_ex")
     return (out, rm, rs) if stats else out
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, pos: int, s_k: float, s_v: float):
+    """intattn_kv_append: code float32 k_new, v_new [B,Hkv,T,D] (CUDA) into rows
+    pos .. pos+T-1 of the int8 caches [B,Hkv,C,D] (in place)."""
+    import torch
+    for name, t, dt in (("k_new", k_new, torch.float32), ("v_new", v_new, torch.float32),
+                        ("k_cache", k_cache, torch.int8), ("v_cache", v_cache, torch.int8)):
+        if t.dtype is not dt or not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D {dt} CUDA tensor")
+    B, Hkv, T, D = k_new.shape
+    if v_new.shape != k_new.shape or k_cache.shape != v_cache.shape or k_cache.shape[:2] != (B, Hkv) \
+            or k_cache.shape[3] != D:
+        raise ValueError("shape mismatch between the new tokens and the caches")
+    code = _lib.intattn_kv_append(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                  B, Hkv, T, D, k_cache.shape[2], int(pos), float(s_k), float(s_v),
+                                  _stream(k_new))
+    _check(code, "intattn_kv_append")

@@ -52,8 +52,8 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
     const int bid = P.kv_group > 1 ? xcd_local_block(blockIdx.x, gridDim.x) : static_cast<int>(blockIdx.x);
     const size_t head = static_cast<size_t>(bid);
     const size_t kvhead = static_cast<size_t>(bid / P.kv_group);
-    const int8_t* kh = k + kvhead * P.Skv * D;
-    const int8_t* vh = v + kvhead * P.Skv * D;
+    const int8_t* kh = k + kvhead * P.kv_rows * D;
+    const int8_t* vh = v + kvhead * P.kv_rows * D;
     const v4i qv = *reinterpret_cast<const v4i*>(q + head * D + 16 * c);
     if (wave == 0) fill_lut_u16(P, s_lut, lane);
 

@@ -63,8 +63,8 @@ __global__ __launch_bounds__(256) void ia_general_kernel(
     const size_t head = static_cast<size_t>(b) * P.H + h;
     const int8_t* qh = q + head * P.Sq * D;
     const size_t kvhead = static_cast<size_t>(b) * (P.H / P.kv_group) + h / P.kv_group;   // grouped K/V heads
-    const int8_t* kh = k + kvhead * P.Skv * D;
-    const int8_t* vh = v + kvhead * P.Skv * D;
+    const int8_t* kh = k + kvhead * P.kv_rows * D;
+    const int8_t* vh = v + kvhead * P.kv_rows * D;
 
     if (wave == 0) fill_lut_u16(P, slut, lane);
 

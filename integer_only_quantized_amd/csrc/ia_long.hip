@@ -100,8 +100,8 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     const size_t head = static_cast<size_t>(head_i);
     const int8_t* qh = q + head * P.Sq * D;
     const size_t kvhead = static_cast<size_t>(head_i / P.kv_group);   // grouped K/V heads
-    const int8_t* kh = k + kvhead * P.Skv * D;
-    const int8_t* vh = v + kvhead * P.Skv * D;
+    const int8_t* kh = k + kvhead * P.kv_rows * D;
+    const int8_t* vh = v + kvhead * P.kv_rows * D;
 
     const int shift = P.Skv - P.Sq;
     const int q0 = qb * kLongRows;

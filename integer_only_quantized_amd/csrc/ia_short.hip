@@ -91,8 +91,8 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     const size_t head = static_cast<size_t>(bid / nqb);
     const int8_t* qh = q + head * P.Sq * D;
     const size_t kvhead = static_cast<size_t>(static_cast<int>(head) / P.kv_group);   // grouped K/V heads
-    const int8_t* kh = k + kvhead * P.Skv * D;
-    const int8_t* vh = v + kvhead * P.Skv * D;
+    const int8_t* kh = k + kvhead * P.kv_rows * D;
+    const int8_t* vh = v + kvhead * P.kv_rows * D;
 
     // ---- staging ---------------------------------------------------------------
     // Each wave stages the key blocks of its own half that it reads (the two

@@ -25,15 +25,19 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Shape, head size and parameter derivation shared by every entry point.
-// lut_size: 32, 64 or 128; kv_heads: K/V heads (0: H), dividing H.
+// lut_size: 32, 64 or 128; kv_heads: K/V heads (0: H), dividing H;
+// kv_capacity: rows per K/V head in memory (0: Skv), at least Skv.
 int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
-                         IaKernelParams* kp, int lut_size = 32, int kv_heads = 0) {
+                         IaKernelParams* kp, int lut_size = 32, int kv_heads = 0, int kv_capacity = 0) {
     int st = intattn_validate_shape(shape, causal);
     if (st != INTATTN_OK) return st;
     if (shape->D != 64 && shape->D != 128) return INTATTN_E_DIM;
     if (kv_heads < 0) return INTATTN_E_SHAPE;
     const int hkv = kv_heads == 0 ? shape->H : kv_heads;
     if (shape->H > 0 && (hkv < 1 || shape->H % hkv != 0)) return INTATTN_E_SHAPE;
+    if (kv_capacity < 0 || (kv_capacity != 0 && kv_capacity < shape->Skv)) return INTATTN_E_SHAPE;
+    const int rows = kv_capacity == 0 ? shape->Skv : kv_capacity;
+    if (static_cast<double>(shape->B) * hkv * rows * shape->D > 9.0e15) return INTATTN_E_SHAPE;
     uint16_t lut[kIaMaxLut] = {};
     int32_t idx_mul = 0, x_clip = 0, req_shift = 0;
     int64_t req_mul = 0;
@@ -59,6 +63,7 @@ int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scale
     kp->slot_k = k;
     kp->slot_k_log2 = k == 4 ? 2 : k - 1;
     kp->kv_group = shape->H > 0 ? shape->H / hkv : 1;
+    kp->kv_rows = rows;
     for (int i = 0; i < kIaMaxLut / 2; ++i)
         kp->lut2[i] = static_cast<uint32_t>(lut[2 * i]) | (static_cast<uint32_t>(lut[2 * i + 1]) << 16);
     return INTATTN_OK;
@@ -66,9 +71,9 @@ int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scale
 
 int prepare(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
             const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
-            IaKernelParams* kp, int lut_size = 32, int kv_heads = 0) {
+            IaKernelParams* kp, int lut_size = 32, int kv_heads = 0, int kv_capacity = 0) {
     if (!q || !k || !v || !out || !shape || !scales) return INTATTN_E_NULL;
-    const int st = derive_kernel_params(shape, scales, clip, causal, kp, lut_size, kv_heads);
+    const int st = derive_kernel_params(shape, scales, clip, causal, kp, lut_size, kv_heads, kv_capacity);
     if (st != INTATTN_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return INTATTN_E_ALIGN;
     return INTATTN_OK;
@@ -120,8 +125,9 @@ extern "C" int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t
     if ((row_max == nullptr) != (row_sum == nullptr)) return INTATTN_E_NULL;
     const int lut_size = variant && variant->lut_size != 0 ? variant->lut_size : 32;
     const int kv_heads = variant ? variant->kv_heads : 0;
+    const int kv_capacity = variant ? variant->kv_capacity : 0;
     IaKernelParams kp;
-    const int st = prepare(q, k, v, out, shape, scales, clip, causal, &kp, lut_size, kv_heads);
+    const int st = prepare(q, k, v, out, shape, scales, clip, causal, &kp, lut_size, kv_heads, kv_capacity);
     if (st != INTATTN_OK) return st;
     if (rows_of(kp) == 0) return INTATTN_OK;
     ia::clear_pending_hip_error();
@@ -141,6 +147,7 @@ extern "C" int intattn_qk_scores(const int8_t* q, const int8_t* k, int32_t* scor
     kp.Sq = shape->Sq;
     kp.Skv = shape->Skv;
     kp.kv_group = 1;
+    kp.kv_rows = shape->Skv;
     if (rows_of(kp) == 0) return INTATTN_OK;
     ia::clear_pending_hip_error();
     return ia::launch_qk_scores(q, k, scores, shape->D, kp, stream);
@@ -177,6 +184,7 @@ extern "C" int intattn_fp_softmax(const int32_t* scores, uint8_t* probs, const i
     kp.Skv = shape->Skv;
     kp.causal = causal ? 1 : 0;
     kp.kv_group = 1;
+    kp.kv_rows = shape->Skv;
     if (kp.Skv > ia::stage_max_keys()) return INTATTN_E_SHAPE;
     if (rows_of(kp) == 0) return INTATTN_OK;
     // dequantisation factor of a score: s_q * s_k / sqrt(D), rounded once to float32
@@ -196,4 +204,20 @@ extern "C" int intattn_pv(const uint8_t* probs, const int8_t* v, int8_t* out, co
     if (rows_of(kp) == 0) return INTATTN_OK;
     ia::clear_pending_hip_error();
     return ia::launch_pv(probs, v, out, shape->D, kp, stream);
+}
+
+extern "C" int intattn_kv_append(const float* k_new, const float* v_new, int8_t* k_cache, int8_t* v_cache,
+                                 int32_t B, int32_t kv_heads, int32_t T, int32_t D, int32_t capacity, int32_t pos,
+                                 float s_k, float s_v, void* stream) {
+    if (!k_new || !v_new || !k_cache || !v_cache) return INTATTN_E_NULL;
+    if (B < 0 || kv_heads < 0 || T < 0 || capacity < 1 || capacity > 65535 || pos < 0 ||
+        static_cast<int64_t>(pos) + T > capacity)
+        return INTATTN_E_SHAPE;
+    if (D != 64 && D != 128) return INTATTN_E_DIM;
+    if (static_cast<double>(B) * kv_heads * capacity * D > 9.0e15) return INTATTN_E_SHAPE;
+    if (!(s_k > 0.0f) || !(s_v > 0.0f) || !std::isfinite(s_k) || !std::isfinite(s_v)) return INTATTN_E_SCALE;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)) return INTATTN_E_ALIGN;
+    if (static_cast<int64_t>(B) * kv_heads * T == 0) return INTATTN_OK;
+    ia::clear_pending_hip_error();
+    return ia::launch_kv_append(k_new, v_new, k_cache, v_cache, B, kv_heads, T, D, capacity, pos, s_k, s_v, stream);
 }

@@ -27,6 +27,7 @@ struct IaKernelParams {
                          // 2 (N <= 64, 2M < 2^23) or 1
     int32_t slot_k_log2; // log2(k)
     int32_t kv_group;    // query heads per K/V head (1: one K/V head each)
+    int32_t kv_rows;     // rows per K/V head in memory (>= Skv: a cache of that capacity)
     uint32_t lut2[kIaMaxLut / 2];   // exp table, entries 2i and 2i+1 packed lo/hi
 };
 
@@ -65,6 +66,11 @@ int launch_decode(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out
 // Any shape (used for long rows): K/V tiles streamed through LDS, three passes.
 int launch_long(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
                 const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum);
+
+// Decode-step cache update: quantise T new tokens (float32) per (b, K/V head)
+// into rows pos .. pos+T-1 of the int8 caches [B, Hkv, capacity, D].
+int launch_kv_append(const float* k_new, const float* v_new, int8_t* k_cache, int8_t* v_cache, int B, int Hkv,
+                     int T, int D, int capacity, int pos, float s_k, float s_v, void* stream);
 
 // Unfused pipeline stages (scores and probabilities in HBM). The softmax
 // stages hold a row in registers: Skv <= stage_max_keys().

@@ -33,7 +33,8 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted(["intattn_build_lut", "intattn_derive_params", "intattn_forward",
                             "intattn_forward_debug", "intattn_strerror", "intattn_qk_scores",
                             "intattn_index_softmax", "intattn_fp_softmax", "intattn_pv",
-                            "intattn_build_lut_ex", "intattn_derive_params_ex", "intattn_forward_ex"])
+                            "intattn_build_lut_ex", "intattn_derive_params_ex", "intattn_forward_ex",
+                            "intattn_kv_append"])
     for n in names:
         assert hasattr(B._lib, n), n
 
@@ -127,6 +128,40 @@ def test_variant_validation_before_any_device_call():
     # a 128-entry table raises mu fourfold over 32 entries: scales that fit 32 entries may not fit 128
     assert B._lib.intattn_derive_params_ex(ctypes.byref(B.Shape(1, 1, 1, 1, 128)), ctypes.byref(B.Scales(0.8, 0.64, 0.4, 0.05)),
                                            O.DEFAULT_CLIP, 128, ctypes.byref(B.ParamsEx())) == E["INTATTN_E_RANGE"]
+
+
+def test_kv_append_validation_before_any_device_call():
+    E = {v: k for k, v in B.STATUS_NAMES.items()}
+    P = (0x1000, 0x2000, 0x3000, 0x4000)
+
+    def call(ptrs=P, B_=2, H=4, T=1, D=128, cap=64, pos=10, sk=0.05, sv=0.05):
+        return B._lib.intattn_kv_append(*ptrs, B_, H, T, D, cap, pos, sk, sv, None)
+    assert call(ptrs=(0, 0x2000, 0x3000, 0x4000)) == E["INTATTN_E_NULL"]
+    assert call(ptrs=(0x1000, 0x2000, 0x3000, 0)) == E["INTATTN_E_NULL"]
+    assert call(pos=-1) == E["INTATTN_E_SHAPE"]
+    assert call(pos=64) == E["INTATTN_E_SHAPE"]                 # pos + T > capacity
+    assert call(T=55, pos=10) == E["INTATTN_E_SHAPE"]
+    assert call(cap=0, pos=0) == E["INTATTN_E_SHAPE"]
+    assert call(cap=65536, pos=0) == E["INTATTN_E_SHAPE"]
+    assert call(B_=-1) == E["INTATTN_E_SHAPE"]
+    assert call(D=96) == E["INTATTN_E_DIM"]
+    for bad in (0.0, -1.0, math.inf, math.nan):
+        assert call(sk=bad) == E["INTATTN_E_SCALE"]
+        assert call(sv=bad) == E["INTATTN_E_SCALE"]
+    assert call(ptrs=(0x1004, 0x2000, 0x3000, 0x4000)) == E["INTATTN_E_ALIGN"]
+    assert call(ptrs=(0x1000, 0x2000, 0x3000, 0x4008)) == E["INTATTN_E_ALIGN"]
+    assert call(T=0) == E["INTATTN_OK"]                          # nothing to do, no device call
+    assert call(B_=0) == E["INTATTN_OK"]
+
+
+def test_cache_capacity_validation():
+    E = {v: k for k, v in B.STATUS_NAMES.items()}
+    sh = B.Shape(1, 4, 1, 100, 64)
+    sc = B.Scales(0.05, 0.05, 0.05, 0.05)
+    for cap, want in ((99, "INTATTN_E_SHAPE"), (-5, "INTATTN_E_SHAPE")):
+        var = B.Variant(32, 2, cap)
+        assert B._lib.intattn_forward_ex(0x1000, 0x2000, 0x3000, 0x4000, ctypes.byref(sh), ctypes.byref(sc),
+                                         O.DEFAULT_CLIP, 0, ctypes.byref(var), None, None, None) == E[want]
 
 
 def _call(shape=(1, 1, 8, 8, 64), scales=(0.05, 0.05, 0.05, 0.05), clip=O.DEFAULT_CLIP,
