@@ -23,6 +23,7 @@ they do not stay in the caches) gives the cold-input rate.
     python bench.py --calibrate peaks   # measured copy GB/s, int8 MFMA TOPS, VALU ops/s
     python bench.py --calibrate copy    # three 256 MiB device copies (counter scaling run)
     python bench.py --breakdown         # per-stage times of the unfused pipelines
+    python bench.py --variants          # finer tables, grouped K/V heads, cache update
 """
 from __future__ import annotations
 
@@ -299,6 +300,110 @@ def breakdown(config, steps=None):
     return 0
 
 
+def _time_calls(fn, stream, n, warm_s=0.3):
+    """Median-free event timing: warm-up for warm_s seconds, then n calls; us per call."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3
+
+
+def variants(steps=None):
+    """The variants beside the 32-entry MHA path: finer exp tables (64, 128
+    entries) on the BERT and causal-prefill workloads (int8 TOPS and MFMA
+    fraction), grouped K/V heads on the batched decode shape (HBM GB/s of
+    Q + K + V + O with K/V read once per K/V head), and the decode-step cache
+    update (HBM GB/s of 4 bytes read and 1 written per value). One JSON line."""
+    import torch
+
+    from integer_only_quantized_amd import _binding as ia
+    from integer_only_quantized_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {"variants": True, "fine_tables": {}, "grouped_decode": {}, "kv_append": {}, "decode_step": {}}
+
+    for cfg in ("bert", "llama_prefill"):
+        w = W.make_config(cfg)
+        q, k, v = (torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
+        out = torch.empty_like(q)
+        ops, _, _ = algorithmic_work(w)
+        row = {}
+        for n in (32, 64, 128):
+            try:
+                ia.derive_params_ex(w.D, w.scales, w.clip, n)
+            except ia.IntAttnError:
+                row[str(n)] = {"refused": "index multiplier outside [2^-16, 2^-1) for this table"}
+                continue
+            fn = lambda n=n: ia.forward_ex(q, k, v, w.scales, w.clip, w.causal, n, out=out)
+            us = _time_calls(fn, stream, steps or (200 if cfg == "bert" else 30))
+            tops = ops / (us * 1e-6) / 1e12
+            row[str(n)] = {"us_per_call": us, "int8_TOPS": tops, "mfma_frac": tops / PEAK_INT8_TOPS}
+        res["fine_tables"][cfg] = row
+
+    # grouped K/V heads on the decode shape: B=16, H=32, Skv=8192, d=128
+    B, H, Skv, D = 16, 32, 8192, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    def codes(shape):
+        x = torch.randn(shape, generator=g, device=dev) * (127.0 / 4.5)
+        return x.round().clamp_(-127, 127).to(torch.int8)
+    q = codes((B, H, 1, D))
+    scales = (4.5 / 127, 4.5 / 127, 4.5 / 127, 0.6 / 127)
+    for hkv in (32, 8, 1):
+        k = codes((B, hkv, Skv, D))
+        v = codes((B, hkv, Skv, D))
+        out = torch.empty_like(q)
+        fn = lambda: ia.forward_ex(q, k, v, scales, W.DEFAULT_CLIP, False, 32, out=out)
+        us = _time_calls(fn, stream, steps or 100)
+        nbytes = 2 * B * H * D + 2 * B * hkv * Skv * D
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res["grouped_decode"][f"Hkv={hkv}"] = {"us_per_call": us, "bytes": nbytes, "GBs": gbs,
+                                               "hbm_frac": gbs / PEAK_HBM_GBS}
+        del k, v
+    torch.cuda.empty_cache()
+
+    # cache update: one decode token and a 4096-token prefill chunk
+    for name, (Bc, hkv, T, cap) in {"decode_token": (16, 8, 1, 8192), "prefill_chunk": (1, 32, 4096, 4096)}.items():
+        kc = torch.zeros((Bc, hkv, cap, D), dtype=torch.int8, device=dev)
+        vc = torch.zeros_like(kc)
+        kn = torch.randn((Bc, hkv, T, D), generator=g, device=dev)
+        vn = torch.randn((Bc, hkv, T, D), generator=g, device=dev)
+        pos = cap - T
+        fn = lambda: ia.kv_append(kn, vn, kc, vc, pos, 0.035, 0.035)
+        us = _time_calls(fn, stream, steps or 200)
+        nbytes = 2 * 5 * Bc * hkv * T * D
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res["kv_append"][name] = {"shape": [Bc, hkv, T, D], "us_per_call": us, "bytes": nbytes, "GBs": gbs,
+                                  "hbm_frac": gbs / PEAK_HBM_GBS}
+        del kc, vc, kn, vn
+
+    # one grouped-query decode step: append the token, attend over the cache
+    Bc, hkv, cap, filled = 16, 8, 8192, 8191
+    kc = codes((Bc, hkv, cap, D))
+    vc = codes((Bc, hkv, cap, D))
+    kn = torch.randn((Bc, hkv, 1, D), generator=g, device=dev)
+    vn = torch.randn((Bc, hkv, 1, D), generator=g, device=dev)
+    out = torch.empty_like(q)
+    def step():
+        ia.kv_append(kn, vn, kc, vc, filled, 4.5 / 127, 4.5 / 127)
+        ia.forward_ex(q, kc, vc, scales, W.DEFAULT_CLIP, False, 32, out=out, skv=filled + 1)
+    us = _time_calls(step, stream, steps or 100)
+    res["decode_step"] = {"shape": {"B": Bc, "H": H, "Hkv": hkv, "Skv": filled + 1, "D": D},
+                          "us_per_step": us, "steps_per_s": 1e6 / us}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,6 +416,8 @@ def main(argv=None):
     ap.add_argument("--calibrate", choices=["peaks", "copy"], default=None)
     ap.add_argument("--breakdown", action="store_true",
                     help="per-stage times of the unfused pipelines (integer and float32 softmax)")
+    ap.add_argument("--variants", action="store_true",
+                    help="finer exp tables, grouped K/V heads and the cache update (one JSON line)")
     ap.add_argument("--no-extra-timing", action="store_true",
                     help="skip the median-of-5 and cold-input blocks")
     args = ap.parse_args(argv)
@@ -325,6 +432,8 @@ def main(argv=None):
         return calibrate(args.calibrate)
     if args.breakdown:
         return breakdown(args.config, args.steps)
+    if args.variants:
+        return variants(args.steps)
 
     import numpy as np
     import torch
