@@ -42,6 +42,12 @@ default):
   * grouped K/V heads: kv_heads K/V heads shared by the H query heads in
     consecutive groups of G = H/kv_heads (query head h reads K/V head h//G);
     kv_heads = H is ordinary multi-head attention, 1 is multi-query.
+  * uint16 probabilities: the dynamic-range item of the same section warns
+    of underflow on skewed or long score rows (a uint8 row of n >= 513
+    uniform keys is all zeros). prob_bits = 16: target row sum 65535,
+    R16 = floor((65535*2^16 + floor(E/2)) / E) and p = (e*R16 + 2^15) >> 16
+    (uint16; e*R16 + 2^15 < 2^32), and the output multiplier
+    mu_o = s_v / (65535 * s_o); every other step is unchanged.
 
 Parity pins: see tests/test_oracle_*.py. Every function here is pinned by a
 property, closed form, brute-force twin or exact-rational bound; none is
@@ -63,6 +69,9 @@ LUT_ONE = 1 << 15             # Q15: table entry for a zero relative score
 IDX_SHIFT = 24                # fixed-point fraction bits of the bin multiplier
 P_ONE = 255                   # uint8 probabilities, target row sum 255
 R_SHIFT = 23                  # reciprocal fixed point: R = round(255*2^23 / E)
+P16_ONE = 65535               # uint16 probabilities (variant), target row sum 65535
+R16_SHIFT = 16                # R16 = round(65535*2^16 / E)
+PROB_BITS = (8, 16)
 REQ_FRAC = 31                 # requantisation multiplier normalised to [2^30, 2^31)
 SKV_MAX = 65535               # keeps E < 2^31 and every int32 accumulator exact
 MU_MIN = 2.0 ** -16           # bin multiplier range (index units per score unit)
@@ -93,8 +102,9 @@ class Params:
     alpha: float          # logit units per integer score unit
     delta: float          # table bin width in logit units
     mu: float             # alpha / delta
-    mu_o: float           # s_v / (255 * s_o)
+    mu_o: float           # s_v / (P_one * s_o), P_one = 255 or 65535
     lut_size: int = LUT_SIZE  # N: table entries (slots 0..N-1)
+    prob_bits: int = 8        # probability width: 8 (uint8) or 16 (uint16 variant)
 
 
 def _f32(x) -> float:
@@ -126,7 +136,7 @@ def build_lut(clip: float, lut_size: int = LUT_SIZE) -> tuple:
 
 
 def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
-                  clip: float, lut_size: int = LUT_SIZE) -> Params:
+                  clip: float, lut_size: int = LUT_SIZE, prob_bits: int = 8) -> Params:
     """Host parameter derivation.
 
     alpha = s_q*s_k/sqrt(D) folds the 1/sqrt(d) attention scale into the
@@ -134,6 +144,8 @@ def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
     table slots; M = round(mu * 2^24).
     """
     n = _check_lut_size(lut_size)
+    if prob_bits not in PROB_BITS:
+        raise OracleRangeError("prob_bits must be 8 or 16")
     if D < 1:
         raise OracleRangeError("D must be >= 1")
     sq, sk, sv, so, c = (_f32(s) for s in (s_q, s_k, s_v, s_o, clip))
@@ -150,7 +162,7 @@ def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
     # smallest x with (x*M + 2^23) >> 24 >= N-1, i.e. x*M >= (2N-3) * 2^23
     num = (2 * n - 3) << (IDX_SHIFT - 1)
     x_clip = -(-num // idx_mul)
-    mu_o = sv / (255.0 * so)
+    mu_o = sv / ((255.0 if prob_bits == 8 else 65535.0) * so)
     m_o, e_o = math.frexp(mu_o)
     req_mul = int(round(math.ldexp(m_o, REQ_FRAC)))
     if req_mul == (1 << REQ_FRAC):
@@ -161,7 +173,7 @@ def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
         raise OracleRangeError("output multiplier outside the encodable range")
     return Params(lut=lut, idx_mul=idx_mul, idx_shift=IDX_SHIFT, x_clip=x_clip,
                   req_mul=req_mul, req_shift=req_shift, alpha=alpha, delta=delta,
-                  mu=mu, mu_o=mu_o, lut_size=n)
+                  mu=mu, mu_o=mu_o, lut_size=n, prob_bits=prob_bits)
 
 
 # ---------------------------------------------------------------------------
@@ -183,6 +195,18 @@ def reciprocal(E):
     """Integer reciprocal of the row sum: R = floor((255*2^23 + floor(E/2)) / E)."""
     E = np.asarray(E, dtype=np.int64)
     return (np.int64(P_ONE << R_SHIFT) + E // 2) // E
+
+
+def reciprocal16(E):
+    """uint16 variant: R16 = floor((65535*2^16 + floor(E/2)) / E)."""
+    E = np.asarray(E, dtype=np.int64)
+    return (np.int64(P16_ONE << R16_SHIFT) + E // 2) // E
+
+
+def normalise16(e, R):
+    """uint16 variant: p = (e*R16 + 2^15) >> 16 (round half up)."""
+    e = np.asarray(e, dtype=np.int64)
+    return (e * R + np.int64(1 << (R16_SHIFT - 1))) >> np.int64(R16_SHIFT)
 
 
 def normalise(e, R):
@@ -231,8 +255,9 @@ def index_softmax(S, prm: Params, causal: bool):
 
     Row max over the allowed keys, relative scores x = m - s, table slots with
     the sparsity-aware clip, int32 row sum E of the table entries, integer
-    reciprocal R and uint8 probabilities p = (e*R + 2^22) >> 23. Keys that are
-    not allowed take the last slot (entry 0, p = 0). Returns P uint8 [Sq, Skv],
+    reciprocal R and uint8 probabilities p = (e*R + 2^22) >> 23 (uint16
+    variant: p = (e*R16 + 2^15) >> 16). Keys that are not allowed take the
+    last slot (entry 0, p = 0). Returns P uint8 (or uint16) [Sq, Skv],
     m int64 [Sq], E int64 [Sq].
     """
     S = np.asarray(S, dtype=np.int64)
@@ -245,6 +270,9 @@ def index_softmax(S, prm: Params, causal: bool):
     lut = np.asarray(prm.lut, dtype=np.int64)
     e = lut[idx]
     E = e.sum(axis=1)
+    if prm.prob_bits == 16:
+        P = normalise16(e, reciprocal16(E)[:, None])
+        return P.astype(np.uint16), m, E
     R = reciprocal(E)
     P = normalise(e, R[:, None])
     return P.astype(np.uint8), m, E
@@ -289,23 +317,24 @@ def check_args(q, k, v, causal, kv_heads=None):
 
 
 def forward(q, k, v, scales, clip=DEFAULT_CLIP, causal=False, stats=False,
-            lut_size=LUT_SIZE, kv_heads=None):
+            lut_size=LUT_SIZE, kv_heads=None, prob_bits=8):
     """Full forward over int8 tensors q [B, H, Sq, D], k and v [B, Hkv, Skv, D].
 
     scales = (s_q, s_k, s_v, s_o); lut_size: table entries (32 is the pages'
     table); kv_heads = Hkv (None: H), query head h reading K/V head
-    h // (H // Hkv). Returns out int8 [B, H, Sq, D]; with stats=True also
-    (m int64 [B,H,Sq], E int64 [B,H,Sq], P uint8 [B,H,Sq,Skv]).
+    h // (H // Hkv); prob_bits: 8 (uint8 P) or 16 (uint16 variant). Returns
+    out int8 [B, H, Sq, D]; with stats=True also (m int64 [B,H,Sq],
+    E int64 [B,H,Sq], P uint8/uint16 [B,H,Sq,Skv]).
     """
     q, k, v = (np.ascontiguousarray(t) for t in (q, k, v))
     B, H, Sq, Skv, D = check_args(q, k, v, causal, kv_heads)
     group = H // k.shape[1]
-    prm = derive_params(D, *scales, clip, lut_size)
+    prm = derive_params(D, *scales, clip, lut_size, prob_bits)
     out = np.zeros((B, H, Sq, D), dtype=np.int8)
     if stats:
         M = np.zeros((B, H, Sq), dtype=np.int64)
         Es = np.zeros((B, H, Sq), dtype=np.int64)
-        Ps = np.zeros((B, H, Sq, Skv), dtype=np.uint8)
+        Ps = np.zeros((B, H, Sq, Skv), dtype=np.uint8 if prob_bits == 8 else np.uint16)
     for b in range(B):
         for h in range(H):
             o, m, E, P = head_forward(q[b, h], k[b, h // group], v[b, h // group], prm, causal)

@@ -13,8 +13,8 @@ operand, a wrong axis, an off-by-one in a rounding) shows up as a mismatch:
   * the slot of a relative score x is found as the nearest bin centre by
     exact rational comparison (|x*mu_q - k| minimal, ties to the upper bin),
     where mu_q = M / 2^24 is the encoded multiplier, not by a shift formula;
-  * probabilities and the requantised output are rounded with Fractions
-    (floor(v + 1/2)), not with add-and-shift.
+  * probabilities (uint8, or the uint16 variant) and the requantised output
+    are rounded with Fractions (floor(v + 1/2)), not with add-and-shift.
 
 Meant for tiny shapes only (Sq, Skv <= ~32).
 """
@@ -63,8 +63,12 @@ def head_forward(q, k, v, prm, causal: bool):
             else:
                 e.append(prm.lut[nearest_slot(m - s, prm.idx_mul, prm.idx_shift, len(prm.lut))])
         E = sum(e)
-        R = round_half_up(Fraction(255 << 23, E))  # R = floor(255*2^23/E + 1/2)
-        p = [round_half_up(Fraction(ej * R, 1 << 23)) for ej in e]
+        if getattr(prm, "prob_bits", 8) == 16:
+            R = round_half_up(Fraction(65535 << 16, E))  # R16 = floor(65535*2^16/E + 1/2)
+            p = [round_half_up(Fraction(ej * R, 1 << 16)) for ej in e]
+        else:
+            R = round_half_up(Fraction(255 << 23, E))  # R = floor(255*2^23/E + 1/2)
+            p = [round_half_up(Fraction(ej * R, 1 << 23)) for ej in e]
         row = []
         for d in range(D):
             a = 0

@@ -217,3 +217,107 @@ def test_grouped_kv_heads_refusals():
         O.forward(q, k, k, (0.05, 0.05, 0.05, 0.05), kv_heads=3)      # 3 does not divide 4
     with pytest.raises(O.OracleRangeError):
         O.forward(q, k, k, (0.05, 0.05, 0.05, 0.05), kv_heads=2)      # shape says 3
+
+
+# ---------------------------------------------------------------------------
+# uint16 probabilities (the dynamic-range variant)
+# ---------------------------------------------------------------------------
+def test_p16_uniform_rows_never_underflow():
+    """A uniform row of n keys (every e = 2^15, E = n 2^15): for every
+    admissible n (1..65535) the uint16 p is the rounding of 65535/n within
+    1/2 + 1/4, and never 0, where uint8 p is 0 for every n >= 513."""
+    n = np.arange(1, 65536, dtype=np.int64)
+    E = n << 15
+    p16 = O.normalise16(np.int64(1 << 15), O.reciprocal16(E))
+    p8 = O.normalise(np.int64(1 << 15), O.reciprocal(E))
+    assert (p16 >= 1).all()
+    assert (np.abs(p16 * n - 65535) <= n * 0.75).all()      # |p - 65535/n| <= 3/4, in integers
+    assert p16[0] == 65535 and p16[1] == 32768 and p16[65534] == 1
+    assert (p8[512:] == 0).all() and (p8[:512] >= 1).all()
+
+
+def test_p16_normalisation_bound_exact():
+    """|p - 65535 e / E| <= 1/2 + e / 2^17 with exact rationals, and e*R16 + 2^15 < 2^32."""
+    rng = np.random.default_rng(21)
+    E = rng.integers(1 << 15, 65535 << 15, 20000).astype(np.int64)
+    e = np.minimum(rng.integers(0, 1 << 15, 20000).astype(np.int64), E)
+    R = O.reciprocal16(E)
+    assert int((e * R + (1 << 15)).max()) < (1 << 32)
+    p = O.normalise16(e, R)
+    for ei, Ei, pi in list(zip(e.tolist(), E.tolist(), p.tolist()))[::7]:
+        assert abs(Fraction(pi) - Fraction(65535 * ei, Ei)) <= Fraction(1, 2) + Fraction(ei, 1 << 17)
+
+
+def test_p16_single_key_returns_v():
+    """One key: p = 65535, and with s_o = s_v the output is v for every int8 value."""
+    vals = np.arange(-127, 128, dtype=np.int8)
+    v1 = vals.reshape(1, 1, 1, 255)
+    rng = np.random.default_rng(22)
+    q1 = rng.integers(-127, 128, (1, 1, 3, 255)).astype(np.int8)
+    k1 = rng.integers(-127, 128, (1, 1, 1, 255)).astype(np.int8)
+    out, _, E, P = O.forward(q1, k1, v1, (0.05, 0.05, 0.01, 0.01), stats=True, prob_bits=16)
+    assert (P == 65535).all() and (E == 1 << 15).all()
+    assert (out[0, 0] == vals[None, :]).all()
+
+
+@pytest.mark.parametrize("Sq,Skv,D,causal,seed,scales", TWIN)
+def test_p16_twin_agrees_on_tiny_shapes(Sq, Skv, D, causal, seed, scales):
+    rng = np.random.default_rng(seed + 50)
+    q = rng.integers(-127, 128, (1, 1, Sq, D)).astype(np.int8)
+    k = rng.integers(-127, 128, (1, 1, Skv, D)).astype(np.int8)
+    v = rng.integers(-127, 128, (1, 1, Skv, D)).astype(np.int8)
+    prm = O.derive_params(D, *scales, O.DEFAULT_CLIP, 32, 16)
+    out, m, E, P = O.forward(q, k, v, scales, O.DEFAULT_CLIP, causal, stats=True, prob_bits=16)
+    tout, tm, tE, tP = T.head_forward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), prm, causal)
+    assert out[0, 0].tolist() == tout and E[0, 0].tolist() == tE and P[0, 0].tolist() == tP
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,D,causal,seed,kind", CASES)
+def test_p16_against_float64_softmax(B, H, Sq, Skv, D, causal, seed, kind):
+    """|p/65535 - p_ref| <= tanh(beta/2) + tau_row + (1/2 + 1/4)/65535 per row."""
+    w = W.make_random(B, H, Sq, Skv, D, causal, seed, kind)
+    prm = O.derive_params(D, *w.scales, w.clip, 32, 16)
+    _, m, _, P = O.forward(w.q, w.k, w.v, w.scales, w.clip, causal, stats=True, prob_bits=16)
+    tb = math.tanh(_beta(prm) / 2)
+    for b in range(B):
+        for h in range(H):
+            pref = _ref_softmax(w.q[b, h], w.k[b, h], prm.alpha, causal)
+            S = w.q[b, h].astype(np.int64) @ w.k[b, h].astype(np.int64).T
+            allow = O.allowed_mask(Sq, Skv, causal)
+            clipped = allow & (m[b, h][:, None] - S >= prm.x_clip)
+            tau = np.where(clipped, pref, 0.0).sum(axis=1)
+            dp = np.abs(P[b, h] / 65535.0 - pref).max(axis=1)
+            assert (dp <= tb + tau + 0.75 / 65535 + 1e-12).all()
+
+
+def test_p16_cures_long_flat_row_underflow():
+    """A decode-like row of 8192 keys from N(0,1) data: with uint8 P most
+    kept keys round to 0 and the output collapses towards 0; with uint16 P
+    the output tracks float64 attention (mean error at least 4x smaller)."""
+    w = W.make_random(1, 2, 1, 8192, 128, False, 23, "normal")
+    sv = w.scales[2]
+    so8 = w.scales[3]
+    out8, _, _, P8 = O.forward(w.q, w.k, w.v, w.scales, w.clip, False, stats=True)
+    out16, _, _, P16 = O.forward(w.q, w.k, w.v, w.scales, w.clip, False, stats=True, prob_bits=16)
+    prm = O.derive_params(128, *w.scales, w.clip)
+    errs = []
+    for out in (out8, out16):
+        e = 0.0
+        for h in range(2):
+            pref = _ref_softmax(w.q[0, h], w.k[0, h], prm.alpha, False)
+            Oref = (pref @ w.v[0, h].astype(np.float64)) * sv / so8
+            e += np.abs(out[0, h].astype(np.float64) - Oref).mean()
+        errs.append(e)
+    assert (P8 > 0).mean() < (P16 > 0).mean()
+    assert errs[1] * 4 < errs[0]
+
+
+def test_prob_bits_refused_outside_8_and_16():
+    for bad in (0, 4, 12, 32):
+        with pytest.raises(O.OracleRangeError):
+            O.derive_params(64, 0.05, 0.05, 0.05, 0.05, O.DEFAULT_CLIP, 32, bad)
+    p8 = O.derive_params(64, 0.05, 0.05, 0.05, 0.05, O.DEFAULT_CLIP, 32, 8)
+    p16 = O.derive_params(64, 0.05, 0.05, 0.05, 0.05, O.DEFAULT_CLIP, 32, 16)
+    # the output multiplier carries the probability scale: mu_o(16) = mu_o(8) * 255 / 65535
+    assert abs(p16.mu_o * 65535 - p8.mu_o * 255) <= 1e-15 * p8.mu_o * 255
+    assert (p16.idx_mul, p16.x_clip, p16.lut) == (p8.idx_mul, p8.x_clip, p8.lut)
