@@ -318,8 +318,9 @@ def _time_calls(fn, stream, n, warm_s=0.3):
 
 def variants(steps=None):
     """The variants beside the 32-entry MHA path: finer exp tables (64, 128
-    entries) on the BERT and causal-prefill workloads (int8 TOPS and MFMA
-    fraction), grouped K/V heads on the batched decode shape (HBM GB/s of
+    entries) and uint16 probabilities on the BERT and causal-prefill workloads
+    (int8 TOPS and MFMA fraction; uint16 also on the decode shape), grouped
+    K/V heads on the batched decode shape (HBM GB/s of
     Q + K + V + O with K/V read once per K/V head), and the decode-step cache
     update (HBM GB/s of 4 bytes read and 1 written per value). One JSON line."""
     import torch
@@ -349,6 +350,12 @@ def variants(steps=None):
             tops = ops / (us * 1e-6) / 1e12
             row[str(n)] = {"us_per_call": us, "int8_TOPS": tops, "mfma_frac": tops / PEAK_INT8_TOPS}
         res["fine_tables"][cfg] = row
+        # uint16 probabilities (32-entry table): the long-row kernel for every Sq > 1 shape
+        fn = lambda: ia.forward_ex(q, k, v, w.scales, w.clip, w.causal, 32, out=out, prob_bits=16)
+        us = _time_calls(fn, stream, steps or (200 if cfg == "bert" else 30))
+        tops = ops / (us * 1e-6) / 1e12
+        res.setdefault("uint16_probabilities", {})[cfg] = {"us_per_call": us, "int8_TOPS": tops,
+                                                          "mfma_frac": tops / PEAK_INT8_TOPS}
 
     # grouped K/V heads on the decode shape: B=16, H=32, Skv=8192, d=128
     B, H, Skv, D = 16, 32, 8192, 128
@@ -369,6 +376,12 @@ def variants(steps=None):
         gbs = nbytes / (us * 1e-6) / 1e9
         res["grouped_decode"][f"Hkv={hkv}"] = {"us_per_call": us, "bytes": nbytes, "GBs": gbs,
                                                "hbm_frac": gbs / PEAK_HBM_GBS}
+        if hkv == 32:
+            fn16 = lambda: ia.forward_ex(q, k, v, scales, W.DEFAULT_CLIP, False, 32, out=out, prob_bits=16)
+            us16 = _time_calls(fn16, stream, steps or 100)
+            gbs16 = nbytes / (us16 * 1e-6) / 1e9
+            res.setdefault("uint16_probabilities", {})["decode"] = {"us_per_call": us16, "GBs": gbs16,
+                                                                    "hbm_frac": gbs16 / PEAK_HBM_GBS}
         del k, v
     torch.cuda.empty_cache()
 

@@ -134,13 +134,21 @@ int intattn_forward_debug(const int8_t* q, const int8_t* k, const int8_t* v, int
  * attention; the pages do not describe this step): k and v hold kv_heads
  * heads, [B, kv_heads, Skv, D], and query head h reads K/V head
  * h / (H / kv_heads); kv_heads must divide H (kv_heads = H is ordinary
- * multi-head attention). */
+ * multi-head attention).
+ * uint16 probabilities: the same section warns of underflow on skewed score
+ * distributions; a uint8 row of 513 or more uniform keys is all zeros. With
+ * prob_bits = 16: R16 = (65535*2^16 + E/2) / E, p = (lut[idx]*R16 + 2^15)
+ * >> 16 (uint16, target row sum 65535), and mu_o = s_v/(65535*s_o); the
+ * long-row and decode kernels run it (P.V as two int8 products, high and
+ * low probability bytes). */
 typedef struct intattn_variant {
     int32_t lut_size;    /* exp-table entries: 32, 64 or 128; 0 means 32     */
     int32_t kv_heads;    /* K/V heads; 0 means H                             */
     int32_t kv_capacity; /* rows per K/V head in memory, >= Skv (a K/V cache
                             of that capacity whose first Skv rows are
                             attended); 0 means Skv                           */
+    int32_t prob_bits;   /* probability width: 8 (uint8, the specification
+                            above) or 16 (uint16 variant); 0 means 8         */
 } intattn_variant;
 
 typedef struct intattn_params_ex {
@@ -152,16 +160,20 @@ typedef struct intattn_params_ex {
     int32_t  x_clip;    /* smallest m - s that lands in slot lut_size-1      */
     int32_t  req_shift; /* sh_o, 1 .. 63                                     */
     int64_t  req_mul;   /* M_o                                               */
+    int32_t  prob_bits; /* 8 or 16                                           */
 } intattn_params_ex;
 
 /* The lut_size-entry exp table (lut_out holds lut_size entries). Host only,
  * pure. Errors: E_NULL, E_CLIP, E_RANGE (lut_size not 32, 64 or 128). */
 int intattn_build_lut_ex(float clip, int32_t lut_size, uint16_t* lut_out);
 
-/* intattn_derive_params for a lut_size-entry table. Host only, pure.
- * Errors: E_NULL, E_SHAPE, E_SCALE, E_CLIP, E_RANGE (also lut_size). */
+/* intattn_derive_params for a lut_size-entry table and prob_bits-wide
+ * probabilities (8 or 16; 16 changes only M_o, sh_o). Host only, pure.
+ * Errors: E_NULL, E_SHAPE, E_SCALE, E_CLIP, E_RANGE (also lut_size,
+ * prob_bits). */
 int intattn_derive_params_ex(const intattn_shape* shape, const intattn_scales* scales,
-                             float clip, int32_t lut_size, intattn_params_ex* out);
+                             float clip, int32_t lut_size, int32_t prob_bits,
+                             intattn_params_ex* out);
 
 /* intattn_forward with a variant (NULL: lut_size 32, kv_heads H, no cache
  * padding). q and out are [B, H, Sq, D]; k and v are [B, kv_heads,

@@ -27,7 +27,7 @@ constexpr int kDecodeMaxKeys = 16384;
 constexpr int kDecodeThreads = 256;
 
 
-template <int D>
+template <int D, bool P16>
 __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, const int8_t* __restrict__ v,
     int8_t* __restrict__ out, const IaKernelParams P, int skv_pad, int32_t* __restrict__ row_max,
@@ -37,10 +37,10 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
     constexpr int KEYS_IT = 4 * GPW * (kDecodeThreads / 64);   // keys per iteration
     extern __shared__ __attribute__((aligned(16))) int32_t dsm[];
     int32_t* s_score = dsm;                                     // skv_pad ints (scores, then slots)
-    uint8_t* s_p = reinterpret_cast<uint8_t*>(dsm + skv_pad);   // skv_pad bytes
+    uint8_t* s_p = reinterpret_cast<uint8_t*>(dsm + skv_pad);   // skv_pad bytes (uint16 P: 2 per key)
     __shared__ uint16_t s_lut[kIaMaxLut];     // exp table (N <= 128 entries, rest 0)
-    __shared__ int32_t s_red[4][D];
-    __shared__ int32_t s_scal[8];
+    __shared__ int32_t s_red[P16 ? 2 : 1][4][D];
+    __shared__ int32_t s_scal[12];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -112,33 +112,53 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
     __syncthreads();
     E = static_cast<uint32_t>(s_scal[4]) + static_cast<uint32_t>(s_scal[5]) +
         static_cast<uint32_t>(s_scal[6]) + static_cast<uint32_t>(s_scal[7]);
-    const uint32_t R = ((255u << 23) + (E >> 1)) / E;
+    const uint32_t R = P16 ? reciprocal16(E) : ((255u << 23) + (E >> 1)) / E;
     if (row_max != nullptr && tid == 0) {
         row_max[head] = m;
         row_sum[head] = E;
     }
-    uint32_t psum = 0;
+    // psum: sum of p (uint16 P: of the high bytes; psum_lo of the low bytes)
+    uint32_t psum = 0, psum_lo = 0;
     for (int j = tid; j < skv_pad; j += kDecodeThreads) {
         uint32_t p = 0;
-        if (j < P.Skv) p = (s_lut[s_score[j]] * R + (1u << 22)) >> 23;
-        s_p[j] = static_cast<uint8_t>(p);
-        psum += p;
+        if constexpr (P16) {
+            if (j < P.Skv) p = (s_lut[s_score[j]] * R + (1u << 15)) >> 16;
+            reinterpret_cast<uint16_t*>(s_p)[j] = static_cast<uint16_t>(p);
+            psum += p >> 8;
+            psum_lo += p & 0xffu;
+        } else {
+            if (j < P.Skv) p = (s_lut[s_score[j]] * R + (1u << 22)) >> 23;
+            s_p[j] = static_cast<uint8_t>(p);
+            psum += p;
+        }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) psum += __shfl_xor(psum, off);
+    if constexpr (P16) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) psum_lo += __shfl_xor(psum_lo, off);
+    }
     __syncthreads();
-    if (lane == 0) s_scal[wave] = static_cast<int32_t>(psum);
+    if (lane == 0) {
+        s_scal[wave] = static_cast<int32_t>(psum);
+        s_scal[8 + wave] = static_cast<int32_t>(psum_lo);
+    }
     __syncthreads();
     psum = static_cast<uint32_t>(s_scal[0]) + static_cast<uint32_t>(s_scal[1]) +
            static_cast<uint32_t>(s_scal[2]) + static_cast<uint32_t>(s_scal[3]);
+    psum_lo = static_cast<uint32_t>(s_scal[8]) + static_cast<uint32_t>(s_scal[9]) +
+              static_cast<uint32_t>(s_scal[10]) + static_cast<uint32_t>(s_scal[11]);
 
     // ---- D: P.V ----------------------------------------------------------------
-    uint32_t acc[16];
+    // uint16 P: acc takes the high probability bytes, acc_lo the low ones
+    uint32_t acc[16], acc_lo[P16 ? 16 : 1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0;
+#pragma unroll
+    for (int i = 0; i < (P16 ? 16 : 1); ++i) acc_lo[i] = 0;
     for (int base = 0; base < P.Skv; base += 2 * KEYS_IT) {
         v4i vr[2][4];
-        uint32_t pk[2];
+        uint32_t pk[2], pk_lo[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int key0 = base + u * KEYS_IT + wave * 4 * GPW + 4 * g;
@@ -148,7 +168,15 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
                 if (key0 + i < P.Skv)
                     vr[u][i] = *reinterpret_cast<const v4i*>(vh + static_cast<size_t>(key0 + i) * D + 16 * c);
             }
-            pk[u] = key0 < skv_pad ? *reinterpret_cast<const uint32_t*>(s_p + key0) : 0u;
+            if constexpr (P16) {
+                // four uint16 p: high bytes into pk, low bytes into pk_lo (key order kept)
+                uint2 w = make_uint2(0u, 0u);
+                if (key0 < skv_pad) w = *reinterpret_cast<const uint2*>(s_p + 2 * key0);
+                pk[u] = __builtin_amdgcn_perm(w.y, w.x, 0x07050301u);
+                pk_lo[u] = __builtin_amdgcn_perm(w.y, w.x, 0x06040200u);
+            } else {
+                pk[u] = key0 < skv_pad ? *reinterpret_cast<const uint32_t*>(s_p + key0) : 0u;
+            }
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -162,10 +190,20 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
                 const uint32_t u1 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);
                 const uint32_t u2 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
                 const uint32_t u3 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
-                acc[4 * w + 0] = __builtin_amdgcn_udot4(__builtin_amdgcn_perm(u2, u0, 0x05040100u), pk[u], acc[4 * w + 0], false);
-                acc[4 * w + 1] = __builtin_amdgcn_udot4(__builtin_amdgcn_perm(u2, u0, 0x07060302u), pk[u], acc[4 * w + 1], false);
-                acc[4 * w + 2] = __builtin_amdgcn_udot4(__builtin_amdgcn_perm(u3, u1, 0x05040100u), pk[u], acc[4 * w + 2], false);
-                acc[4 * w + 3] = __builtin_amdgcn_udot4(__builtin_amdgcn_perm(u3, u1, 0x07060302u), pk[u], acc[4 * w + 3], false);
+                const uint32_t c0 = __builtin_amdgcn_perm(u2, u0, 0x05040100u);
+                const uint32_t c1 = __builtin_amdgcn_perm(u2, u0, 0x07060302u);
+                const uint32_t c2 = __builtin_amdgcn_perm(u3, u1, 0x05040100u);
+                const uint32_t c3 = __builtin_amdgcn_perm(u3, u1, 0x07060302u);
+                acc[4 * w + 0] = __builtin_amdgcn_udot4(c0, pk[u], acc[4 * w + 0], false);
+                acc[4 * w + 1] = __builtin_amdgcn_udot4(c1, pk[u], acc[4 * w + 1], false);
+                acc[4 * w + 2] = __builtin_amdgcn_udot4(c2, pk[u], acc[4 * w + 2], false);
+                acc[4 * w + 3] = __builtin_amdgcn_udot4(c3, pk[u], acc[4 * w + 3], false);
+                if constexpr (P16) {
+                    acc_lo[4 * w + 0] = __builtin_amdgcn_udot4(c0, pk_lo[u], acc_lo[4 * w + 0], false);
+                    acc_lo[4 * w + 1] = __builtin_amdgcn_udot4(c1, pk_lo[u], acc_lo[4 * w + 1], false);
+                    acc_lo[4 * w + 2] = __builtin_amdgcn_udot4(c2, pk_lo[u], acc_lo[4 * w + 2], false);
+                    acc_lo[4 * w + 3] = __builtin_amdgcn_udot4(c3, pk_lo[u], acc_lo[4 * w + 3], false);
+                }
             }
     }
     // lanes with the same column chunk (stride CPR) hold partial sums
@@ -174,15 +212,33 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
 #pragma unroll
         for (int off = CPR; off < 64; off <<= 1) acc[i] += __shfl_xor(acc[i], off);
     }
+    if constexpr (P16) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+#pragma unroll
+            for (int off = CPR; off < 64; off <<= 1) acc_lo[i] += __shfl_xor(acc_lo[i], off);
+        }
+    }
     if (g == 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s_red[wave][16 * c + i] = static_cast<int32_t>(acc[i]);
+        for (int i = 0; i < 16; ++i) s_red[0][wave][16 * c + i] = static_cast<int32_t>(acc[i]);
+        if constexpr (P16) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s_red[P16 ? 1 : 0][wave][16 * c + i] = static_cast<int32_t>(acc_lo[i]);
+        }
     }
     __syncthreads();
     for (int d = tid; d < D; d += kDecodeThreads) {
-        const uint32_t tot = static_cast<uint32_t>(s_red[0][d]) + static_cast<uint32_t>(s_red[1][d]) +
-                             static_cast<uint32_t>(s_red[2][d]) + static_cast<uint32_t>(s_red[3][d]);
-        out[head * D + d] = requantise(static_cast<int32_t>(tot - 128u * psum), P);
+        const uint32_t tot = static_cast<uint32_t>(s_red[0][0][d]) + static_cast<uint32_t>(s_red[0][1][d]) +
+                             static_cast<uint32_t>(s_red[0][2][d]) + static_cast<uint32_t>(s_red[0][3][d]);
+        // sum p v = sum p (v + 128) - 128 sum p; uint16 P: 256 (high bytes) + low bytes
+        uint32_t a = tot - 128u * psum;
+        if constexpr (P16) {
+            const uint32_t lo = static_cast<uint32_t>(s_red[P16 ? 1 : 0][0][d]) + static_cast<uint32_t>(s_red[P16 ? 1 : 0][1][d]) +
+                                static_cast<uint32_t>(s_red[P16 ? 1 : 0][2][d]) + static_cast<uint32_t>(s_red[P16 ? 1 : 0][3][d]);
+            a = 256u * a + (lo - 128u * psum_lo);
+        }
+        out[head * D + d] = requantise(static_cast<int32_t>(a), P);
     }
 }
 
@@ -192,36 +248,35 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
 
 int decode_max_keys() { return kDecodeMaxKeys; }
 
+template <int D, bool P16>
+int launch_decode_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, const IaKernelParams& kp,
+                    hipStream_t stream, unsigned blocks, int skv_pad, int32_t* row_max, uint32_t* row_sum) {
+    constexpr int kBytesPerKey = P16 ? 6 : 5;     // int32 score/slot + uint8 or uint16 p
+    static bool attr = false;
+    if (!attr) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_decode_kernel<D, P16>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kBytesPerKey * kDecodeMaxKeys) != hipSuccess)
+            return INTATTN_E_HIP;
+        attr = true;
+    }
+    const size_t shm = static_cast<size_t>(skv_pad) * kBytesPerKey;
+    hipLaunchKernelGGL((ia_decode_kernel<D, P16>), dim3(blocks), dim3(kDecodeThreads), shm, stream, q, k, v, out,
+                       kp, skv_pad, row_max, row_sum);
+    return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
+}
+
 int launch_decode(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
                   const IaKernelParams& kp, void* stream_v, int32_t* row_max, uint32_t* row_sum) {
     const hipStream_t stream = static_cast<hipStream_t>(stream_v);
     const long long blocks = static_cast<long long>(kp.B) * kp.H;
     if (blocks > INT_MAX) return INTATTN_E_SHAPE;
     const int skv_pad = (kp.Skv + 255) / 256 * 256;
-    const size_t shm = static_cast<size_t>(skv_pad) * 5;
-    if (D == 64) {
-        static bool attr64 = false;
-        if (!attr64) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_decode_kernel<64>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, 5 * kDecodeMaxKeys) != hipSuccess)
-                return INTATTN_E_HIP;
-            attr64 = true;
-        }
-        hipLaunchKernelGGL((ia_decode_kernel<64>), dim3(static_cast<unsigned>(blocks)), dim3(kDecodeThreads), shm,
-                           stream, q, k, v, out, kp, skv_pad, row_max, row_sum);
-    } else {
-        static bool attr128 = false;
-        if (!attr128) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_decode_kernel<128>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, 5 * kDecodeMaxKeys) != hipSuccess)
-                return INTATTN_E_HIP;
-            attr128 = true;
-        }
-        hipLaunchKernelGGL((ia_decode_kernel<128>), dim3(static_cast<unsigned>(blocks)), dim3(kDecodeThreads), shm,
-                           stream, q, k, v, out, kp, skv_pad, row_max, row_sum);
-    }
-    return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
+    const unsigned nb = static_cast<unsigned>(blocks);
+    if (kp.prob_bits == 16)
+        return D == 64 ? launch_decode_t<64, true>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum)
+                       : launch_decode_t<128, true>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum);
+    return D == 64 ? launch_decode_t<64, false>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum)
+                   : launch_decode_t<128, false>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum);
 }
-
 
 }  // namespace ia

@@ -372,4 +372,24 @@ __device__ __forceinline__ uint32_t pack_top_bytes(uint32_t w0, uint32_t w1, uin
     return lo | hi;
 }
 
+// uint16 probabilities: the word e * R16 + 2^15 + 2^31 holds p in bits
+// 16..31 with the top bit flipped (e * R16 + 2^15 < 2^32, so adding 2^31
+// flips bit 31 alone): byte 3 is (p >> 8) ^ 0x80, byte 2 is p & 0xff.
+__device__ __forceinline__ uint32_t prob16_word(uint32_t e, uint32_t R16) { return __umul24(e, R16) + 0x80008000u; }
+
+// Bytes 3 and 2 of four words: hi = their bytes 3, lo = their bytes 2 (in
+// word order), four v_perm.
+__device__ __forceinline__ void pack_bytes_32(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, uint32_t& hi,
+                                              uint32_t& lo) {
+    const uint32_t a = __builtin_amdgcn_perm(w1, w0, 0x07030602u);   // w0.b2 w1.b2 w0.b3 w1.b3
+    const uint32_t b = __builtin_amdgcn_perm(w3, w2, 0x07030602u);   // w2.b2 w3.b2 w2.b3 w3.b3
+    lo = __builtin_amdgcn_perm(b, a, 0x05040100u);
+    hi = __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// R16 = floor((65535 * 2^16 + floor(E/2)) / E) (below 2^17 for E >= 2^15).
+__device__ __forceinline__ uint32_t reciprocal16(uint32_t E) {
+    return static_cast<uint32_t>((0xFFFF0000ull + (E >> 1)) / E);
+}
+
 }  // namespace ia

@@ -62,7 +62,7 @@ struct LongLds {
     int8_t v[kStages][TB];
 };
 
-template <int D, int KM>
+template <int D, int KM, bool P16>
 __global__ __launch_bounds__(256) void ia_long_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, const int8_t* __restrict__ v,
     int8_t* __restrict__ out, const IaKernelParams P, int nqb, int32_t* __restrict__ row_max,
@@ -251,17 +251,21 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
         }
     });
     E += __shfl_xor(E, 32);
-    const uint32_t R = ((255u << 23) + (E >> 1)) / E;
-    const uint32_t R2 = 2 * R;                       // < 2^17
+    // uint8 P: R2 = 2R < 2^17; uint16 P: R16 < 2^17 (both 24-bit operands)
+    const uint32_t R2 = P16 ? reciprocal16(E) : 2 * (((255u << 23) + (E >> 1)) / E);
     if (row_max != nullptr && hh == 0 && qrow < P.Sq) {
         row_max[head * P.Sq + qrow] = mrow;
         row_sum[head * P.Sq + qrow] = E;
     }
 
     // ---- pass 3: P from the table, P.V on the MFMA --------------------------
+    // uint16 P: o holds the high probability bytes' product, o16 the low ones'
     v16i o[DB];
+    v16i o16[P16 ? DB : 1];
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = v16i{};
+#pragma unroll
+    for (int db = 0; db < (P16 ? DB : 1); ++db) o16[db] = v16i{};
     int32_t cs[DB];                          // this lane's part of the column sums
 #pragma unroll
     for (int db = 0; db < DB; ++db) cs[db] = 0;
@@ -269,6 +273,14 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     auto pack = [&](const v16i& s, int w4) -> int {
         return static_cast<int>(pack_top_bytes(pword(s[4 * w4]), pword(s[4 * w4 + 1]), pword(s[4 * w4 + 2]),
                                                pword(s[4 * w4 + 3])));
+    };
+    // uint16 P: signed operands (p >> 8) - 128 and (p & 0xff) - 128 of four keys
+    auto pack16 = [&](const v16i& s, int w4, int& hi, int& lo) {
+        auto pw = [&](int32_t y) -> uint32_t { return prob16_word(table_entry(y), R2); };
+        uint32_t h, l;
+        pack_bytes_32(pw(s[4 * w4]), pw(s[4 * w4 + 1]), pw(s[4 * w4 + 2]), pw(s[4 * w4 + 3]), h, l);
+        hi = static_cast<int>(h);
+        lo = static_cast<int>(l ^ 0x80808080u);
     };
     run_tiles(true, [&](int t, int st) {
         const bool colsum_turn = (t % kLongWaves) == wave;
@@ -279,11 +291,26 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
             constexpr int kb = decltype(kbc)::value;
             v16i s = scores(st, kb, cinit);
             mask(s, t * kLongTile + 32 * kb, kMasked);
-            const v4i pa = v4i{pack(s, 0), pack(s, 1), pack(s, 2), pack(s, 3)};
+            v4i pa, pl;
+            if constexpr (P16) {
+#pragma unroll
+                for (int w4 = 0; w4 < 4; ++w4) {
+                    int h, l;
+                    pack16(s, w4, h, l);
+                    pa[w4] = h;
+                    pl[w4] = l;
+                }
+            } else {
+                pa = v4i{pack(s, 0), pack(s, 1), pack(s, 2), pack(s, 3)};
+            }
             v4i vb[DB];
             tr8_operands<DB, kb * 32 * D>(va, vb);
 #pragma unroll
             for (int db = 0; db < DB; ++db) o[db] = mfma_i8_32x32x32(pa, vb[db], o[db]);
+            if constexpr (P16) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db) o16[db] = mfma_i8_32x32x32(pl, vb[db], o16[db]);
+            }
             if (colsum_turn) {
                 // one wave per tile; the asm keeps the sums from being
                 // computed on every wave and selected afterwards
@@ -334,23 +361,28 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
         const int32_t c128 = 128 * (lds.colsum[0][d] + lds.colsum[1][d] + lds.colsum[2][d] + lds.colsum[3][d]);
         v16i acc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = o[db][r] + c128;
+        for (int r = 0; r < 16; ++r) {
+            // uint16 P: sum p v = 256 (sum hi v) + sum lo v, each byte sum
+            // corrected by its own 128 * colsum (|.| < 2^24)
+            if constexpr (P16) acc[r] = 256 * (o[db][r] + c128) + (o16[db][r] + c128);
+            else acc[r] = o[db][r] + c128;
+        }
         store_rows(acc, obase + d);
     }
 }
 
-template <int D, int KM>
+template <int D, int KM, bool P16>
 int launch_long_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, const IaKernelParams& kp,
                   hipStream_t s, int nqb, unsigned blocks, int32_t* row_max, uint32_t* row_sum) {
     static bool attr_set = false;
     const size_t shm = sizeof(LongLds<D>);
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_long_kernel<D, KM>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_long_kernel<D, KM, P16>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)) != hipSuccess)
             return INTATTN_E_HIP;
         attr_set = true;
     }
-    hipLaunchKernelGGL((ia_long_kernel<D, KM>), dim3(blocks), dim3(256), shm, s, q, k, v, out, kp, nqb,
+    hipLaunchKernelGGL((ia_long_kernel<D, KM, P16>), dim3(blocks), dim3(256), shm, s, q, k, v, out, kp, nqb,
                        row_max, row_sum);
     return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
 }
@@ -364,14 +396,17 @@ int launch_long(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, 
     if (blocks > INT_MAX) return INTATTN_E_SHAPE;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const unsigned nb = static_cast<unsigned>(blocks);
-    if (D == 64) {
-        if (kp.slot_k == 4) return launch_long_t<64, 4>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
-        if (kp.slot_k == 2) return launch_long_t<64, 2>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
-        return launch_long_t<64, 1>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
-    }
-    if (kp.slot_k == 4) return launch_long_t<128, 4>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
-    if (kp.slot_k == 2) return launch_long_t<128, 2>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
-    return launch_long_t<128, 1>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
+    auto go = [&](auto d_c, auto p16_c) -> int {
+        constexpr int DD = decltype(d_c)::value;
+        constexpr bool PP = decltype(p16_c)::value;
+        if (kp.slot_k == 4) return launch_long_t<DD, 4, PP>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
+        if (kp.slot_k == 2) return launch_long_t<DD, 2, PP>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
+        return launch_long_t<DD, 1, PP>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
+    };
+    using D64 = std::integral_constant<int, 64>;
+    using D128 = std::integral_constant<int, 128>;
+    if (kp.prob_bits == 16) return D == 64 ? go(D64{}, std::true_type{}) : go(D128{}, std::true_type{});
+    return D == 64 ? go(D64{}, std::false_type{}) : go(D128{}, std::false_type{});
 }
 
 }  // namespace ia

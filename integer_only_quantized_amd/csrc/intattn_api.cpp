@@ -28,7 +28,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // lut_size: 32, 64 or 128; kv_heads: K/V heads (0: H), dividing H;
 // kv_capacity: rows per K/V head in memory (0: Skv), at least Skv.
 int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
-                         IaKernelParams* kp, int lut_size = 32, int kv_heads = 0, int kv_capacity = 0) {
+                         IaKernelParams* kp, int lut_size = 32, int kv_heads = 0, int kv_capacity = 0,
+                         int prob_bits = 8) {
     int st = intattn_validate_shape(shape, causal);
     if (st != INTATTN_OK) return st;
     if (shape->D != 64 && shape->D != 128) return INTATTN_E_DIM;
@@ -41,7 +42,8 @@ int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scale
     uint16_t lut[kIaMaxLut] = {};
     int32_t idx_mul = 0, x_clip = 0, req_shift = 0;
     int64_t req_mul = 0;
-    st = intattn_derive_core(shape, scales, clip, lut_size, lut, &idx_mul, &x_clip, &req_shift, &req_mul);
+    st = intattn_derive_core(shape, scales, clip, lut_size, lut, &idx_mul, &x_clip, &req_shift, &req_mul,
+                             prob_bits);
     if (st != INTATTN_OK) return st;
     kp->B = shape->B;
     kp->H = shape->H;
@@ -64,6 +66,7 @@ int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scale
     kp->slot_k_log2 = k == 4 ? 2 : k - 1;
     kp->kv_group = shape->H > 0 ? shape->H / hkv : 1;
     kp->kv_rows = rows;
+    kp->prob_bits = prob_bits;
     for (int i = 0; i < kIaMaxLut / 2; ++i)
         kp->lut2[i] = static_cast<uint32_t>(lut[2 * i]) | (static_cast<uint32_t>(lut[2 * i + 1]) << 16);
     return INTATTN_OK;
@@ -71,9 +74,10 @@ int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scale
 
 int prepare(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
             const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
-            IaKernelParams* kp, int lut_size = 32, int kv_heads = 0, int kv_capacity = 0) {
+            IaKernelParams* kp, int lut_size = 32, int kv_heads = 0, int kv_capacity = 0, int prob_bits = 8) {
     if (!q || !k || !v || !out || !shape || !scales) return INTATTN_E_NULL;
-    const int st = derive_kernel_params(shape, scales, clip, causal, kp, lut_size, kv_heads, kv_capacity);
+    const int st =
+        derive_kernel_params(shape, scales, clip, causal, kp, lut_size, kv_heads, kv_capacity, prob_bits);
     if (st != INTATTN_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return INTATTN_E_ALIGN;
     return INTATTN_OK;
@@ -85,7 +89,8 @@ int dispatch(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int
              const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum) {
     if (kp.Sq == 1 && kp.Skv <= ia::decode_max_keys())
         return ia::launch_decode(q, k, v, out, D, kp, stream, row_max, row_sum);
-    if (kp.Skv <= ia::short_max_keys(D))
+    // uint16 probabilities: the long-row kernel serves every other shape
+    if (kp.Skv <= ia::short_max_keys(D) && kp.prob_bits == 8)
         return ia::launch_short(q, k, v, out, D, kp, stream, row_max, row_sum);
     return ia::launch_long(q, k, v, out, D, kp, stream, row_max, row_sum);
 }
@@ -126,8 +131,10 @@ extern "C" int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t
     const int lut_size = variant && variant->lut_size != 0 ? variant->lut_size : 32;
     const int kv_heads = variant ? variant->kv_heads : 0;
     const int kv_capacity = variant ? variant->kv_capacity : 0;
+    const int prob_bits = variant && variant->prob_bits != 0 ? variant->prob_bits : 8;
     IaKernelParams kp;
-    const int st = prepare(q, k, v, out, shape, scales, clip, causal, &kp, lut_size, kv_heads, kv_capacity);
+    const int st =
+        prepare(q, k, v, out, shape, scales, clip, causal, &kp, lut_size, kv_heads, kv_capacity, prob_bits);
     if (st != INTATTN_OK) return st;
     if (rows_of(kp) == 0) return INTATTN_OK;
     ia::clear_pending_hip_error();
@@ -148,6 +155,7 @@ extern "C" int intattn_qk_scores(const int8_t* q, const int8_t* k, int32_t* scor
     kp.Skv = shape->Skv;
     kp.kv_group = 1;
     kp.kv_rows = shape->Skv;
+    kp.prob_bits = 8;
     if (rows_of(kp) == 0) return INTATTN_OK;
     ia::clear_pending_hip_error();
     return ia::launch_qk_scores(q, k, scores, shape->D, kp, stream);
@@ -185,6 +193,7 @@ extern "C" int intattn_fp_softmax(const int32_t* scores, uint8_t* probs, const i
     kp.causal = causal ? 1 : 0;
     kp.kv_group = 1;
     kp.kv_rows = shape->Skv;
+    kp.prob_bits = 8;
     if (kp.Skv > ia::stage_max_keys()) return INTATTN_E_SHAPE;
     if (rows_of(kp) == 0) return INTATTN_OK;
     // dequantisation factor of a score: s_q * s_k / sqrt(D), rounded once to float32

@@ -84,9 +84,11 @@ int intattn_validate_shape(const intattn_shape* s, int causal) {
 }
 
 int intattn_derive_core(const intattn_shape* shape, const intattn_scales* sc, float clip, int lut_size,
-                        uint16_t* lut, int32_t* idx_mul, int32_t* x_clip, int32_t* req_shift, int64_t* req_mul) {
+                        uint16_t* lut, int32_t* idx_mul, int32_t* x_clip, int32_t* req_shift, int64_t* req_mul,
+                        int prob_bits) {
     if (!shape || !sc || !lut || !idx_mul || !x_clip || !req_shift || !req_mul) return INTATTN_E_NULL;
     if (!valid_lut_size(lut_size)) return INTATTN_E_RANGE;
+    if (prob_bits != 8 && prob_bits != 16) return INTATTN_E_RANGE;
     if (shape->D < 1) return INTATTN_E_SHAPE;
     if (!finite_positive(sc->q) || !finite_positive(sc->k) || !finite_positive(sc->v) ||
         !finite_positive(sc->o))
@@ -106,7 +108,9 @@ int intattn_derive_core(const intattn_shape* shape, const intattn_scales* sc, fl
     // x*M >= (2n-3)*2^23  <=>  slot >= n-1
     const int64_t num = int64_t(2 * n - 3) << (kIdxShift - 1);
 
-    const double mu_o = static_cast<double>(sc->v) / (255.0 * static_cast<double>(sc->o));
+    // output multiplier: s_v / (P_one * s_o), P_one = 255 (uint8 P) or 65535
+    const double p_one = prob_bits == 16 ? 65535.0 : 255.0;
+    const double mu_o = static_cast<double>(sc->v) / (p_one * static_cast<double>(sc->o));
     int e_o = 0;
     const double m_o = std::frexp(mu_o, &e_o);
     int64_t Mo = static_cast<int64_t>(std::rint(std::ldexp(m_o, kReqFrac)));
@@ -138,13 +142,14 @@ extern "C" int intattn_derive_params(const intattn_shape* shape, const intattn_s
 }
 
 extern "C" int intattn_derive_params_ex(const intattn_shape* shape, const intattn_scales* sc, float clip,
-                                        int32_t lut_size, intattn_params_ex* out) {
+                                        int32_t lut_size, int32_t prob_bits, intattn_params_ex* out) {
     if (!shape || !sc || !out) return INTATTN_E_NULL;
     intattn_params_ex p{};
     const int st = intattn_derive_core(shape, sc, clip, lut_size, p.lut, &p.idx_mul, &p.x_clip, &p.req_shift,
-                                       &p.req_mul);
+                                       &p.req_mul, prob_bits);
     if (st != INTATTN_OK) return st;
     p.lut_size = lut_size;
+    p.prob_bits = prob_bits;
     p.idx_shift = kIdxShift;
     *out = p;
     return INTATTN_OK;

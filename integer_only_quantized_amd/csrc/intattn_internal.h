@@ -28,6 +28,7 @@ struct IaKernelParams {
     int32_t slot_k_log2; // log2(k)
     int32_t kv_group;    // query heads per K/V head (1: one K/V head each)
     int32_t kv_rows;     // rows per K/V head in memory (>= Skv: a cache of that capacity)
+    int32_t prob_bits;   // 8: uint8 probabilities; 16: the uint16 variant
     uint32_t lut2[kIaMaxLut / 2];   // exp table, entries 2i and 2i+1 packed lo/hi
 };
 
@@ -36,7 +37,8 @@ struct IaKernelParams {
 // requantisation pair. Errors as intattn_derive_params (E_RANGE also for an
 // unsupported lut_size).
 int intattn_derive_core(const intattn_shape* shape, const intattn_scales* sc, float clip, int lut_size,
-                        uint16_t* lut, int32_t* idx_mul, int32_t* x_clip, int32_t* req_shift, int64_t* req_mul);
+                        uint16_t* lut, int32_t* idx_mul, int32_t* x_clip, int32_t* req_shift, int64_t* req_mul,
+                        int prob_bits = 8);
 
 namespace ia {
 

@@ -100,6 +100,13 @@ def test_fine_params_equal_oracle_sweep(n):
                 assert ei.value.code == -6
                 continue
             got = B.derive_params_ex(D, (sq, sk, sv, so), clip, n)
+            ref16 = O.derive_params(D, sq, sk, sv, so, clip, n, 16) if n == 64 else None
+            if ref16 is not None:
+                try:
+                    g16 = B.derive_params_ex(D, (sq, sk, sv, so), clip, n, 16)
+                    assert (g16["req_mul"], g16["req_shift"]) == (ref16.req_mul, ref16.req_shift)
+                except B.IntAttnError as e:
+                    assert e.code == -6
             assert got["lut"] == list(ref.lut) and got["lut_size"] == n
             assert (got["idx_mul"], got["x_clip"]) == (ref.idx_mul, ref.x_clip)
             assert (got["req_mul"], got["req_shift"]) == (ref.req_mul, ref.req_shift)
@@ -113,8 +120,8 @@ def test_variant_validation_before_any_device_call():
     sc = B.Scales(0.05, 0.05, 0.05, 0.05)
     rm = ctypes.c_void_p(0x5000)
 
-    def call(lut_size, kv_heads, row_max=None, row_sum=None):
-        var = B.Variant(lut_size, kv_heads)
+    def call(lut_size, kv_heads, row_max=None, row_sum=None, prob_bits=0):
+        var = B.Variant(lut_size, kv_heads, 0, prob_bits)
         return B._lib.intattn_forward_ex(0x1000, 0x2000, 0x3000, 0x4000, ctypes.byref(sh), ctypes.byref(sc),
                                          O.DEFAULT_CLIP, 0, ctypes.byref(var), None, row_max, row_sum)
     for bad in (16, 33, 96, 256, -32):
@@ -122,12 +129,16 @@ def test_variant_validation_before_any_device_call():
     for bad in (3, 5, 8, -1):
         assert call(32, bad) == E["INTATTN_E_SHAPE"]
     assert call(64, 2, row_max=rm) == E["INTATTN_E_NULL"]
+    for bad in (4, 12, 32, -8):
+        assert call(32, 0, prob_bits=bad) == E["INTATTN_E_RANGE"]
     assert B._lib.intattn_build_lut_ex(O.DEFAULT_CLIP, 48, None) == E["INTATTN_E_NULL"]
     buf = (ctypes.c_uint16 * 128)()
     assert B._lib.intattn_build_lut_ex(O.DEFAULT_CLIP, 48, buf) == E["INTATTN_E_RANGE"]
     # a 128-entry table raises mu fourfold over 32 entries: scales that fit 32 entries may not fit 128
     assert B._lib.intattn_derive_params_ex(ctypes.byref(B.Shape(1, 1, 1, 1, 128)), ctypes.byref(B.Scales(0.8, 0.64, 0.4, 0.05)),
-                                           O.DEFAULT_CLIP, 128, ctypes.byref(B.ParamsEx())) == E["INTATTN_E_RANGE"]
+                                           O.DEFAULT_CLIP, 128, 8, ctypes.byref(B.ParamsEx())) == E["INTATTN_E_RANGE"]
+    assert B._lib.intattn_derive_params_ex(ctypes.byref(B.Shape(1, 1, 1, 1, 64)), ctypes.byref(B.Scales(0.05, 0.05, 0.05, 0.05)),
+                                           O.DEFAULT_CLIP, 32, 12, ctypes.byref(B.ParamsEx())) == E["INTATTN_E_RANGE"]
 
 
 def test_kv_append_validation_before_any_device_call():

@@ -1,5 +1,6 @@
 """GPU parity of the variants through intattn_forward_ex: finer exp tables (64
-and 128 entries) and grouped K/V heads (grouped-query / multi-query).
+and 128 entries), grouped K/V heads (grouped-query / multi-query) and uint16
+probabilities.
 
 Bar: bit-exact against the oracle (out, row max, row sum) on every kernel
 family: short rows (K/V of a head in LDS), long rows (tiled, three passes),
@@ -130,3 +131,44 @@ def test_bert_size_fine_table_sampled():
         _eq(f"bert128 out {b},{h}", out[b, h], ref)
         _eq(f"bert128 m {b},{h}", rm[b, h], m)
         _eq(f"bert128 E {b},{h}", rs[b, h], E)
+
+
+P16_CASES = [
+    # (B, H, Hkv, Sq, Skv, D, causal, lut, seed, kind): uint16 probabilities on
+    # the long-row kernel (every Sq > 1 shape) and the decode kernel (Sq = 1)
+    (2, 2, 2, 128, 128, 64, False, 32, 600, "normal"),
+    (1, 2, 2, 197, 197, 64, False, 64, 601, "channel_outliers"),
+    (1, 2, 2, 300, 1100, 128, True, 32, 602, "student_t_tail"),
+    (1, 4, 2, 257, 700, 64, True, 32, 603, "normal"),
+    (4, 8, 2, 1, 8192, 128, False, 32, 604, "normal"),
+    (2, 2, 2, 1, 3001, 64, False, 64, 605, "channel_outliers"),
+    (1, 2, 1, 1, 777, 128, True, 128, 606, "normal"),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,Sq,Skv,D,causal,lut,seed,kind", P16_CASES)
+def test_uint16_probabilities_bit_exact(B, H, Hkv, Sq, Skv, D, causal, lut, seed, kind):
+    w = W.make_random(B, H, Sq, Skv, D, causal, seed, kind, name="p16")
+    k = np.ascontiguousarray(w.k[:, :Hkv])
+    v = np.ascontiguousarray(w.v[:, :Hkv])
+    _say(f"case p16 q={w.q.shape} kv={k.shape} causal={causal} lut={lut}")
+    out, rm, rs = IA.forward_ex(_dev(w.q), _dev(k), _dev(v), w.scales, O.DEFAULT_CLIP, causal, lut, stats=True,
+                                prob_bits=16)
+    torch.cuda.synchronize()
+    ref, m, E, _ = O.forward(w.q, k, v, w.scales, O.DEFAULT_CLIP, causal, stats=True, lut_size=lut, kv_heads=Hkv,
+                             prob_bits=16)
+    _eq("p16 out", out.cpu().numpy(), ref)
+    _eq("p16 row_max", rm.cpu().numpy(), m)
+    _eq("p16 row_sum", rs.cpu().numpy().view(np.uint32), E)
+
+
+def test_uint16_probabilities_single_key_returns_v():
+    """One key (Skv = 1, the decode kernel): p = 65535 and, with s_o = s_v,
+    out = v exactly on the device as in the oracle."""
+    rng = np.random.default_rng(607)
+    q = rng.integers(-127, 128, (1, 2, 1, 128)).astype(np.int8)
+    k = rng.integers(-127, 128, (1, 2, 1, 128)).astype(np.int8)
+    v = np.tile(np.arange(-64, 64, dtype=np.int8), (1, 2, 1, 1))
+    out = IA.forward_ex(_dev(q), _dev(k), _dev(v), (0.02, 0.02, 0.01, 0.01), O.DEFAULT_CLIP, False, 32, prob_bits=16)
+    torch.cuda.synchronize()
+    _eq("single key", out.cpu().numpy(), v)
