@@ -322,41 +322,25 @@ __device__ __forceinline__ uint32_t tr8_lane_addr(int lane, int db, int rd) {
     return static_cast<uint32_t>(key * D + 16 * ((col >> 4) ^ v_swz<D>(key)) + (col & 15));
 }
 
-// All 2*DB transpose reads of one key block at LDS byte addresses va[i] + OFF,
-// waited for inside the same asm statement (its destination registers are
-// final when it ends); vb[db] is the B operand of column block db.
+// One ds_read_b64_tr_b8 at an LDS byte address (a compiler builtin, so the
+// compiler counts it and places the wait before the first use).
+__device__ __forceinline__ v2i tr8_read(uint32_t addr) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        reinterpret_cast<__attribute__((address_space(3))) v2i*>(static_cast<uintptr_t>(addr)));
+}
+
+// All 2*DB transpose reads of one key block at LDS byte addresses va[i] + OFF
+// (OFF folds into the instructions' offset field); vb[db] is the B operand of
+// column block db.
 template <int DB, int OFF>
 __device__ __forceinline__ void tr8_operands(const uint32_t (&va)[2 * DB], v4i (&vb)[DB]) {
-    v2i r[2 * DB];
-    if constexpr (DB == 4) {
-        asm volatile(
-            "ds_read_b64_tr_b8 %0, %8 offset:%16\n\t"
-            "ds_read_b64_tr_b8 %1, %9 offset:%16\n\t"
-            "ds_read_b64_tr_b8 %2, %10 offset:%16\n\t"
-            "ds_read_b64_tr_b8 %3, %11 offset:%16\n\t"
-            "ds_read_b64_tr_b8 %4, %12 offset:%16\n\t"
-            "ds_read_b64_tr_b8 %5, %13 offset:%16\n\t"
-            "ds_read_b64_tr_b8 %6, %14 offset:%16\n\t"
-            "ds_read_b64_tr_b8 %7, %15 offset:%16\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
-              "=&v"(r[7])
-            : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]),
-              "i"(OFF));
-    } else {
-        static_assert(DB == 2, "column blocks per head: 2 (d = 64) or 4 (d = 128)");
-        asm volatile(
-            "ds_read_b64_tr_b8 %0, %4 offset:%8\n\t"
-            "ds_read_b64_tr_b8 %1, %5 offset:%8\n\t"
-            "ds_read_b64_tr_b8 %2, %6 offset:%8\n\t"
-            "ds_read_b64_tr_b8 %3, %7 offset:%8\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-            : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "i"(OFF));
-    }
+    static_assert(DB == 2 || DB == 4, "column blocks per head: 2 (d = 64) or 4 (d = 128)");
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-        vb[db] = v4i{r[2 * db][0], r[2 * db][1], r[2 * db + 1][0], r[2 * db + 1][1]};
+    for (int db = 0; db < DB; ++db) {
+        const v2i r0 = tr8_read(va[2 * db] + OFF);
+        const v2i r1 = tr8_read(va[2 * db + 1] + OFF);
+        vb[db] = v4i{r0[0], r0[1], r1[0], r1[1]};
+    }
 }
 
 // Top byte of the probability word: for a table entry e <= E and R2 = 2R,
@@ -364,6 +348,34 @@ __device__ __forceinline__ void tr8_operands(const uint32_t (&va)[2 * DB], v4i (
 // p = (e * R + 2^22) >> 23, and adding 2^31 flips its top bit: the byte is
 // p ^ 0x80, i.e. p - 128 as int8.
 __device__ __forceinline__ uint32_t prob_word(uint32_t e, uint32_t R2) { return __umul24(e, R2) + 0x80800000u; }
+
+// P operand word (p - 128 as int8 for four keys) from two words that each
+// hold two table entries e (bits 0..15 and 16..31), for a row reciprocal
+// R < 2^16 (R <= 65280 since E >= 2^15). With x = e * R + 2^22 + 2^30
+// (< 2^32; v_mad_u32_u16, op_sel picking the entry's half), bits 23..30 of
+// x are p ^ 0x80 for p = (e * R + 2^22) >> 23: adding 2^30 adds 128 to
+// x >> 23 and leaves nothing below bit 23 changed. Each byte is shifted into
+// place by an SDWA byte write that keeps the other bytes, so one key costs
+// two VALU ops and no table read.
+__device__ __forceinline__ uint32_t prob_bytes4(uint32_t pw0, uint32_t pw1, uint32_t R) {
+    const uint32_t c = (1u << 22) + (1u << 30);
+    uint32_t x0, x1, x2, x3;
+    asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(x0) : "v"(pw0), "v"(R), "s"(c));
+    asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(x1) : "v"(pw0), "v"(R), "s"(c));
+    asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(x2) : "v"(pw1), "v"(R), "s"(c));
+    asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(x3) : "v"(pw1), "v"(R), "s"(c));
+    uint32_t d = x0 >> 23;             // byte 0 (bit 8 is overwritten below)
+    asm("v_lshrrev_b32_sdwa %0, 23, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(d) : "v"(x1));
+    asm("v_lshrrev_b32_sdwa %0, 23, %1 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(d) : "v"(x2));
+    asm("v_lshrrev_b32_sdwa %0, 23, %1 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(d) : "v"(x3));
+    return d;
+}
+
+// Two table entries (each < 2^16) in one word: a in bits 0..15, b above.
+__device__ __forceinline__ uint32_t entry_pair(uint32_t a, uint32_t b) { return a | (b << 16); }
 
 // Top bytes of four words packed into one (byte i from word i).
 __device__ __forceinline__ uint32_t pack_top_bytes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {

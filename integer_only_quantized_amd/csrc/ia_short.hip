@@ -16,13 +16,14 @@
 //   pass 1:  S^T blocks of the wave's half (K fragments from LDS, Q^T
 //            fragments in registers) -> row max; exchange with the other half;
 //   pass 2:  the MFMA accumulator starts from -m, so it yields y = s - m;
-//            slot word -> shared exp table -> row sum; the slot byte of every
-//            score (top byte of the slot word) is kept in registers; exchange
-//            the sums;
+//            slot word -> shared exp table -> row sum; the table entry of
+//            every score is kept in registers, two 16-bit entries a word;
+//            exchange the sums;
 //   V:       row-major V replaces K in LDS (global_load_lds again; chunks
 //            swizzled for the transpose reads);
-//   pass 3:  P bytes from the kept slot bytes: table entry e, then the top
-//            byte of e * 2R + 2^23 + 2^31 is p - 128 as int8 (P operand);
+//   pass 3:  P bytes from the kept entries, two VALU ops a key and no table
+//            read: bits 23..30 of e * R + 2^22 + 2^30 are p - 128 as int8,
+//            written into the P operand by SDWA byte writes;
 //            V operand by ds_read_b64_tr_b8; P.V on the MFMA; the column sums
 //            of the V rows fed come from the same operands (sdot4), and
 //            o + 128 * colsum = sum p v;
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     const int32_t negMs = -P.slot_k * P.idx_mul;
     const int32_t halfs = P.slot_k << 23;
     constexpr int32_t kMasked = -(1 << 23);   // y of a masked key: saturates to the last slot
-    uint32_t idxw[NBH][4];
+    uint32_t ew[NBH][8];                 // table entries of this wave's keys, two a word
     uint32_t E = 0;
     {
         v16i cinit;
@@ -298,7 +299,8 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
             v16i nxt = cinit;
             if (j + 1 < nvalid) nxt = scores(kb0 + j + 1, cinit);
             if (j >= nvalid) {
-                idxw[j][0] = idxw[j][1] = idxw[j][2] = idxw[j][3] = 0;   // never read
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ew[j][i] = 0;   // never read
                 if (j + 1 < NBH) cur = nxt;
                 __builtin_amdgcn_sched_barrier(0);
                 continue;
@@ -306,17 +308,12 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
             mask(cur, kb0 + j, kMasked);
             uint32_t e[16];
 #pragma unroll
-            for (int w4 = 0; w4 < 4; ++w4) {
-                uint32_t t[4];
+            for (int i = 0; i < 16; ++i) e[i] = lut_load<KM>(lut_byte_addr<KM>(slot_word_sat(cur[i], negMs, halfs)));
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    t[c] = slot_word_sat(cur[4 * w4 + c], negMs, halfs);
-                    e[4 * w4 + c] = lut_load<KM>(lut_byte_addr<KM>(t[c]));
-                }
-                // top bytes: k * slot + fraction bits (127 when saturated)
-                idxw[j][w4] = pack_top_bytes(t[0], t[1], t[2], t[3]);
-                // keep the packed word (not the four values it came from) live
-                asm volatile("" : "+v"(idxw[j][w4]));
+            for (int i = 0; i < 8; ++i) {
+                ew[j][i] = entry_pair(e[2 * i], e[2 * i + 1]);
+                // keep the pair word (not the two entries it came from) live
+                asm volatile("" : "+v"(ew[j][i]));
             }
 #pragma unroll
             for (int i = 0; i < 16; i += 4) E += (e[i] + e[i + 1]) + (e[i + 2] + e[i + 3]);
@@ -334,7 +331,6 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     // past Sq may have E = 0 and are never stored
     const uint32_t Ed = SKIP ? max(E, 1u) : E;
     const uint32_t R = ((255u << 23) + (Ed >> 1)) / Ed;
-    const uint32_t R2 = 2 * R;
     if (row_max != nullptr && half == 0 && hh == 0 && qrow < P.Sq) {
         row_max[head * P.Sq + qrow] = mrow;
         row_sum[head * P.Sq + qrow] = E;
@@ -348,19 +344,12 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
                                  tr8_lane_addr<D>(lane, db, rd);
     }
 
-    // ---- pass 3: P from the slot bytes, P.V on the MFMA -------------------
-    auto plookup = [&](int j, uint32_t (&pl)[16]) {
-#pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pl[4 * w4 + i] = lut_load<KM>(lut_byte_addr_of<KM>(idxw[j][w4], i));
-    };
-    auto ppack = [&](const uint32_t (&pl)[16]) {
+    // ---- pass 3: P from the kept table entries, P.V on the MFMA ------------
+    // P operand of block j: byte c of word w4 is key 4 w4 + c of the block
+    auto pbytes = [&](const uint32_t (&w)[8]) {
         v4i pa;
 #pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4)
-            pa[w4] = static_cast<int>(pack_top_bytes(prob_word(pl[4 * w4], R2), prob_word(pl[4 * w4 + 1], R2),
-                                                     prob_word(pl[4 * w4 + 2], R2), prob_word(pl[4 * w4 + 3], R2)));
+        for (int w4 = 0; w4 < 4; ++w4) pa[w4] = static_cast<int>(prob_bytes4(w[2 * w4], w[2 * w4 + 1], R));
         return pa;
     };
     v16i o[DB];
@@ -371,26 +360,19 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
         cs[db] = 0;
     }
     {
-        uint32_t pl[16];
         v4i pa = v4i{0, 0, 0, 0};
-        if (nvalid > 0) {
-            plookup(0, pl);
-            pa = ppack(pl);
-        }
-        if (nvalid > 1) plookup(1, pl);
+        if (nvalid > 0) pa = pbytes(ew[0]);
         static_for<NBH>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            v4i pnext = v4i{0, 0, 0, 0};
-            if constexpr (j + 1 < NBH) {
-                if (j + 1 < nvalid) pnext = ppack(pl);
-            }
-            if constexpr (j + 2 < NBH) {
-                if (j + 2 < nvalid) plookup(j + 2, pl);
-            }
             sync_block(j, false);
             if (j >= nvalid) return;
             v4i vb[DB];
             tr8_operands<DB, j * 32 * D>(vaddr, vb);
+            // the next block's P operand while the transpose reads land
+            v4i pnext = v4i{0, 0, 0, 0};
+            if constexpr (j + 1 < NBH) {
+                if (j + 1 < nvalid) pnext = pbytes(ew[j + 1]);
+            }
 #pragma unroll
             for (int db = 0; db < DB; ++db) o[db] = mfma_i8_32x32x32(pa, vb[db], o[db]);
             // column sums of the V rows fed: when both query groups feed the
