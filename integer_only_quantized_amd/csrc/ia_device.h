@@ -322,23 +322,27 @@ __device__ __forceinline__ uint32_t tr8_lane_addr(int lane, int db, int rd) {
     return static_cast<uint32_t>(key * D + 16 * ((col >> 4) ^ v_swz<D>(key)) + (col & 15));
 }
 
-// One ds_read_b64_tr_b8 at an LDS byte address (a compiler builtin, so the
-// compiler counts it and places the wait before the first use).
+// One ds_read_b64_tr_b8 at LDS byte address addr + OFF (a compiler builtin,
+// so the compiler counts it and places the wait before the first use; OFF is
+// applied to the LDS pointer, which lets it fold into the offset field).
+template <int OFF>
 __device__ __forceinline__ v2i tr8_read(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
+    typedef __attribute__((address_space(3))) char lds_char;
+    const lds_char* p = reinterpret_cast<const lds_char*>(static_cast<uintptr_t>(addr)) + OFF;
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-        reinterpret_cast<__attribute__((address_space(3))) v2i*>(static_cast<uintptr_t>(addr)));
+        reinterpret_cast<__attribute__((address_space(3))) v2i*>(const_cast<lds_char*>(p)));
 }
 
-// All 2*DB transpose reads of one key block at LDS byte addresses va[i] + OFF
-// (OFF folds into the instructions' offset field); vb[db] is the B operand of
-// column block db.
+// All 2*DB transpose reads of one key block at LDS byte addresses va[i] + OFF;
+// vb[db] is the B operand of column block db.
 template <int DB, int OFF>
 __device__ __forceinline__ void tr8_operands(const uint32_t (&va)[2 * DB], v4i (&vb)[DB]) {
     static_assert(DB == 2 || DB == 4, "column blocks per head: 2 (d = 64) or 4 (d = 128)");
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        const v2i r0 = tr8_read(va[2 * db] + OFF);
-        const v2i r1 = tr8_read(va[2 * db + 1] + OFF);
+        const v2i r0 = tr8_read<OFF>(va[2 * db]);
+        const v2i r1 = tr8_read<OFF>(va[2 * db + 1]);
         vb[db] = v4i{r0[0], r0[1], r1[0], r1[1]};
     }
 }
