@@ -21,6 +21,20 @@ namespace ia {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
+// Wait states around v_mfma_i32_32x32x32_i8 that the compiler inserts only
+// between instructions it emits itself (inline asm is opaque to its hazard
+// checks): a VALU read of the MFMA's result needs 12 (s_nop 11, what it emits
+// before a VALU consumer), and an MFMA reading a VGPR that a VALU op just
+// wrote needs 2. These asm statements carry the wait states and are tied to
+// the registers by their operands, so they sit after the producer and before
+// the consumer: mfma_result_guard where inline asm (the slot word) reads
+// fresh scores, mfma_source_guard where an asm-built P operand feeds P.V.
+__device__ __forceinline__ void mfma_result_guard(v16i& s) { asm volatile("s_nop 11" : "+v"(s)); }
+__device__ __forceinline__ void mfma_result_guard(v16i& s0, v16i& s1) {
+    asm volatile("s_nop 11" : "+v"(s0), "+v"(s1));
+}
+__device__ __forceinline__ void mfma_source_guard(v4i& a) { asm volatile("s_nop 1" : "+v"(a)); }
+
 // S^T tiles: v_mfma_i32_32x32x32_i8 with K as the A operand (rows = keys)
 // and Q^T as the B operand (columns = queries). Lane l (l32 = l % 32,
 // hh = l / 32) holds the 16 accumulator registers of column l32, i.e. scores

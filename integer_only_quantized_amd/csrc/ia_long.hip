@@ -239,6 +239,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     run_tiles(false, [&](int t, int st) {
         v16i s0 = scores(st, 0, cinit);
         v16i s1 = scores(st, 1, cinit);
+        mfma_result_guard(s0, s1);           // the slot word (inline asm) reads them
         mask(s0, t * kLongTile, kMasked);
         mask(s1, t * kLongTile + 32, kMasked);
 #pragma unroll
@@ -290,6 +291,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
         auto kblock = [&](auto kbc) {
             constexpr int kb = decltype(kbc)::value;
             v16i s = scores(st, kb, cinit);
+            mfma_result_guard(s);            // the slot word (inline asm) reads them
             mask(s, t * kLongTile + 32 * kb, kMasked);
             v4i pa, pl;
             if constexpr (P16) {

@@ -292,8 +292,14 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
         v16i cinit;
 #pragma unroll
         for (int r = 0; r < 16; ++r) cinit[r] = -mrow;
+        // the slot word (inline asm) reads each block's scores one block after
+        // its MFMAs, with a whole block of integer work in between, except
+        // for the first block, which is guarded
         v16i cur = cinit;
-        if (nvalid > 0) cur = scores(kb0, cinit);
+        if (nvalid > 0) {
+            cur = scores(kb0, cinit);
+            mfma_result_guard(cur);
+        }
 #pragma unroll
         for (int j = 0; j < NBH; ++j) {
             v16i nxt = cinit;
@@ -373,6 +379,7 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
             if constexpr (j + 1 < NBH) {
                 if (j + 1 < nvalid) pnext = pbytes(ew[j + 1]);
             }
+            mfma_source_guard(pa);               // built by inline asm
 #pragma unroll
             for (int db = 0; db < DB; ++db) o[db] = mfma_i8_32x32x32(pa, vb[db], o[db]);
             // column sums of the V rows fed: when both query groups feed the
