@@ -25,22 +25,29 @@ constexpr int kDecodeMaxKeys = 16384;
 //      then reduced and the result requantised.
 // HBM traffic is one read of K and V; the LDS holds 5 bytes per key.
 constexpr int kDecodeThreads = 256;
+// Key groups a lane loads before using any of them (its loads in flight).
+constexpr int kDecodeUnroll = 2;
 
 
-template <int D, bool P16>
-__global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
+template <int D, bool P16, int QH>
+__global__ __launch_bounds__(kDecodeThreads * QH) void ia_decode_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, const int8_t* __restrict__ v,
     int8_t* __restrict__ out, const IaKernelParams P, int skv_pad, int32_t* __restrict__ row_max,
     uint32_t* __restrict__ row_sum) {
+    static_assert(QH == 1 || (QH == 2 && !P16), "two query heads a workgroup with uint8 P only");
+    constexpr int NT = kDecodeThreads * QH;     // threads: 4 waves per query head
+    constexpr int NW = NT / 64;                 // waves
     constexpr int CPR = D / 16;                 // lanes per key row
     constexpr int GPW = 64 / CPR;               // key groups (of 4 keys) per wave
-    constexpr int KEYS_IT = 4 * GPW * (kDecodeThreads / 64);   // keys per iteration
+    constexpr int KEYS_IT = 4 * GPW * NW;       // keys per iteration
     extern __shared__ __attribute__((aligned(16))) int32_t dsm[];
-    int32_t* s_score = dsm;                                     // skv_pad ints (scores, then slots)
-    uint8_t* s_p = reinterpret_cast<uint8_t*>(dsm + skv_pad);   // skv_pad bytes (uint16 P: 2 per key)
+    // per query head h: skv_pad ints (scores, then slots) at dsm + h * skv_pad,
+    // then skv_pad bytes of P (uint16 P: 2 per key)
+    int32_t* const s_score = dsm;
+    uint8_t* const s_p = reinterpret_cast<uint8_t*>(dsm + QH * skv_pad);
     __shared__ uint16_t s_lut[kIaMaxLut];     // exp table (N <= 128 entries, rest 0)
-    __shared__ int32_t s_red[P16 ? 2 : 1][4][D];
-    __shared__ int32_t s_scal[12];
+    __shared__ int32_t s_red[P16 ? 2 : QH][NW][D];
+    __shared__ int32_t s_scal[QH][3 * NW];     // per wave: row max, row sum, sum of p (uint16 P: low bytes)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -48,21 +55,27 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
     const int c = lane % CPR;                   // 16-byte column chunk
     const int g = lane / CPR;                   // key group within the wave
     // grouped K/V heads: the query heads of one K/V head run on the same XCD
-    // (consecutive logical blocks), so its K and V stream once into that L2
-    const int bid = P.kv_group > 1 ? xcd_local_block(blockIdx.x, gridDim.x) : static_cast<int>(blockIdx.x);
-    const size_t head = static_cast<size_t>(bid);
-    const size_t kvhead = static_cast<size_t>(bid / P.kv_group);
+    // (consecutive logical blocks), so its K and V stream once into that L2;
+    // with QH = 2 a workgroup takes two query heads of one K/V head and reads
+    // each K and V chunk once for both
+    const int bid = P.kv_group > QH ? xcd_local_block(blockIdx.x, gridDim.x) : static_cast<int>(blockIdx.x);
+    const size_t head0 = static_cast<size_t>(bid) * QH;
+    const size_t kvhead = static_cast<size_t>(head0 / P.kv_group);
     const int8_t* kh = k + kvhead * P.kv_rows * D;
     const int8_t* vh = v + kvhead * P.kv_rows * D;
-    const v4i qv = *reinterpret_cast<const v4i*>(q + head * D + 16 * c);
+    v4i qv[QH];
+#pragma unroll
+    for (int h = 0; h < QH; ++h) qv[h] = *reinterpret_cast<const v4i*>(q + (head0 + h) * D + 16 * c);
     if (wave == 0) fill_lut_u16(P, s_lut, lane);
 
     // ---- A: scores ---------------------------------------------------------
-    int32_t tmax = INT_MIN;
-    for (int base = 0; base < P.Skv; base += 2 * KEYS_IT) {
-        v4i kr[2][4];
+    int32_t tmax[QH];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+    for (int h = 0; h < QH; ++h) tmax[h] = INT_MIN;
+    for (int base = 0; base < P.Skv; base += kDecodeUnroll * KEYS_IT) {
+        v4i kr[kDecodeUnroll][4];
+#pragma unroll
+        for (int u = 0; u < kDecodeUnroll; ++u)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = base + u * KEYS_IT + wave * 4 * GPW + 4 * g + i;
@@ -70,97 +83,140 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
                 if (key < P.Skv) kr[u][i] = *reinterpret_cast<const v4i*>(kh + static_cast<size_t>(key) * D + 16 * c);
             }
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < kDecodeUnroll; ++u)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                int32_t sc = __builtin_amdgcn_sdot4(kr[u][i][0], qv[0], 0, false);
-                sc = __builtin_amdgcn_sdot4(kr[u][i][1], qv[1], sc, false);
-                sc = __builtin_amdgcn_sdot4(kr[u][i][2], qv[2], sc, false);
-                sc = __builtin_amdgcn_sdot4(kr[u][i][3], qv[3], sc, false);
-                sc += dpp_xor1(sc);
-                sc += dpp_xor2(sc);
-                if (CPR == 8) sc += dpp_half_mirror(sc);
                 const int key = base + u * KEYS_IT + wave * 4 * GPW + 4 * g + i;
-                if (key < P.Skv) {
-                    tmax = max(tmax, sc);
-                    if (c == i) s_score[key] = sc;
+#pragma unroll
+                for (int h = 0; h < QH; ++h) {
+                    int32_t sc = __builtin_amdgcn_sdot4(kr[u][i][0], qv[h][0], 0, false);
+                    sc = __builtin_amdgcn_sdot4(kr[u][i][1], qv[h][1], sc, false);
+                    sc = __builtin_amdgcn_sdot4(kr[u][i][2], qv[h][2], sc, false);
+                    sc = __builtin_amdgcn_sdot4(kr[u][i][3], qv[h][3], sc, false);
+                    sc += dpp_xor1(sc);
+                    sc += dpp_xor2(sc);
+                    if (CPR == 8) sc += dpp_half_mirror(sc);
+                    if (key < P.Skv) {
+                        tmax[h] = max(tmax[h], sc);
+                        if (c == i) s_score[h * skv_pad + key] = sc;
+                    }
                 }
             }
     }
     // ---- B: row max ----------------------------------------------------------
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) tmax = max(tmax, __shfl_xor(tmax, off));
-    if (lane == 0) s_scal[wave] = tmax;
+    for (int h = 0; h < QH; ++h) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) tmax[h] = max(tmax[h], __shfl_xor(tmax[h], off));
+        if (lane == 0) s_scal[h][wave] = tmax[h];
+    }
     __syncthreads();
-    const int32_t m = max(max(s_scal[0], s_scal[1]), max(s_scal[2], s_scal[3]));
-    const int32_t lo = m - P.x_clip;
-    const uint32_t Cm = static_cast<uint32_t>(m) * static_cast<uint32_t>(P.idx_mul) + (1u << 23);
-    const int32_t negM = -P.idx_mul;
+    int32_t m[QH], lo[QH], negM = -P.idx_mul;
+    uint32_t Cm[QH];
+#pragma unroll
+    for (int h = 0; h < QH; ++h) {
+        m[h] = s_scal[h][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) m[h] = max(m[h], s_scal[h][w]);
+        lo[h] = m[h] - P.x_clip;
+        Cm[h] = static_cast<uint32_t>(m[h]) * static_cast<uint32_t>(P.idx_mul) + (1u << 23);
+    }
 
     // ---- C: slots and row sum, then probabilities ------------------------------
-    uint32_t E = 0;
-    for (int j = tid; j < P.Skv; j += kDecodeThreads) {
-        const int32_t sp = max(s_score[j], lo);
-        const uint32_t slot = (Cm + static_cast<uint32_t>(__mul24(sp, negM))) >> 24;
-        E += s_lut[slot];
-        s_score[j] = static_cast<int32_t>(slot);
-    }
+    uint32_t E[QH];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) E += __shfl_xor(E, off);
-    __syncthreads();
-    if (lane == 0) s_scal[4 + wave] = static_cast<int32_t>(E);
-    __syncthreads();
-    E = static_cast<uint32_t>(s_scal[4]) + static_cast<uint32_t>(s_scal[5]) +
-        static_cast<uint32_t>(s_scal[6]) + static_cast<uint32_t>(s_scal[7]);
-    const uint32_t R = P16 ? reciprocal16(E) : ((255u << 23) + (E >> 1)) / E;
-    if (row_max != nullptr && tid == 0) {
-        row_max[head] = m;
-        row_sum[head] = E;
-    }
-    // psum: sum of p (uint16 P: of the high bytes; psum_lo of the low bytes)
-    uint32_t psum = 0, psum_lo = 0;
-    for (int j = tid; j < skv_pad; j += kDecodeThreads) {
-        uint32_t p = 0;
-        if constexpr (P16) {
-            if (j < P.Skv) p = (s_lut[s_score[j]] * R + (1u << 15)) >> 16;
-            reinterpret_cast<uint16_t*>(s_p)[j] = static_cast<uint16_t>(p);
-            psum += p >> 8;
-            psum_lo += p & 0xffu;
-        } else {
-            if (j < P.Skv) p = (s_lut[s_score[j]] * R + (1u << 22)) >> 23;
-            s_p[j] = static_cast<uint8_t>(p);
-            psum += p;
+    for (int h = 0; h < QH; ++h) E[h] = 0;
+    for (int j = tid; j < P.Skv; j += NT) {
+#pragma unroll
+        for (int h = 0; h < QH; ++h) {
+            const int32_t sp = max(s_score[h * skv_pad + j], lo[h]);
+            const uint32_t slot = (Cm[h] + static_cast<uint32_t>(__mul24(sp, negM))) >> 24;
+            E[h] += s_lut[slot];
+            s_score[h * skv_pad + j] = static_cast<int32_t>(slot);
         }
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) psum += __shfl_xor(psum, off);
+    for (int h = 0; h < QH; ++h) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) E[h] += __shfl_xor(E[h], off);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < QH; ++h)
+        if (lane == 0) s_scal[h][NW + wave] = static_cast<int32_t>(E[h]);
+    __syncthreads();
+    uint32_t R[QH];
+#pragma unroll
+    for (int h = 0; h < QH; ++h) {
+        E[h] = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) E[h] += static_cast<uint32_t>(s_scal[h][NW + w]);
+        R[h] = P16 ? reciprocal16(E[h]) : ((255u << 23) + (E[h] >> 1)) / E[h];
+        if (row_max != nullptr && tid == 0) {
+            row_max[head0 + h] = m[h];
+            row_sum[head0 + h] = E[h];
+        }
+    }
+    // psum: sum of p (uint16 P: of the high bytes; psum_lo of the low bytes)
+    uint32_t psum[QH], psum_lo = 0;
+#pragma unroll
+    for (int h = 0; h < QH; ++h) psum[h] = 0;
+    for (int j = tid; j < skv_pad; j += NT) {
+#pragma unroll
+        for (int h = 0; h < QH; ++h) {
+            uint32_t p = 0;
+            if constexpr (P16) {
+                if (j < P.Skv) p = (s_lut[s_score[j]] * R[0] + (1u << 15)) >> 16;
+                reinterpret_cast<uint16_t*>(s_p)[j] = static_cast<uint16_t>(p);
+                psum[0] += p >> 8;
+                psum_lo += p & 0xffu;
+            } else {
+                if (j < P.Skv) p = (s_lut[s_score[h * skv_pad + j]] * R[h] + (1u << 22)) >> 23;
+                s_p[h * skv_pad + j] = static_cast<uint8_t>(p);
+                psum[h] += p;
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < QH; ++h) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) psum[h] += __shfl_xor(psum[h], off);
+    }
     if constexpr (P16) {
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) psum_lo += __shfl_xor(psum_lo, off);
     }
     __syncthreads();
     if (lane == 0) {
-        s_scal[wave] = static_cast<int32_t>(psum);
-        s_scal[8 + wave] = static_cast<int32_t>(psum_lo);
+#pragma unroll
+        for (int h = 0; h < QH; ++h) s_scal[h][wave] = static_cast<int32_t>(psum[h]);
+        s_scal[0][2 * NW + wave] = static_cast<int32_t>(psum_lo);
     }
     __syncthreads();
-    psum = static_cast<uint32_t>(s_scal[0]) + static_cast<uint32_t>(s_scal[1]) +
-           static_cast<uint32_t>(s_scal[2]) + static_cast<uint32_t>(s_scal[3]);
-    psum_lo = static_cast<uint32_t>(s_scal[8]) + static_cast<uint32_t>(s_scal[9]) +
-              static_cast<uint32_t>(s_scal[10]) + static_cast<uint32_t>(s_scal[11]);
+    psum_lo = 0;
+#pragma unroll
+    for (int h = 0; h < QH; ++h) {
+        psum[h] = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) psum[h] += static_cast<uint32_t>(s_scal[h][w]);
+    }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) psum_lo += static_cast<uint32_t>(s_scal[0][2 * NW + w]);
 
     // ---- D: P.V ----------------------------------------------------------------
     // uint16 P: acc takes the high probability bytes, acc_lo the low ones
-    uint32_t acc[16], acc_lo[P16 ? 16 : 1];
+    uint32_t acc[QH][16], acc_lo[P16 ? 16 : 1];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0;
+    for (int h = 0; h < QH; ++h)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[h][i] = 0;
 #pragma unroll
     for (int i = 0; i < (P16 ? 16 : 1); ++i) acc_lo[i] = 0;
-    for (int base = 0; base < P.Skv; base += 2 * KEYS_IT) {
-        v4i vr[2][4];
-        uint32_t pk[2], pk_lo[2];
+    for (int base = 0; base < P.Skv; base += kDecodeUnroll * KEYS_IT) {
+        v4i vr[kDecodeUnroll][4];
+        uint32_t pk[kDecodeUnroll][QH], pk_lo[kDecodeUnroll];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < kDecodeUnroll; ++u) {
             const int key0 = base + u * KEYS_IT + wave * 4 * GPW + 4 * g;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -172,14 +228,16 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
                 // four uint16 p: high bytes into pk, low bytes into pk_lo (key order kept)
                 uint2 w = make_uint2(0u, 0u);
                 if (key0 < skv_pad) w = *reinterpret_cast<const uint2*>(s_p + 2 * key0);
-                pk[u] = __builtin_amdgcn_perm(w.y, w.x, 0x07050301u);
+                pk[u][0] = __builtin_amdgcn_perm(w.y, w.x, 0x07050301u);
                 pk_lo[u] = __builtin_amdgcn_perm(w.y, w.x, 0x06040200u);
             } else {
-                pk[u] = key0 < skv_pad ? *reinterpret_cast<const uint32_t*>(s_p + key0) : 0u;
+#pragma unroll
+                for (int h = 0; h < QH; ++h)
+                    pk[u][h] = key0 < skv_pad ? *reinterpret_cast<const uint32_t*>(s_p + h * skv_pad + key0) : 0u;
             }
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < kDecodeUnroll; ++u)
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const uint32_t r0 = static_cast<uint32_t>(vr[u][0][w]) ^ 0x80808080u;
@@ -194,10 +252,13 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
                 const uint32_t c1 = __builtin_amdgcn_perm(u2, u0, 0x07060302u);
                 const uint32_t c2 = __builtin_amdgcn_perm(u3, u1, 0x05040100u);
                 const uint32_t c3 = __builtin_amdgcn_perm(u3, u1, 0x07060302u);
-                acc[4 * w + 0] = __builtin_amdgcn_udot4(c0, pk[u], acc[4 * w + 0], false);
-                acc[4 * w + 1] = __builtin_amdgcn_udot4(c1, pk[u], acc[4 * w + 1], false);
-                acc[4 * w + 2] = __builtin_amdgcn_udot4(c2, pk[u], acc[4 * w + 2], false);
-                acc[4 * w + 3] = __builtin_amdgcn_udot4(c3, pk[u], acc[4 * w + 3], false);
+#pragma unroll
+                for (int h = 0; h < QH; ++h) {
+                    acc[h][4 * w + 0] = __builtin_amdgcn_udot4(c0, pk[u][h], acc[h][4 * w + 0], false);
+                    acc[h][4 * w + 1] = __builtin_amdgcn_udot4(c1, pk[u][h], acc[h][4 * w + 1], false);
+                    acc[h][4 * w + 2] = __builtin_amdgcn_udot4(c2, pk[u][h], acc[h][4 * w + 2], false);
+                    acc[h][4 * w + 3] = __builtin_amdgcn_udot4(c3, pk[u][h], acc[h][4 * w + 3], false);
+                }
                 if constexpr (P16) {
                     acc_lo[4 * w + 0] = __builtin_amdgcn_udot4(c0, pk_lo[u], acc_lo[4 * w + 0], false);
                     acc_lo[4 * w + 1] = __builtin_amdgcn_udot4(c1, pk_lo[u], acc_lo[4 * w + 1], false);
@@ -208,10 +269,12 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
     }
     // lanes with the same column chunk (stride CPR) hold partial sums
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int h = 0; h < QH; ++h)
 #pragma unroll
-        for (int off = CPR; off < 64; off <<= 1) acc[i] += __shfl_xor(acc[i], off);
-    }
+        for (int i = 0; i < 16; ++i) {
+#pragma unroll
+            for (int off = CPR; off < 64; off <<= 1) acc[h][i] += __shfl_xor(acc[h][i], off);
+        }
     if constexpr (P16) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -221,24 +284,29 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
     }
     if (g == 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s_red[0][wave][16 * c + i] = static_cast<int32_t>(acc[i]);
+        for (int h = 0; h < QH; ++h)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s_red[h][wave][16 * c + i] = static_cast<int32_t>(acc[h][i]);
         if constexpr (P16) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) s_red[P16 ? 1 : 0][wave][16 * c + i] = static_cast<int32_t>(acc_lo[i]);
         }
     }
     __syncthreads();
-    for (int d = tid; d < D; d += kDecodeThreads) {
-        const uint32_t tot = static_cast<uint32_t>(s_red[0][0][d]) + static_cast<uint32_t>(s_red[0][1][d]) +
-                             static_cast<uint32_t>(s_red[0][2][d]) + static_cast<uint32_t>(s_red[0][3][d]);
+    for (int e = tid; e < QH * D; e += NT) {
+        const int h = e / D, d = e % D;
+        uint32_t tot = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) tot += static_cast<uint32_t>(s_red[h][w][d]);
         // sum p v = sum p (v + 128) - 128 sum p; uint16 P: 256 (high bytes) + low bytes
-        uint32_t a = tot - 128u * psum;
+        uint32_t a = tot - 128u * psum[QH == 1 ? 0 : (h & (QH - 1))];
         if constexpr (P16) {
-            const uint32_t lo = static_cast<uint32_t>(s_red[P16 ? 1 : 0][0][d]) + static_cast<uint32_t>(s_red[P16 ? 1 : 0][1][d]) +
-                                static_cast<uint32_t>(s_red[P16 ? 1 : 0][2][d]) + static_cast<uint32_t>(s_red[P16 ? 1 : 0][3][d]);
-            a = 256u * a + (lo - 128u * psum_lo);
+            uint32_t lo16 = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) lo16 += static_cast<uint32_t>(s_red[P16 ? 1 : 0][w][d]);
+            a = 256u * a + (lo16 - 128u * psum_lo);
         }
-        out[head * D + d] = requantise(static_cast<int32_t>(a), P);
+        out[(head0 + h) * D + d] = requantise(static_cast<int32_t>(a), P);
     }
 }
 
@@ -248,19 +316,20 @@ __global__ __launch_bounds__(kDecodeThreads) void ia_decode_kernel(
 
 int decode_max_keys() { return kDecodeMaxKeys; }
 
-template <int D, bool P16>
+template <int D, bool P16, int QH>
 int launch_decode_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, const IaKernelParams& kp,
                     hipStream_t stream, unsigned blocks, int skv_pad, int32_t* row_max, uint32_t* row_sum) {
-    constexpr int kBytesPerKey = P16 ? 6 : 5;     // int32 score/slot + uint8 or uint16 p
+    constexpr int kBytesPerKey = P16 ? 6 : 5 * QH;     // int32 score/slot + uint8 or uint16 p, per query head
+    constexpr int kMaxKeys = QH == 1 ? kDecodeMaxKeys : kDecodeMaxKeys / 2;
     static bool attr = false;
     if (!attr) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_decode_kernel<D, P16>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kBytesPerKey * kDecodeMaxKeys) != hipSuccess)
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_decode_kernel<D, P16, QH>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kBytesPerKey * kMaxKeys) != hipSuccess)
             return INTATTN_E_HIP;
         attr = true;
     }
     const size_t shm = static_cast<size_t>(skv_pad) * kBytesPerKey;
-    hipLaunchKernelGGL((ia_decode_kernel<D, P16>), dim3(blocks), dim3(kDecodeThreads), shm, stream, q, k, v, out,
+    hipLaunchKernelGGL((ia_decode_kernel<D, P16, QH>), dim3(blocks), dim3(kDecodeThreads * QH), shm, stream, q, k, v, out,
                        kp, skv_pad, row_max, row_sum);
     return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
 }
@@ -268,15 +337,23 @@ int launch_decode_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* o
 int launch_decode(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
                   const IaKernelParams& kp, void* stream_v, int32_t* row_max, uint32_t* row_sum) {
     const hipStream_t stream = static_cast<hipStream_t>(stream_v);
-    const long long blocks = static_cast<long long>(kp.B) * kp.H;
-    if (blocks > INT_MAX) return INTATTN_E_SHAPE;
+    const long long heads = static_cast<long long>(kp.B) * kp.H;
+    if (heads > INT_MAX) return INTATTN_E_SHAPE;
     const int skv_pad = (kp.Skv + 255) / 256 * 256;
-    const unsigned nb = static_cast<unsigned>(blocks);
+    const unsigned nb = static_cast<unsigned>(heads);
     if (kp.prob_bits == 16)
-        return D == 64 ? launch_decode_t<64, true>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum)
-                       : launch_decode_t<128, true>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum);
-    return D == 64 ? launch_decode_t<64, false>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum)
-                   : launch_decode_t<128, false>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum);
+        return D == 64 ? launch_decode_t<64, true, 1>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum)
+                       : launch_decode_t<128, true, 1>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum);
+    // two query heads of one K/V head a workgroup when heads share K/V in
+    // pairs, the rows fit its LDS (10 bytes a key) and the halved grid still
+    // gives every compute unit a workgroup
+    if (kp.kv_group % 2 == 0 && skv_pad <= kDecodeMaxKeys / 2 && heads / 2 >= 256) {
+        const unsigned nb2 = static_cast<unsigned>(heads / 2);
+        return D == 64 ? launch_decode_t<64, false, 2>(q, k, v, out, kp, stream, nb2, skv_pad, row_max, row_sum)
+                       : launch_decode_t<128, false, 2>(q, k, v, out, kp, stream, nb2, skv_pad, row_max, row_sum);
+    }
+    return D == 64 ? launch_decode_t<64, false, 1>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum)
+                   : launch_decode_t<128, false, 1>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum);
 }
 
 }  // namespace ia

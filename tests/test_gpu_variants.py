@@ -105,6 +105,11 @@ GQA_CASES = [
     (1, 6, 3, 257, 600, 64, False, 128),
     (4, 32, 8, 1, 2048, 128, False, 32),
     (2, 8, 1, 1, 777, 64, False, 128),
+    # decode with at least 512 query heads in pairs: two query heads of one
+    # K/V head a workgroup (K and V read once for both)
+    (16, 32, 8, 1, 3000, 128, False, 32),
+    (32, 16, 2, 1, 8192, 64, False, 64),
+    (16, 32, 1, 1, 1001, 128, False, 128),
 ]
 
 
