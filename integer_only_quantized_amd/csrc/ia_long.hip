@@ -149,6 +149,13 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
         }
     };
 
+    // K tile stage st: 0..2 in the K ring; the passes that read K alone also
+    // use the V ring, as stages 3..5 (the two rings are contiguous)
+    static_assert(offsetof(L, v) == offsetof(L, k) + kStages * L::TB, "K and V rings adjacent");
+    auto kstage = [&](int st) -> int8_t* {
+        return reinterpret_cast<int8_t*>(&lds) + offsetof(L, k) + static_cast<size_t>(st) * L::TB;
+    };
+
     // S^T block kb (0 or 1) of the K tile in stage st, from accumulator c0
     auto scores = [&](int st, int kb, const v16i& c0) {
         v16i s = c0;
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int c = (2 * ks + hh) ^ k_swz<D>(r);
-            const v4i a = *reinterpret_cast<const v4i*>(&lds.k[st][r * D + 16 * c]);
+            const v4i a = *reinterpret_cast<const v4i*>(kstage(st) + r * D + 16 * c);
             s = mfma_i8_32x32x32(a, qf[ks], s);
         }
         return s;
@@ -210,10 +217,35 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
         }
     };
 
+    // Passes over K alone: six stages, two tiles between workgroup barriers,
+    // loads requested four tiles ahead. Tiles t+4 and t+5 go to the stages of
+    // t-2 and t-1, which every wave finished before the last barrier; at the
+    // end of a pair, tiles t+2 and t+3 must have landed.
+    auto run_k_tiles = [&](auto&& body) {
+        wait_vmcnt(0);                       // nothing else in flight when counting
+        const int pre = min(ntiles, 4);
+        for (int t = 0; t < pre; ++t) issue(kh, kstage(t), koff, t);
+        wait_vmcnt(max(0, pre - 2) * LOADS);  // tiles 0 and 1 landed
+        lds_barrier();
+        for (int t = 0; t < ntiles; t += 2) {
+            int issued = 0;
+            for (int u = 4; u < 6; ++u) {
+                if (t + u < ntiles) {
+                    issue(kh, kstage((t + u) % (2 * kStages)), koff, t + u);
+                    ++issued;
+                }
+            }
+            body(t, t % (2 * kStages));
+            if (t + 1 < ntiles) body(t + 1, (t + 1) % (2 * kStages));
+            wait_vmcnt(issued * LOADS);
+            lds_barrier();
+        }
+    };
+
     // ---- pass 1: row max ---------------------------------------------------
     const v16i zero16 = v16i{};
     int32_t mrow = INT_MIN;
-    run_tiles(false, [&](int t, int st) {
+    run_k_tiles([&](int t, int st) {
         v16i s0 = scores(st, 0, zero16);
         v16i s1 = scores(st, 1, zero16);
         mask(s0, t * kLongTile, INT_MIN);
@@ -236,7 +268,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
 
     // ---- pass 2: row sum of the table entries ------------------------------
     uint32_t E = 0;
-    run_tiles(false, [&](int t, int st) {
+    run_k_tiles([&](int t, int st) {
         v16i s0 = scores(st, 0, cinit);
         v16i s1 = scores(st, 1, cinit);
         mfma_result_guard(s0, s1);           // the slot word (inline asm) reads them
