@@ -118,30 +118,6 @@ __device__ __forceinline__ uint32_t lut_byte_addr(uint32_t t) {
     return a;
 }
 
-// Byte address of the table entry for byte i of a packed word of top bytes
-// (the same mapping as lut_byte_addr), one SDWA op.
-template <int KM>
-__device__ __forceinline__ uint32_t lut_byte_addr_of(uint32_t w, int i) {
-    uint32_t a;
-    if constexpr (KM == 1) {
-        switch (i) {
-            case 0: asm("v_lshlrev_b32_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(a) : "v"(w)); break;
-            case 1: asm("v_lshlrev_b32_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(a) : "v"(w)); break;
-            case 2: asm("v_lshlrev_b32_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(a) : "v"(w)); break;
-            default: asm("v_lshlrev_b32_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(a) : "v"(w)); break;
-        }
-    } else {
-        const uint32_t m = KM == 4 ? 0x7cu : 0x7eu;
-        switch (i) {
-            case 0: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
-            case 1: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
-            case 2: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
-            default: asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD" : "=v"(a) : "v"(w), "s"(m)); break;
-        }
-    }
-    return a;
-}
-
 // int32 accumulator -> int8: sign(a) * min(127, (|a|*M_o + 2^(sh_o-1)) >> sh_o).
 // One signed product instead of magnitude and sign: with h = 2^(sh-1),
 // -floor((|a|M + h) / 2^sh) = floor((aM + 2^sh - 1 - h) / 2^sh) for a < 0, so

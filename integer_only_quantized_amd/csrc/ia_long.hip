@@ -10,10 +10,12 @@
 //   * one workgroup = 4 waves = 128 query rows of one (b, h); each wave owns
 //     32 rows, holds their Q fragments, and produces S^T blocks (32 keys x
 //     32 queries) on v_mfma_i32_32x32x32_i8, so each lane holds one row;
-//   * keys and values arrive in tiles of 64 rows through a three-stage LDS
-//     ring filled by global_load_lds_dwordx4 (no register staging): tile
-//     t+2 is requested while tile t is computed, and only tile t+1 is
-//     waited for (s_waitcnt vmcnt) before the per-tile barrier;
+//   * keys and values arrive in tiles of 64 rows through an LDS ring filled
+//     by global_load_lds_dwordx4 (no register staging). The P.V pass uses
+//     three K+V stages: tile t+2 is requested while tile t is computed, and
+//     only tile t+1 is waited for (s_waitcnt vmcnt) before the per-tile
+//     barrier. The two passes over K alone use the V stages as well (six K
+//     stages): two tiles between barriers, loads four tiles ahead;
 //   * LDS reads are bank-conflict free on the 64-bank LDS (16 lanes per
 //     cycle for 16-byte reads): K rows have their 16-byte chunks XOR-swizzled
 //     by the row; V rows stay row-major (chunks swizzled by the key) and the
@@ -188,15 +190,17 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
             vaddr[2 * db + rd] = static_cast<uint32_t>(offsetof(L, v)) + tr8_lane_addr<D>(lane, db, rd);
     }
 
-    auto run_tiles = [&](bool with_v, auto&& body) {
+    // The pass over K and V: three stages, one tile between workgroup
+    // barriers, loads requested two tiles ahead.
+    auto run_kv_tiles = [&](auto&& body) {
         // prologue: tiles 0 and 1 requested, tile 0 waited for
-        const int per_tile = with_v ? 2 * LOADS : LOADS;
+        constexpr int per_tile = 2 * LOADS;
         wait_vmcnt(0);                       // nothing else in flight when counting
         issue(kh, lds.k[0], koff, 0);
-        if (with_v) issue(vh, lds.v[0], voff, 0);
+        issue(vh, lds.v[0], voff, 0);
         if (ntiles > 1) {
             issue(kh, lds.k[1], koff, 1);
-            if (with_v) issue(vh, lds.v[1], voff, 1);
+            issue(vh, lds.v[1], voff, 1);
             wait_vmcnt(per_tile);
         } else {
             wait_vmcnt(0);
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
             if (t + 2 < ntiles) {
                 const int st2 = (t + 2) % kStages;
                 issue(kh, lds.k[st2], koff, t + 2);
-                if (with_v) issue(vh, lds.v[st2], voff, t + 2);
+                issue(vh, lds.v[st2], voff, t + 2);
             }
             body(t, st);
             // tile t+1 must have landed; tile t+2 may stay in flight
@@ -315,7 +319,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
         hi = static_cast<int>(h);
         lo = static_cast<int>(l ^ 0x80808080u);
     };
-    run_tiles(true, [&](int t, int st) {
+    run_kv_tiles([&](int t, int st) {
         const bool colsum_turn = (t % kLongWaves) == wave;
         uint32_t va[2 * DB];
 #pragma unroll

@@ -43,7 +43,6 @@
 namespace ia {
 namespace {
 
-constexpr int kShortLut = 128;
 // Staging of a key block: split between the two query-group waves of its key
 // half (each loads part of it; a workgroup barrier per block makes the other
 // part visible), or loaded whole by both (identical bytes; each wave waits
