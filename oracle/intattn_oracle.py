@@ -48,6 +48,16 @@ default):
     R16 = floor((65535*2^16 + floor(E/2)) / E) and p = (e*R16 + 2^15) >> 16
     (uint16; e*R16 + 2^15 < 2^32), and the output multiplier
     mu_o = s_v / (65535 * s_o); every other step is unchanged.
+  * uint8 table: the lookup-table granularity item frames the table as a
+    trade-off between accuracy and memory; lut_bits = 8 is the narrow end
+    of that trade (entry width, independent of N). Entries
+    e8[k] = rint(255 exp(-k delta)) for k < N-1 (255 for a key at the row
+    max), e8[N-1] = 0; E8 = sum of the e8; the reciprocal is the nearest
+    integer to 255*2^16 / E8, halves rounded up:
+    R8 = floor((255*2^17 + E8) / (2*E8)), p = (e8*R8 + 2^15) >> 16 (uint8);
+    with uint16 probabilities R8 = floor((65535*2^10 + E8) / (2*E8))
+    (nearest to 65535*2^9 / E8) and p = (e8*R8 + 2^8) >> 9. The row sum
+    reported is E8.
 
 Parity pins: see tests/test_oracle_*.py. Every function here is pinned by a
 property, closed form, brute-force twin or exact-rational bound; none is
@@ -72,6 +82,8 @@ R_SHIFT = 23                  # reciprocal fixed point: R = round(255*2^23 / E)
 P16_ONE = 65535               # uint16 probabilities (variant), target row sum 65535
 R16_SHIFT = 16                # R16 = round(65535*2^16 / E)
 PROB_BITS = (8, 16)
+LUT8_ONE = 255                # uint8 table variant: entry for a zero relative score
+LUT_BITS = (16, 8)            # table entry width: Q15 (the specification) or uint8
 REQ_FRAC = 31                 # requantisation multiplier normalised to [2^30, 2^31)
 SKV_MAX = 65535               # keeps E < 2^31 and every int32 accumulator exact
 MU_MIN = 2.0 ** -16           # bin multiplier range (index units per score unit)
@@ -93,7 +105,7 @@ class OracleRangeError(ValueError):
 @dataclass(frozen=True)
 class Params:
     """Integers frozen on the host before any score is computed."""
-    lut: tuple            # lut_size uint16 table entries, the last one 0
+    lut: tuple            # lut_size table entries (Q15, or uint8 when lut_bits = 8), the last one 0
     idx_mul: int          # M: bin multiplier, idx = (x*M + 2^23) >> 24
     idx_shift: int        # always IDX_SHIFT
     x_clip: int           # smallest relative score x that lands in slot 31
@@ -105,6 +117,7 @@ class Params:
     mu_o: float           # s_v / (P_one * s_o), P_one = 255 or 65535
     lut_size: int = LUT_SIZE  # N: table entries (slots 0..N-1)
     prob_bits: int = 8        # probability width: 8 (uint8) or 16 (uint16 variant)
+    lut_bits: int = 16        # table entry width: 16 (Q15) or 8 (uint8 variant)
 
 
 def _f32(x) -> float:
@@ -118,25 +131,34 @@ def _check_lut_size(lut_size: int) -> int:
     return int(lut_size)
 
 
-def build_lut(clip: float, lut_size: int = LUT_SIZE) -> tuple:
+def _check_lut_bits(lut_bits: int) -> int:
+    if lut_bits not in LUT_BITS:
+        raise OracleRangeError("lut_bits must be 16 or 8")
+    return int(lut_bits)
+
+
+def build_lut(clip: float, lut_size: int = LUT_SIZE, lut_bits: int = 16) -> tuple:
     """The N-entry exp table (N = 32: the pages' table).
 
     Slot k approximates exp(-k * delta) with delta = clip / (N-1), stored as
-    round-half-even(2^15 * exp(-k*delta)) for k < N-1. Slot N-1 is the
-    sparse tail and holds 0: every key clipped there drops out of the sum.
+    round-half-even(one * exp(-k*delta)) for k < N-1, one = 2^15 (Q15) or
+    255 (uint8 variant). Slot N-1 is the sparse tail and holds 0: every key
+    clipped there drops out of the sum.
     """
     n = _check_lut_size(lut_size)
+    one = LUT_ONE if _check_lut_bits(lut_bits) == 16 else LUT8_ONE
     c = _f32(clip)
     if not (math.isfinite(c) and c > 0.0):
         raise OracleRangeError("clip must be finite and > 0")
     delta = c / float(n - 1)
-    lut = [int(round(LUT_ONE * math.exp(-(float(k) * delta)))) for k in range(n - 1)]
+    lut = [int(round(one * math.exp(-(float(k) * delta)))) for k in range(n - 1)]
     lut.append(0)
     return tuple(lut)
 
 
 def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
-                  clip: float, lut_size: int = LUT_SIZE, prob_bits: int = 8) -> Params:
+                  clip: float, lut_size: int = LUT_SIZE, prob_bits: int = 8,
+                  lut_bits: int = 16) -> Params:
     """Host parameter derivation.
 
     alpha = s_q*s_k/sqrt(D) folds the 1/sqrt(d) attention scale into the
@@ -144,6 +166,7 @@ def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
     table slots; M = round(mu * 2^24).
     """
     n = _check_lut_size(lut_size)
+    lut_bits = _check_lut_bits(lut_bits)
     if prob_bits not in PROB_BITS:
         raise OracleRangeError("prob_bits must be 8 or 16")
     if D < 1:
@@ -152,7 +175,7 @@ def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
     for s in (sq, sk, sv, so):
         if not (math.isfinite(s) and s > 0.0):
             raise OracleRangeError("scales must be finite and > 0")
-    lut = build_lut(c, n)
+    lut = build_lut(c, n, lut_bits)
     alpha = (sq * sk) / math.sqrt(float(D))
     delta = c / float(n - 1)
     mu = alpha / delta
@@ -173,7 +196,7 @@ def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
         raise OracleRangeError("output multiplier outside the encodable range")
     return Params(lut=lut, idx_mul=idx_mul, idx_shift=IDX_SHIFT, x_clip=x_clip,
                   req_mul=req_mul, req_shift=req_shift, alpha=alpha, delta=delta,
-                  mu=mu, mu_o=mu_o, lut_size=n, prob_bits=prob_bits)
+                  mu=mu, mu_o=mu_o, lut_size=n, prob_bits=prob_bits, lut_bits=lut_bits)
 
 
 # ---------------------------------------------------------------------------
@@ -213,6 +236,32 @@ def normalise(e, R):
     """uint8 probability p = (e*R + 2^22) >> 23 (round half up)."""
     e = np.asarray(e, dtype=np.int64)
     return (e * R + np.int64(1 << (R_SHIFT - 1))) >> np.int64(R_SHIFT)
+
+
+def reciprocal8(E8):
+    """uint8 table: R8 = floor((255*2^17 + E8) / (2*E8)), the nearest integer
+    to 255*2^16 / E8 (halves up)."""
+    E8 = np.asarray(E8, dtype=np.int64)
+    return (np.int64(P_ONE << 17) + E8) // (2 * E8)
+
+
+def normalise8(e8, R8):
+    """uint8 table, uint8 p = (e8*R8 + 2^15) >> 16."""
+    e8 = np.asarray(e8, dtype=np.int64)
+    return (e8 * R8 + np.int64(1 << 15)) >> np.int64(16)
+
+
+def reciprocal8_16(E8):
+    """uint8 table, uint16 p: R = floor((65535*2^10 + E8) / (2*E8)), the
+    nearest integer to 65535*2^9 / E8 (halves up)."""
+    E8 = np.asarray(E8, dtype=np.int64)
+    return (np.int64(P16_ONE << 10) + E8) // (2 * E8)
+
+
+def normalise8_16(e8, R):
+    """uint8 table, uint16 p = (e8*R + 2^8) >> 9."""
+    e8 = np.asarray(e8, dtype=np.int64)
+    return (e8 * R + np.int64(1 << 8)) >> np.int64(9)
 
 
 def requantise(a, prm: Params):
@@ -256,7 +305,8 @@ def index_softmax(S, prm: Params, causal: bool):
     Row max over the allowed keys, relative scores x = m - s, table slots with
     the sparsity-aware clip, int32 row sum E of the table entries, integer
     reciprocal R and uint8 probabilities p = (e*R + 2^22) >> 23 (uint16
-    variant: p = (e*R16 + 2^15) >> 16). Keys that are not allowed take the
+    variant: p = (e*R16 + 2^15) >> 16; uint8 table: reciprocal8 and
+    normalise8, or their uint16 forms). Keys that are not allowed take the
     last slot (entry 0, p = 0). Returns P uint8 (or uint16) [Sq, Skv],
     m int64 [Sq], E int64 [Sq].
     """
@@ -270,6 +320,12 @@ def index_softmax(S, prm: Params, causal: bool):
     lut = np.asarray(prm.lut, dtype=np.int64)
     e = lut[idx]
     E = e.sum(axis=1)
+    if prm.lut_bits == 8:
+        if prm.prob_bits == 16:
+            P = normalise8_16(e, reciprocal8_16(E)[:, None])
+            return P.astype(np.uint16), m, E
+        P = normalise8(e, reciprocal8(E)[:, None])
+        return P.astype(np.uint8), m, E
     if prm.prob_bits == 16:
         P = normalise16(e, reciprocal16(E)[:, None])
         return P.astype(np.uint16), m, E
@@ -317,19 +373,20 @@ def check_args(q, k, v, causal, kv_heads=None):
 
 
 def forward(q, k, v, scales, clip=DEFAULT_CLIP, causal=False, stats=False,
-            lut_size=LUT_SIZE, kv_heads=None, prob_bits=8):
+            lut_size=LUT_SIZE, kv_heads=None, prob_bits=8, lut_bits=16):
     """Full forward over int8 tensors q [B, H, Sq, D], k and v [B, Hkv, Skv, D].
 
     scales = (s_q, s_k, s_v, s_o); lut_size: table entries (32 is the pages'
     table); kv_heads = Hkv (None: H), query head h reading K/V head
-    h // (H // Hkv); prob_bits: 8 (uint8 P) or 16 (uint16 variant). Returns
+    h // (H // Hkv); prob_bits: 8 (uint8 P) or 16 (uint16 variant);
+    lut_bits: 16 (Q15 table) or 8 (uint8 table variant). Returns
     out int8 [B, H, Sq, D]; with stats=True also (m int64 [B,H,Sq],
     E int64 [B,H,Sq], P uint8/uint16 [B,H,Sq,Skv]).
     """
     q, k, v = (np.ascontiguousarray(t) for t in (q, k, v))
     B, H, Sq, Skv, D = check_args(q, k, v, causal, kv_heads)
     group = H // k.shape[1]
-    prm = derive_params(D, *scales, clip, lut_size, prob_bits)
+    prm = derive_params(D, *scales, clip, lut_size, prob_bits, lut_bits)
     out = np.zeros((B, H, Sq, D), dtype=np.int8)
     if stats:
         M = np.zeros((B, H, Sq), dtype=np.int64)

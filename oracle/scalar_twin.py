@@ -5,7 +5,7 @@ smoke check and the benchmark's CPU-baseline leg may import it).
 
 It restates each IndexSoftmax step of the IntAttention digest pages
 (section "Methodology", step 2: clip, table lookup (32 entries, or a finer
-table of 64 or 128), int32 sum,
+table of 64 or 128, with Q15 or uint8 entries), int32 sum,
 reciprocal multiply + shift; step 3: integer Q.K^T and P.V) in a different
 form from the vectorised oracle, so that a slip in either (a transposed
 operand, a wrong axis, an off-by-one in a rounding) shows up as a mismatch:
@@ -63,7 +63,12 @@ def head_forward(q, k, v, prm, causal: bool):
             else:
                 e.append(prm.lut[nearest_slot(m - s, prm.idx_mul, prm.idx_shift, len(prm.lut))])
         E = sum(e)
-        if getattr(prm, "prob_bits", 8) == 16:
+        if getattr(prm, "lut_bits", 16) == 8:
+            # uint8 table: R nearest to 255*2^16/E (uint8 p) or 65535*2^9/E (uint16 p)
+            one, frac = (65535, 9) if getattr(prm, "prob_bits", 8) == 16 else (255, 16)
+            R = round_half_up(Fraction(one << frac, E))
+            p = [round_half_up(Fraction(ej * R, 1 << frac)) for ej in e]
+        elif getattr(prm, "prob_bits", 8) == 16:
             R = round_half_up(Fraction(65535 << 16, E))  # R16 = floor(65535*2^16/E + 1/2)
             p = [round_half_up(Fraction(ej * R, 1 << 16)) for ej in e]
         else:

@@ -1,5 +1,5 @@
-"""Pins for the oracle's variants: finer exp tables (64 and 128 entries) and
-grouped K/V heads.
+"""Pins for the oracle's variants: finer exp tables (64 and 128 entries),
+uint8 table entries, grouped K/V heads and uint16 probabilities.
 
 The pages' "Limitations & Future Work" (lookup-table granularity) say the
 32-entry table trades accuracy for memory and that very large heads may need
@@ -321,3 +321,142 @@ def test_prob_bits_refused_outside_8_and_16():
     # the output multiplier carries the probability scale: mu_o(16) = mu_o(8) * 255 / 65535
     assert abs(p16.mu_o * 65535 - p8.mu_o * 255) <= 1e-15 * p8.mu_o * 255
     assert (p16.idx_mul, p16.x_clip, p16.lut) == (p8.idx_mul, p8.x_clip, p8.lut)
+
+
+# ---------------------------------------------------------------------------
+# uint8 exp table (the narrow end of the table's accuracy/memory trade)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [32] + FINE)
+@pytest.mark.parametrize("clip", CLIPS)
+def test_lut8_matches_high_precision_exp(n, clip):
+    """|e8[k] - 255 exp(-k c/(N-1))| <= 1/2 in 50-digit decimal; 255 at a
+    zero relative score, 0 in the tail slot; non-increasing."""
+    getcontext().prec = 50
+    lut = O.build_lut(clip, n, 8)
+    assert len(lut) == n and lut[0] == 255 and lut[-1] == 0
+    c = Decimal(float(np.float32(clip)))
+    for k in range(n - 1):
+        ref = Decimal(255) * (-(Decimal(k) * c / Decimal(n - 1))).exp()
+        assert abs(Decimal(lut[k]) - ref) <= Decimal("0.5") + Decimal("1e-9"), (n, k)
+    assert all(lut[k] >= lut[k + 1] for k in range(n - 1))
+
+
+@pytest.mark.parametrize("n", [32] + FINE)
+def test_lut8_halving_table(n):
+    """clip = (N-1) ln 2 makes the bin width ln 2, so slot k holds 255 / 2^k
+    rounded: 64, 32, 16, 8, 4, 2, 1 for k = 2..8 and 0 from k = 9 on (slot 1,
+    127.5, sits on a rounding tie that float32 clip decides either way)."""
+    lut = O.build_lut((n - 1) * math.log(2.0), n, 8)
+    assert lut[0] == 255 and lut[1] in (127, 128)
+    assert list(lut[2:9]) == [64, 32, 16, 8, 4, 2, 1]
+    assert not any(lut[9:])
+
+
+def test_lut8_uniform_rows():
+    """A uniform row of n keys (every e8 = 255, E8 = 255 n): uint8 p is
+    floor(255/n + 1/2) for every admissible n, hence 0 from n = 511 on; the
+    uint16 p stays within 3/4 of 65535/n and never reaches 0."""
+    n = np.arange(1, 65536, dtype=np.int64)
+    E8 = 255 * n
+    p8 = O.normalise8(np.int64(255), O.reciprocal8(E8))
+    want = np.array([(Fraction(255, int(k)) + Fraction(1, 2)).__floor__() for k in n[:4000]])
+    assert np.array_equal(p8[:4000], want)
+    assert (p8[510:] == 0).all() and (p8[:510] >= 1).all()
+    p16 = O.normalise8_16(np.int64(255), O.reciprocal8_16(E8))
+    assert (p16 >= 1).all() and p16[0] == 65535 and p16[1] == 32768
+    assert (np.abs(p16 * n - 65535) <= n * 0.75).all()
+
+
+def test_lut8_normalisation_bound_exact():
+    """|p - 255 e8/E8| <= 1/2 + e8/2^17 (uint8 p) and |p - 65535 e8/E8| <=
+    1/2 + e8/2^10 (uint16 p) with exact rationals: the reciprocal is within
+    1/2 of its real value. p never exceeds 255 (65535)."""
+    rng = np.random.default_rng(31)
+    E8 = rng.integers(255, 65535 * 255, 20000).astype(np.int64)
+    e8 = np.minimum(rng.integers(0, 256, 20000).astype(np.int64), E8)
+    p8 = O.normalise8(e8, O.reciprocal8(E8))
+    p16 = O.normalise8_16(e8, O.reciprocal8_16(E8))
+    assert int(p8.max()) <= 255 and int(p16.max()) <= 65535
+    for ei, Ei, a, b in list(zip(e8.tolist(), E8.tolist(), p8.tolist(), p16.tolist()))[::7]:
+        assert abs(Fraction(a) - Fraction(255 * ei, Ei)) <= Fraction(1, 2) + Fraction(ei, 1 << 17)
+        assert abs(Fraction(b) - Fraction(65535 * ei, Ei)) <= Fraction(1, 2) + Fraction(ei, 1 << 10)
+    # a row whose keys all sit at the max: p = 255 (65535)
+    assert int(O.normalise8(255, O.reciprocal8(255))) == 255
+    assert int(O.normalise8_16(255, O.reciprocal8_16(255))) == 65535
+
+
+def test_lut8_equals_the_q15_normaliser_on_entries_times_128():
+    """128 e8 in a Q15 slot leaves every probability unchanged: with E = 128 E8
+    the Q15 reciprocal floor((255*2^23 + E/2)/E) equals floor((255*2^17 + E8)/(2 E8))
+    and (128 e8 R + 2^22) >> 23 equals (e8 R + 2^15) >> 16 (and likewise for
+    uint16 p), exhaustively over e8 and over row sums from one key up."""
+    rng = np.random.default_rng(32)
+    E8 = np.concatenate([np.arange(255, 5000), rng.integers(5000, 65535 * 255, 20000)]).astype(np.int64)
+    assert np.array_equal(O.reciprocal8(E8), O.reciprocal(128 * E8))
+    assert np.array_equal(O.reciprocal8_16(E8), O.reciprocal16(128 * E8))
+    for e in range(256):
+        ee = np.minimum(np.int64(e), E8)
+        assert np.array_equal(O.normalise8(ee, O.reciprocal8(E8)), O.normalise(128 * ee, O.reciprocal(128 * E8)))
+        assert np.array_equal(O.normalise8_16(ee, O.reciprocal8_16(E8)),
+                              O.normalise16(128 * ee, O.reciprocal16(128 * E8)))
+
+
+def test_lut_bits_refused_outside_the_variants():
+    for bad in (0, 4, 12, 32):
+        with pytest.raises(O.OracleRangeError):
+            O.build_lut(O.DEFAULT_CLIP, 32, bad)
+        with pytest.raises(O.OracleRangeError):
+            O.derive_params(64, 0.05, 0.05, 0.05, 0.05, O.DEFAULT_CLIP, 32, 8, bad)
+
+
+@pytest.mark.parametrize("n", [32, 128])
+@pytest.mark.parametrize("prob_bits", [8, 16])
+@pytest.mark.parametrize("Sq,Skv,D,causal,seed,scales", TWIN)
+def test_lut8_twin_agrees_on_tiny_shapes(n, prob_bits, Sq, Skv, D, causal, seed, scales):
+    rng = np.random.default_rng(seed + 40)
+    q = rng.integers(-127, 128, (1, 1, Sq, D)).astype(np.int8)
+    k = rng.integers(-127, 128, (1, 1, Skv, D)).astype(np.int8)
+    v = rng.integers(-127, 128, (1, 1, Skv, D)).astype(np.int8)
+    prm = O.derive_params(D, *scales, O.DEFAULT_CLIP, n, prob_bits, 8)
+    out, m, E, P = O.forward(q, k, v, scales, O.DEFAULT_CLIP, causal, stats=True, lut_size=n,
+                             prob_bits=prob_bits, lut_bits=8)
+    tout, tm, tE, tP = T.head_forward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), prm, causal)
+    assert out[0, 0].tolist() == tout and m[0, 0].tolist() == tm
+    assert E[0, 0].tolist() == tE and P[0, 0].tolist() == tP
+
+
+def test_lut8_single_key_returns_v():
+    """One key: e8 = 255, p = 255, and with s_o = s_v the output is v."""
+    vals = np.arange(-127, 128, dtype=np.int8)
+    v1 = vals.reshape(1, 1, 1, 255)
+    rng = np.random.default_rng(33)
+    q1 = rng.integers(-127, 128, (1, 1, 3, 255)).astype(np.int8)
+    k1 = rng.integers(-127, 128, (1, 1, 1, 255)).astype(np.int8)
+    out, _, E, P = O.forward(q1, k1, v1, (0.05, 0.05, 0.01, 0.01), stats=True, lut_bits=8)
+    assert (P == 255).all() and (E == 255).all()
+    assert (out[0, 0] == vals[None, :]).all()
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,D,causal,seed,kind", CASES)
+def test_lut8_against_float64_softmax(B, H, Sq, Skv, D, causal, seed, kind):
+    """The float64 bound of the Q15 tables holds for the uint8 table with its
+    own per-key error (beta from its smallest nonzero entry), and on these
+    rows the mean |p/255 - p_ref| stays within 2% of the Q15 table's."""
+    w = W.make_random(B, H, Sq, Skv, D, causal, seed, kind)
+    prm = O.derive_params(D, *w.scales, w.clip, 32, 8, 8)
+    _, m, _, P = O.forward(w.q, w.k, w.v, w.scales, w.clip, causal, stats=True, lut_bits=8)
+    P16 = O.forward(w.q, w.k, w.v, w.scales, w.clip, causal, stats=True)[3]
+    tb = math.tanh(_beta(prm) / 2)
+    e8 = e16 = 0.0
+    for b in range(B):
+        for h in range(H):
+            pref = _ref_softmax(w.q[b, h], w.k[b, h], prm.alpha, causal)
+            S = w.q[b, h].astype(np.int64) @ w.k[b, h].astype(np.int64).T
+            allow = O.allowed_mask(Sq, Skv, causal)
+            clipped = allow & (m[b, h][:, None] - S >= prm.x_clip)
+            tau = np.where(clipped, pref, 0.0).sum(axis=1)
+            dp = np.abs(P[b, h] / 255.0 - pref).max(axis=1)
+            assert (dp <= tb + tau + (0.5 + 2 ** -9) / 255 + 1e-12).all()
+            e8 += np.abs(P[b, h] / 255.0 - pref).mean()
+            e16 += np.abs(P16[b, h] / 255.0 - pref).mean()
+    assert e8 <= 1.02 * e16
