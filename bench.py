@@ -318,8 +318,9 @@ def _time_calls(fn, stream, n, warm_s=0.3):
 
 def variants(steps=None):
     """The variants beside the 32-entry MHA path: finer exp tables (64, 128
-    entries) and uint16 probabilities on the BERT and causal-prefill workloads
-    (int8 TOPS and MFMA fraction; uint16 also on the decode shape), grouped
+    entries), uint8 table entries and uint16 probabilities on the BERT and
+    causal-prefill workloads (int8 TOPS and MFMA fraction; uint8 entries and
+    uint16 also on the decode shape), grouped
     K/V heads on the batched decode shape (HBM GB/s of
     Q + K + V + O with K/V read once per K/V head), and the decode-step cache
     update (HBM GB/s of 4 bytes read and 1 written per value). One JSON line."""
@@ -356,6 +357,12 @@ def variants(steps=None):
         tops = ops / (us * 1e-6) / 1e12
         res.setdefault("uint16_probabilities", {})[cfg] = {"us_per_call": us, "int8_TOPS": tops,
                                                           "mfma_frac": tops / PEAK_INT8_TOPS}
+        # uint8 table entries (32 entries): the same kernels, the table in Q15 units
+        fn = lambda: ia.forward_ex(q, k, v, w.scales, w.clip, w.causal, 32, out=out, lut_bits=8)
+        us = _time_calls(fn, stream, steps or (200 if cfg == "bert" else 30))
+        tops = ops / (us * 1e-6) / 1e12
+        res.setdefault("uint8_table", {})[cfg] = {"us_per_call": us, "int8_TOPS": tops,
+                                                  "mfma_frac": tops / PEAK_INT8_TOPS}
 
     # grouped K/V heads on the decode shape: B=16, H=32, Skv=8192, d=128
     B, H, Skv, D = 16, 32, 8192, 128
@@ -382,6 +389,11 @@ def variants(steps=None):
             gbs16 = nbytes / (us16 * 1e-6) / 1e9
             res.setdefault("uint16_probabilities", {})["decode"] = {"us_per_call": us16, "GBs": gbs16,
                                                                     "hbm_frac": gbs16 / PEAK_HBM_GBS}
+            fn8 = lambda: ia.forward_ex(q, k, v, scales, W.DEFAULT_CLIP, False, 32, out=out, lut_bits=8)
+            us8 = _time_calls(fn8, stream, steps or 100)
+            gbs8 = nbytes / (us8 * 1e-6) / 1e9
+            res.setdefault("uint8_table", {})["decode"] = {"us_per_call": us8, "GBs": gbs8,
+                                                           "hbm_frac": gbs8 / PEAK_HBM_GBS}
         del k, v
     torch.cuda.empty_cache()
 

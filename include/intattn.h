@@ -140,7 +140,16 @@ int intattn_forward_debug(const int8_t* q, const int8_t* k, const int8_t* v, int
  * prob_bits = 16: R16 = (65535*2^16 + E/2) / E, p = (lut[idx]*R16 + 2^15)
  * >> 16 (uint16, target row sum 65535), and mu_o = s_v/(65535*s_o); the
  * long-row and decode kernels run it (P.V as two int8 products, high and
- * low probability bytes). */
+ * low probability bytes).
+ * uint8 table entries: the lookup-table granularity item frames the table as
+ * an accuracy/memory trade; lut_bits = 8 stores e8[k] = rint(255 exp(-k
+ * delta)) for k < N-1 and e8[N-1] = 0 (any N), and with E8 = sum_j e8
+ *   R8 = (255*2^17 + E8) / (2*E8),  p = (e8*R8 + 2^15) >> 16        (uint8)
+ *   R8 = (65535*2^10 + E8) / (2*E8), p = (e8*R8 + 2^8) >> 9     (uint16 P).
+ * The kernels receive the table in Q15 units, lut = 128*e8: with E = 128*E8
+ * the Q15 reciprocal and product above give exactly these R8 and p (both
+ * fractions reduce by 128), so every kernel serves both widths; row_sum then
+ * reports E = 128*E8. */
 typedef struct intattn_variant {
     int32_t lut_size;    /* exp-table entries: 32, 64 or 128; 0 means 32     */
     int32_t kv_heads;    /* K/V heads; 0 means H                             */
@@ -149,11 +158,13 @@ typedef struct intattn_variant {
                             attended); 0 means Skv                           */
     int32_t prob_bits;   /* probability width: 8 (uint8, the specification
                             above) or 16 (uint16 variant); 0 means 8         */
+    int32_t lut_bits;    /* table entry width: 16 (Q15, the specification
+                            above) or 8 (uint8 entries); 0 means 16          */
 } intattn_variant;
 
 typedef struct intattn_params_ex {
-    uint16_t lut[128];  /* entries 0..lut_size-1 (entry lut_size-1 is 0);
-                           the rest 0                                        */
+    uint16_t lut[128];  /* entries 0..lut_size-1 in Q15 units (128*e8 for
+                           lut_bits 8; entry lut_size-1 is 0); the rest 0   */
     int32_t  lut_size;
     int32_t  idx_mul;   /* M                                                 */
     int32_t  idx_shift; /* always 24                                         */
@@ -161,28 +172,32 @@ typedef struct intattn_params_ex {
     int32_t  req_shift; /* sh_o, 1 .. 63                                     */
     int64_t  req_mul;   /* M_o                                               */
     int32_t  prob_bits; /* 8 or 16                                           */
+    int32_t  lut_bits;  /* 16 or 8                                           */
 } intattn_params_ex;
 
-/* The lut_size-entry exp table (lut_out holds lut_size entries). Host only,
- * pure. Errors: E_NULL, E_CLIP, E_RANGE (lut_size not 32, 64 or 128). */
-int intattn_build_lut_ex(float clip, int32_t lut_size, uint16_t* lut_out);
+/* The lut_size-entry exp table of lut_bits-bit entries (lut_out holds
+ * lut_size entries: Q15 for 16, e8 in 0..255 for 8). Host only, pure.
+ * Errors: E_NULL, E_CLIP, E_RANGE (lut_size not 32, 64 or 128, lut_bits not
+ * 16 or 8). */
+int intattn_build_lut_ex(float clip, int32_t lut_size, int32_t lut_bits, uint16_t* lut_out);
 
-/* intattn_derive_params for a lut_size-entry table and prob_bits-wide
+/* intattn_derive_params for a lut_size-entry table of lut_bits-bit entries
+ * (16 or 8; out->lut holds the table in Q15 units) and prob_bits-wide
  * probabilities (8 or 16; 16 changes only M_o, sh_o). Host only, pure.
  * Errors: E_NULL, E_SHAPE, E_SCALE, E_CLIP, E_RANGE (also lut_size,
- * prob_bits). */
+ * prob_bits, lut_bits). */
 int intattn_derive_params_ex(const intattn_shape* shape, const intattn_scales* scales,
-                             float clip, int32_t lut_size, int32_t prob_bits,
+                             float clip, int32_t lut_size, int32_t prob_bits, int32_t lut_bits,
                              intattn_params_ex* out);
 
 /* intattn_forward with a variant (NULL: lut_size 32, kv_heads H, no cache
- * padding). q and out are [B, H, Sq, D]; k and v are [B, kv_heads,
+ * padding, uint8 P, Q15 table). q and out are [B, H, Sq, D]; k and v are [B, kv_heads,
  * kv_capacity, D], of which rows 0..Skv-1 of each head are read. row_max / row_sum:
  * optional device outputs [B, H, Sq] (both NULL or both set), as in
  * intattn_forward_debug. Every tensor pointer 16-byte aligned; allocates no
  * device memory. Errors: those of intattn_forward, E_NULL for one of
  * row_max / row_sum without the other, E_SHAPE for kv_heads < 0 or not
- * dividing H or for 0 < kv_capacity < Skv, E_RANGE for lut_size. */
+ * dividing H or for 0 < kv_capacity < Skv, E_RANGE for lut_size, prob_bits or lut_bits. */
 int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
                        const intattn_shape* shape, const intattn_scales* scales, float clip,
                        int causal, const intattn_variant* variant, void* stream,

@@ -49,12 +49,13 @@ class Params(ctypes.Structure):
 class ParamsEx(ctypes.Structure):
     _fields_ = [("lut", ctypes.c_uint16 * 128), ("lut_size", ctypes.c_int32), ("idx_mul", ctypes.c_int32),
                 ("idx_shift", ctypes.c_int32), ("x_clip", ctypes.c_int32),
-                ("req_shift", ctypes.c_int32), ("req_mul", ctypes.c_int64), ("prob_bits", ctypes.c_int32)]
+                ("req_shift", ctypes.c_int32), ("req_mul", ctypes.c_int64), ("prob_bits", ctypes.c_int32),
+                ("lut_bits", ctypes.c_int32)]
 
 
 class Variant(ctypes.Structure):
     _fields_ = [("lut_size", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("kv_capacity", ctypes.c_int32),
-                ("prob_bits", ctypes.c_int32)]
+                ("prob_bits", ctypes.c_int32), ("lut_bits", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -83,9 +84,9 @@ def _load():
     lib.intattn_forward_debug.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape),
                                           ctypes.POINTER(Scales), f32, i32, vp, vp, vp, vp]
     lib.intattn_forward_debug.restype = i32
-    lib.intattn_build_lut_ex.argtypes = [f32, i32, ctypes.POINTER(ctypes.c_uint16)]
+    lib.intattn_build_lut_ex.argtypes = [f32, i32, i32, ctypes.POINTER(ctypes.c_uint16)]
     lib.intattn_build_lut_ex.restype = i32
-    lib.intattn_derive_params_ex.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Scales), f32, i32, i32,
+    lib.intattn_derive_params_ex.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Scales), f32, i32, i32, i32,
                                              ctypes.POINTER(ParamsEx)]
     lib.intattn_derive_params_ex.restype = i32
     lib.intattn_forward_ex.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), ctypes.POINTER(Scales), f32, i32,
@@ -135,21 +136,23 @@ def derive_params(D: int, scales, clip: float = DEFAULT_CLIP) -> dict:
             "x_clip": p.x_clip, "req_shift": p.req_shift, "req_mul": p.req_mul}
 
 
-def build_lut_ex(clip: float = DEFAULT_CLIP, lut_size: int = 32) -> list:
+def build_lut_ex(clip: float = DEFAULT_CLIP, lut_size: int = 32, lut_bits: int = 16) -> list:
     buf = (ctypes.c_uint16 * 128)()
-    _check(_lib.intattn_build_lut_ex(float(clip), int(lut_size), buf), "intattn_build_lut_ex")
+    _check(_lib.intattn_build_lut_ex(float(clip), int(lut_size), int(lut_bits), buf), "intattn_build_lut_ex")
     return list(buf)[: int(lut_size)]
 
 
-def derive_params_ex(D: int, scales, clip: float = DEFAULT_CLIP, lut_size: int = 32, prob_bits: int = 8) -> dict:
+def derive_params_ex(D: int, scales, clip: float = DEFAULT_CLIP, lut_size: int = 32, prob_bits: int = 8,
+                     lut_bits: int = 16) -> dict:
     shape = Shape(1, 1, 1, 1, int(D))
     sc = Scales(*[float(s) for s in scales])
     p = ParamsEx()
     _check(_lib.intattn_derive_params_ex(ctypes.byref(shape), ctypes.byref(sc), float(clip), int(lut_size),
-                                         int(prob_bits), ctypes.byref(p)), "intattn_derive_params_ex")
+                                         int(prob_bits), int(lut_bits), ctypes.byref(p)),
+           "intattn_derive_params_ex")
     return {"lut": list(p.lut)[: p.lut_size], "lut_size": p.lut_size, "idx_mul": p.idx_mul,
             "idx_shift": p.idx_shift, "x_clip": p.x_clip, "req_shift": p.req_shift, "req_mul": p.req_mul,
-            "prob_bits": p.prob_bits}
+            "prob_bits": p.prob_bits, "lut_bits": p.lut_bits}
 
 
 _STRUCTS = {}
@@ -337,12 +340,13 @@ def pv(probs, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False, out=N
 
 
 def forward_ex(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False, lut_size: int = 32,
-               stats: bool = False, out=None, skv: int = None, prob_bits: int = 8):
+               stats: bool = False, out=None, skv: int = None, prob_bits: int = 8, lut_bits: int = 16):
     """intattn_forward_ex: q [B,H,Sq,D], k and v [B,Hkv,C,D] int8 CUDA tensors
     (Hkv divides H; query head h reads K/V head h // (H // Hkv)); the first
     skv rows of each K/V head are attended (default all C: a cache of capacity
-    C holding skv tokens); a table of lut_size entries. Returns out, or
-    (out, row_max, row_sum) with stats."""
+    C holding skv tokens); a table of lut_size entries of lut_bits bits;
+    prob_bits-wide probabilities. Returns out, or (out, row_max, row_sum)
+    with stats (row_sum in Q15 units: 128 times the uint8 table's sum)."""
     import torch
     B, H, Sq, C, D = _check_tensors(q, k, v, grouped=True)
     skv = C if skv is None else int(skv)
@@ -351,7 +355,7 @@ def forward_ex(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False
     elif (out.shape != q.shape or out.dtype is not torch.int8 or not out.is_contiguous()
           or out.device != q.device):
         raise ValueError("out must be a contiguous int8 tensor shaped like q, on q's device")
-    var = Variant(int(lut_size), int(k.shape[1]), int(C), int(prob_bits))
+    var = Variant(int(lut_size), int(k.shape[1]), int(C), int(prob_bits), int(lut_bits))
     sh, sc = _structs((B, H, Sq, skv, D), scales)
     rm = rs = None
     if stats:

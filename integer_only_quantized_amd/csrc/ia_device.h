@@ -345,7 +345,7 @@ __device__ __forceinline__ uint32_t prob_word(uint32_t e, uint32_t R2) { return 
 
 // P operand word (p - 128 as int8 for four keys) from two words that each
 // hold two table entries e (bits 0..15 and 16..31), for a row reciprocal
-// R < 2^16 (R <= 65280 since E >= 2^15). With x = e * R + 2^22 + 2^30
+// R < 2^16 and p <= 255. With x = e * R + 2^22 + 2^30
 // (< 2^32; v_mad_u32_u16, op_sel picking the entry's half), bits 23..30 of
 // x are p ^ 0x80 for p = (e * R + 2^22) >> 23: adding 2^30 adds 128 to
 // x >> 23 and leaves nothing below bit 23 changed. Each byte is shifted into
@@ -393,7 +393,8 @@ __device__ __forceinline__ void pack_bytes_32(uint32_t w0, uint32_t w1, uint32_t
     hi = __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
-// R16 = floor((65535 * 2^16 + floor(E/2)) / E) (below 2^17 for E >= 2^15).
+// R16 = floor((65535 * 2^16 + floor(E/2)) / E) (below 2^18 for E >= 128*255,
+// a 24-bit operand).
 __device__ __forceinline__ uint32_t reciprocal16(uint32_t E) {
     return static_cast<uint32_t>((0xFFFF0000ull + (E >> 1)) / E);
 }

@@ -288,7 +288,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
         }
     });
     E += __shfl_xor(E, 32);
-    // uint8 P: R2 = 2R < 2^17; uint16 P: R16 < 2^17 (both 24-bit operands)
+    // uint8 P: R2 = 2R <= 2^17; uint16 P: R16 < 2^18 (E >= 128*255; both 24-bit operands)
     const uint32_t R2 = P16 ? reciprocal16(E) : 2 * (((255u << 23) + (E >> 1)) / E);
     if (row_max != nullptr && hh == 0 && qrow < P.Sq) {
         row_max[head * P.Sq + qrow] = mrow;

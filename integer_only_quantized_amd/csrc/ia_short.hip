@@ -332,10 +332,15 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     lds_barrier();                       // every wave is also done with K (and its K loads)
     stage(vh, true, kb0, nvalid, false);   // V replaces K (whole blocks)
     E += lds.xe[qg][half ^ 1][l32];
-    // E >= 2^15 for every row that exists (it attends at least one key); rows
-    // past Sq may have E = 0 and are never stored
+    // E >= 128*255 for every row that exists (it attends at least one key,
+    // whose entry is 2^15, or 128*255 for a table of uint8 entries); rows
+    // past Sq may have E = 0 and are never stored. R <= 65280 once
+    // E >= 2^15; the one larger value, R = 65536 at E = 128*255, is clamped
+    // to the 16-bit operand's 65535 without changing any p: the entries are
+    // then multiples of 128, and (e*R + 2^22) >> 23 is e/128 for R = 2^16
+    // and for R = 2^16 - 1 alike (e <= 2^15 < 2^22).
     const uint32_t Ed = SKIP ? max(E, 1u) : E;
-    const uint32_t R = ((255u << 23) + (Ed >> 1)) / Ed;
+    const uint32_t R = min(((255u << 23) + (Ed >> 1)) / Ed, 65535u);
     if (row_max != nullptr && half == 0 && hh == 0 && qrow < P.Sq) {
         row_max[head * P.Sq + qrow] = mrow;
         row_sum[head * P.Sq + qrow] = E;

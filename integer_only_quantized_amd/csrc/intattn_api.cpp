@@ -6,6 +6,8 @@
 //   Sq == 1 and Skv <= 16384                -> decode kernel (HBM streaming)
 //   Skv <= 512 (d = 64) or 256 (d = 128)      -> short-row kernel (K/V in LDS)
 //   otherwise                                -> long-row kernel (tiled, 3 passes)
+// (table sizes, entry widths, K/V head groupings and probability widths all
+// run on the same kernels: the table reaches them in Q15 units)
 // intattn_forward_debug with a probability buffer runs the general kernel,
 // which is the only one that materialises P.
 //
@@ -26,10 +28,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Shape, head size and parameter derivation shared by every entry point.
 // lut_size: 32, 64 or 128; kv_heads: K/V heads (0: H), dividing H;
-// kv_capacity: rows per K/V head in memory (0: Skv), at least Skv.
+// kv_capacity: rows per K/V head in memory (0: Skv), at least Skv;
+// prob_bits: 8 or 16; lut_bits: table entry width, 16 or 8.
 int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
                          IaKernelParams* kp, int lut_size = 32, int kv_heads = 0, int kv_capacity = 0,
-                         int prob_bits = 8) {
+                         int prob_bits = 8, int lut_bits = 16) {
     int st = intattn_validate_shape(shape, causal);
     if (st != INTATTN_OK) return st;
     if (shape->D != 64 && shape->D != 128) return INTATTN_E_DIM;
@@ -43,7 +46,7 @@ int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scale
     int32_t idx_mul = 0, x_clip = 0, req_shift = 0;
     int64_t req_mul = 0;
     st = intattn_derive_core(shape, scales, clip, lut_size, lut, &idx_mul, &x_clip, &req_shift, &req_mul,
-                             prob_bits);
+                             prob_bits, lut_bits);
     if (st != INTATTN_OK) return st;
     kp->B = shape->B;
     kp->H = shape->H;
@@ -74,10 +77,11 @@ int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scale
 
 int prepare(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
             const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
-            IaKernelParams* kp, int lut_size = 32, int kv_heads = 0, int kv_capacity = 0, int prob_bits = 8) {
+            IaKernelParams* kp, int lut_size = 32, int kv_heads = 0, int kv_capacity = 0, int prob_bits = 8,
+            int lut_bits = 16) {
     if (!q || !k || !v || !out || !shape || !scales) return INTATTN_E_NULL;
-    const int st =
-        derive_kernel_params(shape, scales, clip, causal, kp, lut_size, kv_heads, kv_capacity, prob_bits);
+    const int st = derive_kernel_params(shape, scales, clip, causal, kp, lut_size, kv_heads, kv_capacity,
+                                        prob_bits, lut_bits);
     if (st != INTATTN_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return INTATTN_E_ALIGN;
     return INTATTN_OK;
@@ -132,9 +136,10 @@ extern "C" int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t
     const int kv_heads = variant ? variant->kv_heads : 0;
     const int kv_capacity = variant ? variant->kv_capacity : 0;
     const int prob_bits = variant && variant->prob_bits != 0 ? variant->prob_bits : 8;
+    const int lut_bits = variant && variant->lut_bits != 0 ? variant->lut_bits : 16;
     IaKernelParams kp;
-    const int st =
-        prepare(q, k, v, out, shape, scales, clip, causal, &kp, lut_size, kv_heads, kv_capacity, prob_bits);
+    const int st = prepare(q, k, v, out, shape, scales, clip, causal, &kp, lut_size, kv_heads, kv_capacity,
+                           prob_bits, lut_bits);
     if (st != INTATTN_OK) return st;
     if (rows_of(kp) == 0) return INTATTN_OK;
     ia::clear_pending_hip_error();

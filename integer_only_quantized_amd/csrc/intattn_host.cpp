@@ -6,7 +6,10 @@
 // normalisation; the widths below are this library's fixed reading of them
 // (stated in include/intattn.h). Finer tables of 64 or 128 entries (the
 // pages' "Limitations & Future Work", lookup-table granularity) change only
-// the bin width clip/(N-1) and the table. All arithmetic is IEEE binary64 from float32
+// the bin width clip/(N-1) and the table; a table of uint8 entries (the
+// narrow end of the same section's accuracy/memory trade) reaches the
+// kernels as 128 times its entries, which leaves every probability unchanged
+// (the identity is stated in include/intattn.h). All arithmetic is IEEE binary64 from float32
 // inputs with correctly rounded operations only; the file is compiled with
 // -ffp-contract=off so no multiply-add is fused, and rint() (round half to
 // even in the default rounding mode) is the only rounding used.
@@ -20,7 +23,9 @@
 namespace {
 
 constexpr int kLutSize = 32;
-constexpr double kLutOne = 32768.0;
+constexpr double kLutOne = 32768.0;   // Q15 entry for a zero relative score
+constexpr double kLut8One = 255.0;    // uint8 entry for a zero relative score
+constexpr int kLut8Scale = 128;       // uint8 entries in Q15 units
 constexpr int kIdxShift = 24;
 constexpr int kReqFrac = 31;
 
@@ -40,12 +45,15 @@ struct NearestRounding {
 };
 
 bool valid_lut_size(int n) { return n == 32 || n == 64 || n == 128; }
+bool valid_lut_bits(int b) { return b == 16 || b == 8; }
 
-// Entries k < n-1: rint(2^15 exp(-k clip/(n-1))); entry n-1: 0 (the sparse tail).
-void fill_lut(double clip, int n, uint16_t* lut) {
+// Entries k < n-1: rint(one * exp(-k clip/(n-1))), one = 2^15 (16-bit
+// entries) or 255 (8-bit); entry n-1: 0 (the sparse tail).
+void fill_lut(double clip, int n, int bits, uint16_t* lut) {
+    const double one = bits == 8 ? kLut8One : kLutOne;
     const double delta = clip / static_cast<double>(n - 1);
     for (int k = 0; k < n - 1; ++k) {
-        const double v = std::rint(kLutOne * std::exp(-(static_cast<double>(k) * delta)));
+        const double v = std::rint(one * std::exp(-(static_cast<double>(k) * delta)));
         lut[k] = static_cast<uint16_t>(v);
     }
     lut[n - 1] = 0;
@@ -57,16 +65,16 @@ extern "C" int intattn_build_lut(float clip, uint16_t lut_out[32]) {
     if (!lut_out) return INTATTN_E_NULL;
     if (!finite_positive(clip)) return INTATTN_E_CLIP;
     NearestRounding guard;
-    fill_lut(static_cast<double>(clip), kLutSize, lut_out);
+    fill_lut(static_cast<double>(clip), kLutSize, 16, lut_out);
     return INTATTN_OK;
 }
 
-extern "C" int intattn_build_lut_ex(float clip, int32_t lut_size, uint16_t* lut_out) {
+extern "C" int intattn_build_lut_ex(float clip, int32_t lut_size, int32_t lut_bits, uint16_t* lut_out) {
     if (!lut_out) return INTATTN_E_NULL;
-    if (!valid_lut_size(lut_size)) return INTATTN_E_RANGE;
+    if (!valid_lut_size(lut_size) || !valid_lut_bits(lut_bits)) return INTATTN_E_RANGE;
     if (!finite_positive(clip)) return INTATTN_E_CLIP;
     NearestRounding guard;
-    fill_lut(static_cast<double>(clip), lut_size, lut_out);
+    fill_lut(static_cast<double>(clip), lut_size, lut_bits, lut_out);
     return INTATTN_OK;
 }
 
@@ -85,9 +93,9 @@ int intattn_validate_shape(const intattn_shape* s, int causal) {
 
 int intattn_derive_core(const intattn_shape* shape, const intattn_scales* sc, float clip, int lut_size,
                         uint16_t* lut, int32_t* idx_mul, int32_t* x_clip, int32_t* req_shift, int64_t* req_mul,
-                        int prob_bits) {
+                        int prob_bits, int lut_bits) {
     if (!shape || !sc || !lut || !idx_mul || !x_clip || !req_shift || !req_mul) return INTATTN_E_NULL;
-    if (!valid_lut_size(lut_size)) return INTATTN_E_RANGE;
+    if (!valid_lut_size(lut_size) || !valid_lut_bits(lut_bits)) return INTATTN_E_RANGE;
     if (prob_bits != 8 && prob_bits != 16) return INTATTN_E_RANGE;
     if (shape->D < 1) return INTATTN_E_SHAPE;
     if (!finite_positive(sc->q) || !finite_positive(sc->k) || !finite_positive(sc->v) ||
@@ -121,7 +129,9 @@ int intattn_derive_core(const intattn_shape* shape, const intattn_scales* sc, fl
     const int sh_o = kReqFrac - e_o;
     if (sh_o < 1 || sh_o > 63) return INTATTN_E_RANGE;
 
-    fill_lut(c, n, lut);
+    fill_lut(c, n, lut_bits, lut);
+    if (lut_bits == 8)
+        for (int i = 0; i < n; ++i) lut[i] = static_cast<uint16_t>(lut[i] * kLut8Scale);
     *idx_mul = static_cast<int32_t>(M);
     *x_clip = static_cast<int32_t>((num + M - 1) / M);
     *req_shift = sh_o;
@@ -142,14 +152,16 @@ extern "C" int intattn_derive_params(const intattn_shape* shape, const intattn_s
 }
 
 extern "C" int intattn_derive_params_ex(const intattn_shape* shape, const intattn_scales* sc, float clip,
-                                        int32_t lut_size, int32_t prob_bits, intattn_params_ex* out) {
+                                        int32_t lut_size, int32_t prob_bits, int32_t lut_bits,
+                                        intattn_params_ex* out) {
     if (!shape || !sc || !out) return INTATTN_E_NULL;
     intattn_params_ex p{};
     const int st = intattn_derive_core(shape, sc, clip, lut_size, p.lut, &p.idx_mul, &p.x_clip, &p.req_shift,
-                                       &p.req_mul, prob_bits);
+                                       &p.req_mul, prob_bits, lut_bits);
     if (st != INTATTN_OK) return st;
     p.lut_size = lut_size;
     p.prob_bits = prob_bits;
+    p.lut_bits = lut_bits;
     p.idx_shift = kIdxShift;
     *out = p;
     return INTATTN_OK;

@@ -33,12 +33,13 @@ struct IaKernelParams {
 };
 
 // Host derivation of every integer the kernels receive, for a table of
-// lut_size entries (32, 64 or 128): the exp table, M, the clip point and the
+// lut_size entries (32, 64 or 128) of lut_bits bits (16 or 8): the exp
+// table in Q15 units (8-bit entries times 128), M, the clip point and the
 // requantisation pair. Errors as intattn_derive_params (E_RANGE also for an
-// unsupported lut_size).
+// unsupported lut_size, prob_bits or lut_bits).
 int intattn_derive_core(const intattn_shape* shape, const intattn_scales* sc, float clip, int lut_size,
                         uint16_t* lut, int32_t* idx_mul, int32_t* x_clip, int32_t* req_shift, int64_t* req_mul,
-                        int prob_bits = 8);
+                        int prob_bits = 8, int lut_bits = 16);
 
 namespace ia {
 

@@ -82,6 +82,32 @@ def test_params_equal_oracle_sweep():
 @pytest.mark.parametrize("clip", CLIPS[:6])
 def test_fine_lut_equals_oracle(n, clip):
     assert B.build_lut_ex(clip, n) == list(O.build_lut(clip, n))
+    assert B.build_lut_ex(clip, n, 8) == list(O.build_lut(clip, n, 8))
+
+
+@pytest.mark.parametrize("n", [32, 64, 128])
+def test_uint8_table_params_equal_oracle(n):
+    """lut_bits = 8: the kernels' table is 128 times the oracle's uint8
+    entries; every other parameter equals the 16-bit derivation's."""
+    rng = np.random.default_rng(70 + n)
+    checked = 0
+    for D in (64, 128):
+        for _ in range(120):
+            sq, sk, sv, so = (float(np.float32(10 ** rng.uniform(-3.0, 0.0))) for _ in range(4))
+            clip = float(np.float32(rng.uniform(0.5, 12.0)))
+            pb = int(rng.choice([8, 16]))
+            try:
+                ref = O.derive_params(D, sq, sk, sv, so, clip, n, pb, 8)
+            except O.OracleRangeError:
+                with pytest.raises(B.IntAttnError):
+                    B.derive_params_ex(D, (sq, sk, sv, so), clip, n, pb, 8)
+                continue
+            got = B.derive_params_ex(D, (sq, sk, sv, so), clip, n, pb, 8)
+            assert got["lut"] == [128 * e for e in ref.lut] and got["lut_bits"] == 8
+            assert (got["idx_mul"], got["x_clip"]) == (ref.idx_mul, ref.x_clip)
+            assert (got["req_mul"], got["req_shift"]) == (ref.req_mul, ref.req_shift)
+            checked += 1
+    assert checked > 100
 
 
 @pytest.mark.parametrize("n", [64, 128])
@@ -120,8 +146,8 @@ def test_variant_validation_before_any_device_call():
     sc = B.Scales(0.05, 0.05, 0.05, 0.05)
     rm = ctypes.c_void_p(0x5000)
 
-    def call(lut_size, kv_heads, row_max=None, row_sum=None, prob_bits=0):
-        var = B.Variant(lut_size, kv_heads, 0, prob_bits)
+    def call(lut_size, kv_heads, row_max=None, row_sum=None, prob_bits=0, lut_bits=0):
+        var = B.Variant(lut_size, kv_heads, 0, prob_bits, lut_bits)
         return B._lib.intattn_forward_ex(0x1000, 0x2000, 0x3000, 0x4000, ctypes.byref(sh), ctypes.byref(sc),
                                          O.DEFAULT_CLIP, 0, ctypes.byref(var), None, row_max, row_sum)
     for bad in (16, 33, 96, 256, -32):
@@ -131,14 +157,20 @@ def test_variant_validation_before_any_device_call():
     assert call(64, 2, row_max=rm) == E["INTATTN_E_NULL"]
     for bad in (4, 12, 32, -8):
         assert call(32, 0, prob_bits=bad) == E["INTATTN_E_RANGE"]
-    assert B._lib.intattn_build_lut_ex(O.DEFAULT_CLIP, 48, None) == E["INTATTN_E_NULL"]
+    for bad in (4, 12, 32, -8):
+        assert call(32, 0, lut_bits=bad) == E["INTATTN_E_RANGE"]
+    assert B._lib.intattn_build_lut_ex(O.DEFAULT_CLIP, 48, 16, None) == E["INTATTN_E_NULL"]
     buf = (ctypes.c_uint16 * 128)()
-    assert B._lib.intattn_build_lut_ex(O.DEFAULT_CLIP, 48, buf) == E["INTATTN_E_RANGE"]
+    assert B._lib.intattn_build_lut_ex(O.DEFAULT_CLIP, 48, 16, buf) == E["INTATTN_E_RANGE"]
+    for bad in (0, 4, 12, 32):
+        assert B._lib.intattn_build_lut_ex(O.DEFAULT_CLIP, 32, bad, buf) == E["INTATTN_E_RANGE"]
     # a 128-entry table raises mu fourfold over 32 entries: scales that fit 32 entries may not fit 128
     assert B._lib.intattn_derive_params_ex(ctypes.byref(B.Shape(1, 1, 1, 1, 128)), ctypes.byref(B.Scales(0.8, 0.64, 0.4, 0.05)),
-                                           O.DEFAULT_CLIP, 128, 8, ctypes.byref(B.ParamsEx())) == E["INTATTN_E_RANGE"]
-    assert B._lib.intattn_derive_params_ex(ctypes.byref(B.Shape(1, 1, 1, 1, 64)), ctypes.byref(B.Scales(0.05, 0.05, 0.05, 0.05)),
-                                           O.DEFAULT_CLIP, 32, 12, ctypes.byref(B.ParamsEx())) == E["INTATTN_E_RANGE"]
+                                           O.DEFAULT_CLIP, 128, 8, 16, ctypes.byref(B.ParamsEx())) == E["INTATTN_E_RANGE"]
+    for pb, lb in ((12, 16), (8, 12), (8, 0)):
+        assert B._lib.intattn_derive_params_ex(ctypes.byref(B.Shape(1, 1, 1, 1, 64)),
+                                               ctypes.byref(B.Scales(0.05, 0.05, 0.05, 0.05)), O.DEFAULT_CLIP, 32,
+                                               pb, lb, ctypes.byref(B.ParamsEx())) == E["INTATTN_E_RANGE"]
 
 
 def test_kv_append_validation_before_any_device_call():

@@ -1,7 +1,8 @@
 """Seeded random sweep over shapes and variants, GPU against the oracle.
 
 Each case draws B, H, a K/V head count dividing H, Sq, Skv (and a cache
-capacity at least Skv), d, causal, the table size and the probability width,
+capacity at least Skv), d, causal, the table size, the probability width and
+the table's entry width (Q15 or uint8),
 so that every kernel (short rows, long rows, decode, with one or two query
 heads a workgroup) and the edges between them are met: ragged query groups
 and key blocks, a single key, a single query row, keys just past a block or
@@ -47,7 +48,8 @@ def _case(i):
     lut = int(rng.choice([32, 32, 64, 128]))
     prob_bits = int(rng.choice([8, 8, 16]))
     kind = KINDS[i % 3]
-    return B, H, Hkv, Sq, Skv, cap, D, causal, lut, prob_bits, kind
+    lut_bits = int(rng.choice([16, 16, 8]))
+    return B, H, Hkv, Sq, Skv, cap, D, causal, lut, prob_bits, kind, lut_bits
 
 
 CASES = [_case(i) for i in range(40)]
@@ -63,24 +65,24 @@ def _eq(name, got, ref):
 
 @pytest.mark.parametrize("i", range(len(CASES)))
 def test_random_shape_bit_exact(i):
-    B, H, Hkv, Sq, Skv, cap, D, causal, lut, prob_bits, kind = CASES[i]
+    B, H, Hkv, Sq, Skv, cap, D, causal, lut, prob_bits, kind, lut_bits = CASES[i]
     print(f"case {i}: B={B} H={H} Hkv={Hkv} Sq={Sq} Skv={Skv} cap={cap} D={D} causal={causal} "
-          f"lut={lut} prob_bits={prob_bits} kind={kind}", flush=True)
+          f"lut={lut} prob_bits={prob_bits} kind={kind} lut_bits={lut_bits}", flush=True)
     w = W.make_random(B, H, Sq, cap, D, False, 9100 + i, kind, name="sweep")
     k = np.ascontiguousarray(w.k[:, :Hkv])
     v = np.ascontiguousarray(w.v[:, :Hkv])
     try:
         ref, m, E, _ = O.forward(w.q, k[:, :, :Skv], v[:, :, :Skv], w.scales, O.DEFAULT_CLIP, causal,
-                                 stats=True, lut_size=lut, kv_heads=Hkv, prob_bits=prob_bits)
+                                 stats=True, lut_size=lut, kv_heads=Hkv, prob_bits=prob_bits, lut_bits=lut_bits)
     except O.OracleRangeError:
         with pytest.raises(IA.IntAttnError):
             IA.forward_ex(torch.from_numpy(w.q).cuda(), torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
-                          w.scales, O.DEFAULT_CLIP, causal, lut, skv=Skv, prob_bits=prob_bits)
+                          w.scales, O.DEFAULT_CLIP, causal, lut, skv=Skv, prob_bits=prob_bits, lut_bits=lut_bits)
         return
     out, rm, rs = IA.forward_ex(torch.from_numpy(w.q).cuda(), torch.from_numpy(k).cuda(),
                                 torch.from_numpy(v).cuda(), w.scales, O.DEFAULT_CLIP, causal, lut, stats=True,
-                                skv=Skv, prob_bits=prob_bits)
+                                skv=Skv, prob_bits=prob_bits, lut_bits=lut_bits)
     torch.cuda.synchronize()
     _eq("out", out.cpu().numpy(), ref)
     _eq("row_max", rm.cpu().numpy(), m)
-    _eq("row_sum", rs.cpu().numpy().view(np.uint32), E)
+    _eq("row_sum", rs.cpu().numpy().view(np.uint32), E * (128 if lut_bits == 8 else 1))   # Q15 units

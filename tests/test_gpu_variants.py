@@ -177,3 +177,66 @@ def test_uint16_probabilities_single_key_returns_v():
     out = IA.forward_ex(_dev(q), _dev(k), _dev(v), (0.02, 0.02, 0.01, 0.01), O.DEFAULT_CLIP, False, 32, prob_bits=16)
     torch.cuda.synchronize()
     _eq("single key", out.cpu().numpy(), v)
+
+
+# ---------------------------------------------------------------------------
+# uint8 table entries (reach the kernels as 128 e8 in the Q15 slots)
+# ---------------------------------------------------------------------------
+LUT8_CASES = [
+    # (B, H, Hkv, Sq, Skv, D, causal, lut, prob_bits, seed, kind): short rows,
+    # long rows and decode (one and two query heads a workgroup), uint8 and
+    # uint16 probabilities
+    (2, 2, 2, 128, 128, 64, False, 32, 8, 700, "normal"),
+    (1, 2, 2, 197, 197, 64, False, 32, 8, 701, "channel_outliers"),
+    (1, 2, 2, 100, 256, 128, True, 64, 8, 702, "student_t_tail"),
+    (1, 2, 2, 300, 1100, 128, True, 32, 8, 703, "normal"),
+    (1, 4, 2, 257, 700, 64, False, 128, 8, 704, "channel_outliers"),
+    (4, 2, 2, 1, 3000, 128, False, 32, 8, 705, "normal"),
+    (16, 32, 8, 1, 3000, 128, False, 32, 8, 706, "student_t_tail"),
+    (1, 2, 2, 300, 1100, 128, True, 32, 16, 707, "normal"),
+    (4, 8, 2, 1, 4096, 128, False, 64, 16, 708, "channel_outliers"),
+]
+
+
+def _run8(q, k, v, scales, causal, lut, prob_bits, label):
+    Hkv = k.shape[1]
+    _say(f"case {label} q={q.shape} kv={k.shape} causal={causal} lut={lut} prob_bits={prob_bits} lut_bits=8")
+    out, rm, rs = IA.forward_ex(_dev(q), _dev(k), _dev(v), scales, O.DEFAULT_CLIP, causal, lut, stats=True,
+                                prob_bits=prob_bits, lut_bits=8)
+    torch.cuda.synchronize()
+    ref, m, E8, _ = O.forward(q, k, v, scales, O.DEFAULT_CLIP, causal, stats=True, lut_size=lut, kv_heads=Hkv,
+                              prob_bits=prob_bits, lut_bits=8)
+    rs = rs.cpu().numpy().view(np.uint32)
+    _eq(f"{label} out", out.cpu().numpy(), ref)
+    _eq(f"{label} row_max", rm.cpu().numpy(), m)
+    _eq(f"{label} row_sum", rs, 128 * E8)        # the row sum in Q15 units
+    return rs
+
+
+@pytest.mark.parametrize("B,H,Hkv,Sq,Skv,D,causal,lut,prob_bits,seed,kind", LUT8_CASES)
+def test_uint8_table_bit_exact(B, H, Hkv, Sq, Skv, D, causal, lut, prob_bits, seed, kind):
+    w = W.make_random(B, H, Sq, Skv, D, causal, seed, kind, name="lut8")
+    k = np.ascontiguousarray(w.k[:, :Hkv])
+    v = np.ascontiguousarray(w.v[:, :Hkv])
+    _run8(w.q, k, v, w.scales, causal, lut, prob_bits, "lut8")
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,D,prob_bits", [
+    (2, 2, 64, 300, 64, 8), (1, 2, 100, 256, 128, 8), (1, 2, 300, 1100, 128, 8),
+    (4, 4, 1, 1000, 128, 8), (1, 2, 300, 1100, 128, 16), (4, 4, 1, 1000, 64, 16)])
+def test_uint8_table_one_hot_rows(B, H, Sq, Skv, D, prob_bits):
+    """Every row has one key far above the rest (a key equal to 127 times the
+    signs of its query, every other key within +-2), so every other key is
+    clipped and E8 = 255: the smallest row sum, where the short-row kernel's
+    reciprocal reaches 2^16 and is clamped. Bit-exact, and every row sum is
+    128 * 255."""
+    rng = np.random.default_rng(710 + Skv + D)
+    q = rng.integers(-127, 128, (B, H, Sq, D)).astype(np.int8)
+    q[q == 0] = 1
+    k = rng.integers(-2, 3, (B, H, Skv, D)).astype(np.int8)
+    hot = rng.permutation(Skv)[:Sq]
+    for i in range(Sq):
+        k[:, :, hot[i]] = (127 * np.sign(q[:, :, i])).astype(np.int8)
+    v = rng.integers(-127, 128, (B, H, Skv, D)).astype(np.int8)
+    rs = _run8(q, k, v, (0.02, 0.02, 0.05, 0.05), False, 32, prob_bits, "lut8 one-hot")
+    assert (rs == 128 * 255).all()
