@@ -4,6 +4,7 @@
 // Method: IntAttention digest pages (arXiv 2511.21513v1), "Methodology",
 // steps 2-3; integer widths and roundings as stated in include/intattn.h.
 #include "ia_device.h"
+#include "ia_launch.h"
 
 namespace ia {
 namespace {
@@ -321,13 +322,10 @@ int launch_decode_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* o
                     hipStream_t stream, unsigned blocks, int skv_pad, int32_t* row_max, uint32_t* row_sum) {
     constexpr int kBytesPerKey = P16 ? 6 : 5 * QH;     // int32 score/slot + uint8 or uint16 p, per query head
     constexpr int kMaxKeys = QH == 1 ? kDecodeMaxKeys : kDecodeMaxKeys / 2;
-    static bool attr = false;
-    if (!attr) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_decode_kernel<D, P16, QH>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kBytesPerKey * kMaxKeys) != hipSuccess)
-            return INTATTN_E_HIP;
-        attr = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const int st = ensure_dynamic_lds(reinterpret_cast<const void*>(&ia_decode_kernel<D, P16, QH>),
+                                      kBytesPerKey * kMaxKeys, lds_set);
+    if (st != INTATTN_OK) return st;
     const size_t shm = static_cast<size_t>(skv_pad) * kBytesPerKey;
     hipLaunchKernelGGL((ia_decode_kernel<D, P16, QH>), dim3(blocks), dim3(kDecodeThreads * QH), shm, stream, q, k, v, out,
                        kp, skv_pad, row_max, row_sum);

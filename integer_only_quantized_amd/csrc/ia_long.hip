@@ -45,6 +45,7 @@
 #include <type_traits>
 
 #include "ia_device.h"
+#include "ia_launch.h"
 
 namespace ia {
 namespace {
@@ -412,14 +413,11 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
 template <int D, int KM, bool P16>
 int launch_long_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, const IaKernelParams& kp,
                   hipStream_t s, int nqb, unsigned blocks, int32_t* row_max, uint32_t* row_sum) {
-    static bool attr_set = false;
+    static std::atomic<uint64_t> lds_set{0};
     const size_t shm = sizeof(LongLds<D>);
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ia_long_kernel<D, KM, P16>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)) != hipSuccess)
-            return INTATTN_E_HIP;
-        attr_set = true;
-    }
+    const int st = ensure_dynamic_lds(reinterpret_cast<const void*>(&ia_long_kernel<D, KM, P16>),
+                                      static_cast<int>(shm), lds_set);
+    if (st != INTATTN_OK) return st;
     hipLaunchKernelGGL((ia_long_kernel<D, KM, P16>), dim3(blocks), dim3(256), shm, s, q, k, v, out, kp, nqb,
                        row_max, row_sum);
     return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;

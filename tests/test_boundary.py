@@ -288,3 +288,38 @@ def test_stage_empty_problems_are_noops():
         assert _stage(fn, shape=(0, 12, 512, 512, 64), ptrs=(0x1000, 0x2000, 0x3000, 0x4000)) == 0, fn
         assert _stage(fn, shape=(2, 3, 0, 7, 128), ptrs=(0x1000, 0x2000, 0x3000, 0x4000)) == 0, fn
 
+
+
+def test_parameter_derivation_from_many_threads():
+    """The host derivation keeps no shared state (the rounding-mode guard is
+    per thread): eight threads deriving at once get the oracle's integers."""
+    import threading
+    rng = np.random.default_rng(91)
+    sets = []
+    for _ in range(40):
+        sq, sk, sv, so = (float(np.float32(10 ** rng.uniform(-2.5, -0.5))) for _ in range(4))
+        n = int(rng.choice([32, 64, 128]))
+        lb = int(rng.choice([16, 8]))
+        try:
+            ref = O.derive_params(64, sq, sk, sv, so, O.DEFAULT_CLIP, n, 8, lb)
+        except O.OracleRangeError:
+            continue
+        sets.append(((sq, sk, sv, so), n, lb, ref))
+    assert len(sets) > 20
+    bad = []
+
+    def worker():
+        for _ in range(25):
+            for sc, n, lb, ref in sets:
+                got = B.derive_params_ex(64, sc, O.DEFAULT_CLIP, n, 8, lb)
+                want = [e * (128 if lb == 8 else 1) for e in ref.lut]
+                if (got["lut"], got["idx_mul"], got["req_mul"], got["req_shift"]) != \
+                        (want, ref.idx_mul, ref.req_mul, ref.req_shift):
+                    bad.append((sc, n, lb))
+                    return
+    threads = [threading.Thread(target=worker) for _ in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:3]
