@@ -32,6 +32,10 @@
  * symmetric range [-127, 127]; the library does not read device data to check
  * this.
  *
+ * Devices and streams: every launch goes to the calling thread's current
+ * HIP device, and `stream` (NULL: the null stream) must belong to it; the
+ * tensors must be memory that device can read and write.
+ *
  * Ownership: all tensor pointers are caller-owned device memory and must stay
  * valid until the work queued on `stream` has finished. Structs are
  * caller-owned host memory read during the call only. The library keeps no

@@ -201,8 +201,13 @@ def _check_tensors(q, k, v, grouped: bool = False):
 
 def _stream(q):
     """Raw handle of the current stream of q's device (what the C entry point
-    takes); torch's raw accessor when present, else the public Stream object."""
+    takes); torch's raw accessor when present, else the public Stream object.
+    The library launches on the calling thread's current device, so q must
+    live there."""
     import torch
+    if q.device.index is not None and q.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensors are on {q.device} but the current device is cuda:{torch.cuda.current_device()}; "
+                         "call under torch.cuda.device(tensor.device)")
     raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
     if raw is not None:
         return raw(q.device.index)

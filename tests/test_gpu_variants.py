@@ -148,6 +148,10 @@ P16_CASES = [
     (4, 8, 2, 1, 8192, 128, False, 32, 604, "normal"),
     (2, 2, 2, 1, 3001, 64, False, 64, 605, "channel_outliers"),
     (1, 2, 1, 1, 777, 128, True, 128, 606, "normal"),
+    # the decode kernel's largest key count (96 KB of LDS with uint16 P), and
+    # one key past it (a single query row on the long-row kernel)
+    (1, 2, 2, 1, 16384, 128, False, 32, 608, "normal"),
+    (1, 2, 1, 1, 16385, 64, False, 32, 609, "student_t_tail"),
 ]
 
 
