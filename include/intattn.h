@@ -8,7 +8,10 @@
  * table, sums the pseudo-exponents in int32, and scales them by an integer
  * reciprocal (multiply + right shift) into uint8 probabilities; the uint8
  * probabilities multiply int8 V; the int32 result is requantised to int8.
- * No floating point is used on the device.
+ * No floating point is used on the device: the integer divisions (each row's
+ * reciprocal, the split of a workgroup index into head and query block) run
+ * on integer instructions as well. The float32 comparator and the cache
+ * update below take float inputs by definition.
  *
  * Integer specification (the pages leave every width and rounding open; this
  * is the reading the library implements, bit for bit):

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kDecodeThreads * QH) void ia_decode_kernel(
     // each K and V chunk once for both
     const int bid = P.kv_group > QH ? xcd_local_block(blockIdx.x, gridDim.x) : static_cast<int>(blockIdx.x);
     const size_t head0 = static_cast<size_t>(bid) * QH;
-    const size_t kvhead = static_cast<size_t>(head0 / P.kv_group);
+    const size_t kvhead = divmod_invariant(static_cast<uint32_t>(head0), P.kvg_div).q;
     const int8_t* kh = k + kvhead * P.kv_rows * D;
     const int8_t* vh = v + kvhead * P.kv_rows * D;
     v4i qv[QH];
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kDecodeThreads * QH) void ia_decode_kernel(
         E[h] = 0;
 #pragma unroll
         for (int w = 0; w < NW; ++w) E[h] += static_cast<uint32_t>(s_scal[h][NW + w]);
-        R[h] = P16 ? reciprocal16(E[h]) : ((255u << 23) + (E[h] >> 1)) / E[h];
+        R[h] = P16 ? reciprocal16(E[h]) : reciprocal8(E[h]);
         if (row_max != nullptr && tid == 0) {
             row_max[head0 + h] = m[h];
             row_sum[head0 + h] = E[h];

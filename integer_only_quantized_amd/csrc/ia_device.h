@@ -14,6 +14,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "ia_intdiv.h"
 #include "intattn_internal.h"
 
 namespace ia {
@@ -393,10 +394,27 @@ __device__ __forceinline__ void pack_bytes_32(uint32_t w0, uint32_t w1, uint32_t
     hi = __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// Every row that exists has E >= 128 * 255 (its max key alone contributes the
+// first table entry, 2^15 or 128 * 255), so the row reciprocals below take
+// E at least that (a row that does not exist, and is never stored, may have
+// E = 0) and divide with the 24-bit row division.
+constexpr uint32_t kRowSumMin = 128u * 255u;
+
+// Row reciprocal R = floor((255 * 2^23 + floor(E/2)) / E) for E < 2^31 (the
+// numerator stays below 2^32), by integer division.
+__device__ __forceinline__ uint32_t reciprocal8(uint32_t E) {
+    const uint32_t e = max(E, kRowSumMin);
+    return udiv_row((255u << 23) + (e >> 1), e);
+}
+
 // R16 = floor((65535 * 2^16 + floor(E/2)) / E) (below 2^18 for E >= 128*255,
-// a 24-bit operand).
+// a 24-bit operand): with 65535 * 2^16 = q E + r, adding floor(E/2) < E
+// carries into the quotient at most once.
 __device__ __forceinline__ uint32_t reciprocal16(uint32_t E) {
-    return static_cast<uint32_t>((0xFFFF0000ull + (E >> 1)) / E);
+    const uint32_t e = max(E, kRowSumMin);
+    const uint32_t q = udiv_row(0xFFFF0000u, e);
+    const uint32_t r = 0xFFFF0000u - q * e;
+    return q + (r + (e >> 1) >= e ? 1u : 0u);
 }
 
 }  // namespace ia

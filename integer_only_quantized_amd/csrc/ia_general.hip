@@ -39,7 +39,7 @@ constexpr int kVtStride = kKeyTile + 16;          // bytes per transposed V row 
 template <int D, bool kDebug>
 __global__ __launch_bounds__(256) void ia_general_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, const int8_t* __restrict__ v,
-    int8_t* __restrict__ out, const IaKernelParams P, int nqb,
+    int8_t* __restrict__ out, const IaKernelParams P, InvariantDiv nqb_div,
     int32_t* __restrict__ row_max, uint32_t* __restrict__ row_sum, uint8_t* __restrict__ probs) {
     constexpr int KS = D / 32;       // 32-deep k-steps of the Q.K^T contraction
     constexpr int DB = D / 32;       // 32-wide value-column blocks of the output
@@ -55,14 +55,16 @@ __global__ __launch_bounds__(256) void ia_general_kernel(
     const int l32 = lane & 31;
     const int hh = lane >> 5;
 
-    int bid = blockIdx.x;
-    const int qb = bid % nqb;
-    bid /= nqb;
-    const int h = bid % P.H;
-    const int b = bid / P.H;
+    const UDivMod bq = divmod_invariant(blockIdx.x, nqb_div);
+    const int qb = static_cast<int>(bq.r);
+    const UDivMod bh = divmod_invariant(bq.q, P.h_div);
+    const int h = static_cast<int>(bh.r);
+    const int b = static_cast<int>(bh.q);
     const size_t head = static_cast<size_t>(b) * P.H + h;
     const int8_t* qh = q + head * P.Sq * D;
-    const size_t kvhead = static_cast<size_t>(b) * (P.H / P.kv_group) + h / P.kv_group;   // grouped K/V heads
+    // grouped K/V heads: query head h reads K/V head h / kv_group of its batch
+    const uint32_t hkv = divmod_invariant(static_cast<uint32_t>(P.H), P.kvg_div).q;
+    const size_t kvhead = static_cast<size_t>(b) * hkv + divmod_invariant(static_cast<uint32_t>(h), P.kvg_div).q;
     const int8_t* kh = k + kvhead * P.kv_rows * D;
     const int8_t* vh = v + kvhead * P.kv_rows * D;
 
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(256) void ia_general_kernel(
         }
     }
     E += __shfl_xor(E, 32);
-    const uint32_t R = ((255u << 23) + (E >> 1)) / E;
+    const uint32_t R = reciprocal8(E);
 
     if (kDebug && hh == 0 && qrow < P.Sq) {
         row_max[head * P.Sq + qrow] = mrow;
@@ -255,20 +257,21 @@ int launch_general(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* ou
                    uint8_t* probs) {
     const int nqb = (kp.Sq + kQBlock - 1) / kQBlock;
     const long long blocks = static_cast<long long>(nqb) * kp.H * kp.B;
+    const InvariantDiv nqb_div = invariant_div(static_cast<uint32_t>(nqb));
     if (blocks > INT_MAX) return INTATTN_E_SHAPE;
     const dim3 grid(static_cast<unsigned>(blocks)), block(256);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool debug = row_max != nullptr;
     if (D == 64) {
         if (debug)
-            hipLaunchKernelGGL((ia_general_kernel<64, true>), grid, block, 0, s, q, k, v, out, kp, nqb, row_max, row_sum, probs);
+            hipLaunchKernelGGL((ia_general_kernel<64, true>), grid, block, 0, s, q, k, v, out, kp, nqb_div, row_max, row_sum, probs);
         else
-            hipLaunchKernelGGL((ia_general_kernel<64, false>), grid, block, 0, s, q, k, v, out, kp, nqb, row_max, row_sum, probs);
+            hipLaunchKernelGGL((ia_general_kernel<64, false>), grid, block, 0, s, q, k, v, out, kp, nqb_div, row_max, row_sum, probs);
     } else {
         if (debug)
-            hipLaunchKernelGGL((ia_general_kernel<128, true>), grid, block, 0, s, q, k, v, out, kp, nqb, row_max, row_sum, probs);
+            hipLaunchKernelGGL((ia_general_kernel<128, true>), grid, block, 0, s, q, k, v, out, kp, nqb_div, row_max, row_sum, probs);
         else
-            hipLaunchKernelGGL((ia_general_kernel<128, false>), grid, block, 0, s, q, k, v, out, kp, nqb, row_max, row_sum, probs);
+            hipLaunchKernelGGL((ia_general_kernel<128, false>), grid, block, 0, s, q, k, v, out, kp, nqb_div, row_max, row_sum, probs);
     }
     return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
 }

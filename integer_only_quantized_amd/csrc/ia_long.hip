@@ -68,7 +68,7 @@ struct LongLds {
 template <int D, int KM, bool P16>
 __global__ __launch_bounds__(256) void ia_long_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, const int8_t* __restrict__ v,
-    int8_t* __restrict__ out, const IaKernelParams P, int nqb, int32_t* __restrict__ row_max,
+    int8_t* __restrict__ out, const IaKernelParams P, int nqb, InvariantDiv map_div, int32_t* __restrict__ row_max,
     uint32_t* __restrict__ row_sum) {
     using L = LongLds<D>;
     constexpr int KS = D / 32;
@@ -90,19 +90,22 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     int head_i, qb;
     if (P.causal && (nheads & 7) == 0) {
         const int hpx = nheads >> 3, j = bid >> 3;
-        head_i = (bid & 7) + 8 * (j % hpx);
-        qb = nqb - 1 - j / hpx;
+        const UDivMod t = divmod_invariant(static_cast<uint32_t>(j), map_div);   // by hpx
+        head_i = (bid & 7) + 8 * static_cast<int>(t.r);
+        qb = nqb - 1 - static_cast<int>(t.q);
     } else if (P.causal) {
-        head_i = bid % nheads;
-        qb = nqb - 1 - bid / nheads;
+        const UDivMod t = divmod_invariant(static_cast<uint32_t>(bid), map_div);   // by nheads
+        head_i = static_cast<int>(t.r);
+        qb = nqb - 1 - static_cast<int>(t.q);
     } else {
         const int lb = xcd_local_block(bid, static_cast<int>(gridDim.x));
-        qb = lb % nqb;
-        head_i = lb / nqb;
+        const UDivMod t = divmod_invariant(static_cast<uint32_t>(lb), map_div);   // by nqb
+        qb = static_cast<int>(t.r);
+        head_i = static_cast<int>(t.q);
     }
     const size_t head = static_cast<size_t>(head_i);
     const int8_t* qh = q + head * P.Sq * D;
-    const size_t kvhead = static_cast<size_t>(head_i / P.kv_group);   // grouped K/V heads
+    const size_t kvhead = divmod_invariant(static_cast<uint32_t>(head_i), P.kvg_div).q;   // grouped K/V heads
     const int8_t* kh = k + kvhead * P.kv_rows * D;
     const int8_t* vh = v + kvhead * P.kv_rows * D;
 
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     });
     E += __shfl_xor(E, 32);
     // uint8 P: R2 = 2R <= 2^17; uint16 P: R16 < 2^18 (E >= 128*255; both 24-bit operands)
-    const uint32_t R2 = P16 ? reciprocal16(E) : 2 * (((255u << 23) + (E >> 1)) / E);
+    const uint32_t R2 = P16 ? reciprocal16(E) : 2 * reciprocal8(E);
     if (row_max != nullptr && hh == 0 && qrow < P.Sq) {
         row_max[head * P.Sq + qrow] = mrow;
         row_sum[head * P.Sq + qrow] = E;
@@ -418,8 +421,11 @@ int launch_long_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out
     const int st = ensure_dynamic_lds(reinterpret_cast<const void*>(&ia_long_kernel<D, KM, P16>),
                                       static_cast<int>(shm), lds_set);
     if (st != INTATTN_OK) return st;
+    // the divisor of the workgroup -> (head, query block) split the kernel takes
+    const int nheads = kp.B * kp.H;
+    const uint32_t map_d = kp.causal ? ((nheads & 7) == 0 ? nheads >> 3 : nheads) : nqb;
     hipLaunchKernelGGL((ia_long_kernel<D, KM, P16>), dim3(blocks), dim3(256), shm, s, q, k, v, out, kp, nqb,
-                       row_max, row_sum);
+                       invariant_div(map_d), row_max, row_sum);
     return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
 }
 

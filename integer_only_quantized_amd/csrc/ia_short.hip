@@ -87,10 +87,11 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     const int hh = lane >> 5;
 
     const int bid = xcd_local_block(blockIdx.x, static_cast<int>(gridDim.x));
-    const int qb = bid % nqb;
-    const size_t head = static_cast<size_t>(bid / nqb);
+    const UDivMod hq = divmod_invariant(static_cast<uint32_t>(bid), P.qb_div);
+    const int qb = static_cast<int>(hq.r);
+    const size_t head = hq.q;
     const int8_t* qh = q + head * P.Sq * D;
-    const size_t kvhead = static_cast<size_t>(static_cast<int>(head) / P.kv_group);   // grouped K/V heads
+    const size_t kvhead = divmod_invariant(static_cast<uint32_t>(head), P.kvg_div).q;   // grouped K/V heads
     const int8_t* kh = k + kvhead * P.kv_rows * D;
     const int8_t* vh = v + kvhead * P.kv_rows * D;
 
@@ -339,8 +340,7 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     // to the 16-bit operand's 65535 without changing any p: the entries are
     // then multiples of 128, and (e*R + 2^22) >> 23 is e/128 for R = 2^16
     // and for R = 2^16 - 1 alike (e <= 2^15 < 2^22).
-    const uint32_t Ed = SKIP ? max(E, 1u) : E;
-    const uint32_t R = min(((255u << 23) + (Ed >> 1)) / Ed, 65535u);
+    const uint32_t R = min(reciprocal8(E), 65535u);
     if (row_max != nullptr && half == 0 && hh == 0 && qrow < P.Sq) {
         row_max[head * P.Sq + qrow] = mrow;
         row_sum[head * P.Sq + qrow] = E;
@@ -485,9 +485,11 @@ int launch_short_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* ou
     const int tail_rows = kp.Sq % 64;
     const bool skip = kp.causal || (tail_rows != 0 && tail_rows <= 32) || kp.Skv <= 64 * NBH - 32;
     const dim3 grid(static_cast<unsigned>(blocks));
+    IaKernelParams kq = kp;
+    kq.qb_div = invariant_div(static_cast<uint32_t>(nqb));
     auto go = [&](auto skip_c, auto km_c) {
         hipLaunchKernelGGL((ia_short_kernel<D, NBH, decltype(skip_c)::value, decltype(km_c)::value>), grid,
-                           dim3(256), 0, stream, q, k, v, out, kp, nqb, row_max, row_sum);
+                           dim3(256), 0, stream, q, k, v, out, kq, nqb, row_max, row_sum);
     };
     using T = std::true_type;
     using F = std::false_type;

@@ -26,18 +26,31 @@ constexpr int kStageMaxChunks = 64;
 // (queries x keys) on v_mfma_i32_32x32x32_i8 with Q as the A operand: lane
 // (l32, hh) holds key column l32 of 16 query rows, so every store writes 32
 // consecutive int32 of a row per lane half.
+// Query row within its head of stage row 4 * block + w (w < 4), i.e.
+// (4 * block + w) mod Sq, from a 32-bit division of the block index: the
+// remainder r of block by Sq gives 4r + w < 4 Sq, three subtractions at most.
+__device__ __forceinline__ int row_in_head(uint32_t block, int w, int Sq, const InvariantDiv& sq_div) {
+    uint64_t t = 4ull * divmod_invariant(block, sq_div).r + static_cast<uint64_t>(w);
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        if (t >= static_cast<uint64_t>(Sq)) t -= static_cast<uint64_t>(Sq);
+    return static_cast<int>(t);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void ia_qk_kernel(const int8_t* __restrict__ q, const int8_t* __restrict__ k,
-                                                    int32_t* __restrict__ scores, int Sq, int Skv, int nqb,
-                                                    int nkt) {
+                                                    int32_t* __restrict__ scores, int Sq, int Skv,
+                                                    InvariantDiv nqb_div, InvariantDiv nkt_div) {
     constexpr int KS = D / 32;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31;
     const int hh = lane >> 5;
-    const int kt = blockIdx.x % nkt;
-    const int qb = (blockIdx.x / nkt) % nqb;
-    const size_t head = static_cast<size_t>(blockIdx.x / nkt / nqb);
+    const UDivMod bk = divmod_invariant(blockIdx.x, nkt_div);
+    const UDivMod bq = divmod_invariant(bk.q, nqb_div);
+    const int kt = static_cast<int>(bk.r);
+    const int qb = static_cast<int>(bq.r);
+    const size_t head = bq.q;
     const int8_t* qh = q + head * Sq * D;
     const int8_t* kh = k + head * Skv * D;
     const int q0 = qb * 128 + 32 * wave;
@@ -108,7 +121,8 @@ __global__ __launch_bounds__(256) void ia_index_softmax_kernel(const int32_t* __
                                                                uint8_t* __restrict__ probs,
                                                                int32_t* __restrict__ row_max,
                                                                uint32_t* __restrict__ row_sum,
-                                                               const IaKernelParams P, long long rows) {
+                                                               const IaKernelParams P, long long rows,
+                                                               InvariantDiv sq_div) {
     __shared__ uint32_t lut[kIaMaxLut / 2];    // exp table, layout KM
     const int tid = threadIdx.x;
     if (tid < 64) fill_lut_table<KM>(P, lut, tid);   // wave 0, whole
@@ -117,7 +131,7 @@ __global__ __launch_bounds__(256) void ia_index_softmax_kernel(const int32_t* __
     const long long row = static_cast<long long>(blockIdx.x) * 4 + (tid >> 6);
     if (row >= rows) return;
     const int Skv = P.Skv;
-    const int i = static_cast<int>(row % P.Sq);
+    const int i = row_in_head(blockIdx.x, tid >> 6, P.Sq, sq_div);
     const int kend = P.causal ? min(Skv, i + (Skv - P.Sq) + 1) : Skv;
     const int32_t* src = scores + row * Skv;
 
@@ -145,7 +159,7 @@ __global__ __launch_bounds__(256) void ia_index_softmax_kernel(const int32_t* __
         E += e[c];
     }
     E = wave_sum(E);
-    const uint32_t R2 = 2 * (((255u << 23) + (E >> 1)) / E);
+    const uint32_t R2 = 2 * reciprocal8(E);
     uint8_t* dst = probs + row * Skv;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -215,7 +229,8 @@ __device__ __forceinline__ int vc_swz(int key) {
 
 template <int D, bool ALIGNED>
 __global__ __launch_bounds__(256) void ia_pv_kernel(const uint8_t* __restrict__ probs, const int8_t* __restrict__ v,
-                                                    int8_t* __restrict__ out, const IaKernelParams P, int nqb) {
+                                                    int8_t* __restrict__ out, const IaKernelParams P,
+                                                    InvariantDiv nqb_div) {
     constexpr int DB = D / 32;
     constexpr int TB = 64 * D;                   // bytes per V tile
     constexpr int CPR = D / 16;
@@ -228,8 +243,9 @@ __global__ __launch_bounds__(256) void ia_pv_kernel(const uint8_t* __restrict__ 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int hh = lane >> 5;
-    const int qb = blockIdx.x % nqb;
-    const size_t head = static_cast<size_t>(blockIdx.x / nqb);
+    const UDivMod bq = divmod_invariant(blockIdx.x, nqb_div);
+    const int qb = static_cast<int>(bq.r);
+    const size_t head = bq.q;
     const int Sq = P.Sq, Skv = P.Skv;
     const uint8_t* ph = probs + head * Sq * Skv;
     const int8_t* vh = v + head * Skv * D;
@@ -361,13 +377,13 @@ int launch_isoftmax_n(int nch, const int32_t* scores, uint8_t* probs, int32_t* r
             return launch_isoftmax_n<NCH * 2>(nch, scores, probs, row_max, row_sum, kp, s, rows, blocks);
         if (kp.slot_k == 4)
             hipLaunchKernelGGL((ia_index_softmax_kernel<NCH, 4>), dim3(blocks), dim3(256), 0, s, scores, probs,
-                               row_max, row_sum, kp, rows);
+                               row_max, row_sum, kp, rows, invariant_div(static_cast<uint32_t>(kp.Sq)));
         else if (kp.slot_k == 2)
             hipLaunchKernelGGL((ia_index_softmax_kernel<NCH, 2>), dim3(blocks), dim3(256), 0, s, scores, probs,
-                               row_max, row_sum, kp, rows);
+                               row_max, row_sum, kp, rows, invariant_div(static_cast<uint32_t>(kp.Sq)));
         else
             hipLaunchKernelGGL((ia_index_softmax_kernel<NCH, 1>), dim3(blocks), dim3(256), 0, s, scores, probs,
-                               row_max, row_sum, kp, rows);
+                               row_max, row_sum, kp, rows, invariant_div(static_cast<uint32_t>(kp.Sq)));
         return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
     }
 }
@@ -398,10 +414,10 @@ int launch_qk_scores(const int8_t* q, const int8_t* k, int32_t* scores, int D, c
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (D == 64)
         hipLaunchKernelGGL((ia_qk_kernel<64>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, q, k, scores,
-                           kp.Sq, kp.Skv, nqb, nkt);
+                           kp.Sq, kp.Skv, invariant_div(nqb), invariant_div(nkt));
     else
         hipLaunchKernelGGL((ia_qk_kernel<128>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, q, k, scores,
-                           kp.Sq, kp.Skv, nqb, nkt);
+                           kp.Sq, kp.Skv, invariant_div(nqb), invariant_div(nkt));
     return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
 }
 
@@ -425,16 +441,17 @@ int launch_fp_softmax(const int32_t* scores, uint8_t* probs, float alpha, const 
 int launch_pv(const uint8_t* probs, const int8_t* v, int8_t* out, int D, const IaKernelParams& kp, void* stream) {
     const int nqb = (kp.Sq + 127) / 128;
     const long long blocks = static_cast<long long>(kp.B) * kp.H * nqb;
+    const InvariantDiv nqb_div = invariant_div(static_cast<uint32_t>(nqb));
     if (blocks > INT_MAX) return INTATTN_E_SHAPE;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool aligned = (kp.Skv % 16) == 0 && (reinterpret_cast<uintptr_t>(probs) & 15u) == 0;
     const dim3 g(static_cast<unsigned>(blocks));
     if (D == 64) {
-        if (aligned) hipLaunchKernelGGL((ia_pv_kernel<64, true>), g, dim3(256), 0, s, probs, v, out, kp, nqb);
-        else hipLaunchKernelGGL((ia_pv_kernel<64, false>), g, dim3(256), 0, s, probs, v, out, kp, nqb);
+        if (aligned) hipLaunchKernelGGL((ia_pv_kernel<64, true>), g, dim3(256), 0, s, probs, v, out, kp, nqb_div);
+        else hipLaunchKernelGGL((ia_pv_kernel<64, false>), g, dim3(256), 0, s, probs, v, out, kp, nqb_div);
     } else {
-        if (aligned) hipLaunchKernelGGL((ia_pv_kernel<128, true>), g, dim3(256), 0, s, probs, v, out, kp, nqb);
-        else hipLaunchKernelGGL((ia_pv_kernel<128, false>), g, dim3(256), 0, s, probs, v, out, kp, nqb);
+        if (aligned) hipLaunchKernelGGL((ia_pv_kernel<128, true>), g, dim3(256), 0, s, probs, v, out, kp, nqb_div);
+        else hipLaunchKernelGGL((ia_pv_kernel<128, false>), g, dim3(256), 0, s, probs, v, out, kp, nqb_div);
     }
     return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
 }

@@ -68,6 +68,8 @@ int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scale
     kp->slot_k = k;
     kp->slot_k_log2 = k == 4 ? 2 : k - 1;
     kp->kv_group = shape->H > 0 ? shape->H / hkv : 1;
+    kp->kvg_div = ia::invariant_div(static_cast<uint32_t>(kp->kv_group));
+    kp->h_div = ia::invariant_div(static_cast<uint32_t>(shape->H > 0 ? shape->H : 1));
     kp->kv_rows = rows;
     kp->prob_bits = prob_bits;
     for (int i = 0; i < kIaMaxLut / 2; ++i)
@@ -159,6 +161,8 @@ extern "C" int intattn_qk_scores(const int8_t* q, const int8_t* k, int32_t* scor
     kp.Sq = shape->Sq;
     kp.Skv = shape->Skv;
     kp.kv_group = 1;
+    kp.kvg_div = ia::invariant_div(1);
+    kp.h_div = ia::invariant_div(static_cast<uint32_t>(shape->H > 0 ? shape->H : 1));
     kp.kv_rows = shape->Skv;
     kp.prob_bits = 8;
     if (rows_of(kp) == 0) return INTATTN_OK;
@@ -197,6 +201,8 @@ extern "C" int intattn_fp_softmax(const int32_t* scores, uint8_t* probs, const i
     kp.Skv = shape->Skv;
     kp.causal = causal ? 1 : 0;
     kp.kv_group = 1;
+    kp.kvg_div = ia::invariant_div(1);
+    kp.h_div = ia::invariant_div(static_cast<uint32_t>(shape->H > 0 ? shape->H : 1));
     kp.kv_rows = shape->Skv;
     kp.prob_bits = 8;
     if (kp.Skv > ia::stage_max_keys()) return INTATTN_E_SHAPE;

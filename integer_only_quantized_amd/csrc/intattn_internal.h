@@ -5,6 +5,7 @@
 
 #include <cstdint>
 
+#include "ia_intdiv.h"
 #include "intattn.h"
 
 // Shape checks common to every entry point (no device access).
@@ -29,6 +30,9 @@ struct IaKernelParams {
     int32_t kv_group;    // query heads per K/V head (1: one K/V head each)
     int32_t kv_rows;     // rows per K/V head in memory (>= Skv: a cache of that capacity)
     int32_t prob_bits;   // 8: uint8 probabilities; 16: the uint16 variant
+    ia::InvariantDiv kvg_div;   // division by kv_group (query head -> K/V head)
+    ia::InvariantDiv h_div;     // division by H (batch, head of a flat head index)
+    ia::InvariantDiv qb_div;    // division by the launch's query-block count (set by the launcher)
     uint32_t lut2[kIaMaxLut / 2];   // exp table, entries 2i and 2i+1 packed lo/hi
 };
 
