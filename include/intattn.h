@@ -92,7 +92,9 @@ enum {
     INTATTN_E_CLIP  = -5,  /* clip is not finite and > 0                     */
     INTATTN_E_RANGE = -6,  /* mu outside [2^-16, 2^-1) or sh_o outside 1..63 */
     INTATTN_E_HIP   = -7,  /* the HIP runtime reported an error              */
-    INTATTN_E_ALIGN = -8   /* a tensor pointer is not 16-byte aligned        */
+    INTATTN_E_ALIGN = -8,  /* a tensor pointer is not 16-byte aligned        */
+    INTATTN_E_WORKSPACE = -9  /* workspace smaller than intattn_workspace_bytes,
+                                 or not 256-byte aligned                    */
 };
 
 /* The 32-entry exp table for a clip threshold (in logit units): lut_out[k] =
@@ -167,6 +169,13 @@ typedef struct intattn_variant {
                             above) or 16 (uint16 variant); 0 means 8         */
     int32_t lut_bits;    /* table entry width: 16 (Q15, the specification
                             above) or 8 (uint8 entries); 0 means 16          */
+    void*    workspace;  /* device memory, caller-owned, for decode over long
+                            caches (Sq = 1, Skv > 16384): keys are split into
+                            chunks over several workgroups per head (exact:
+                            the row max and sum are combined before any
+                            probability, and the P.V partials are integers).
+                            NULL: those shapes run on the long-row kernel   */
+    uint64_t workspace_bytes; /* size of workspace                           */
 } intattn_variant;
 
 typedef struct intattn_params_ex {
@@ -204,7 +213,16 @@ int intattn_derive_params_ex(const intattn_shape* shape, const intattn_scales* s
  * intattn_forward_debug. Every tensor pointer 16-byte aligned; allocates no
  * device memory. Errors: those of intattn_forward, E_NULL for one of
  * row_max / row_sum without the other, E_SHAPE for kv_heads < 0 or not
- * dividing H or for 0 < kv_capacity < Skv, E_RANGE for lut_size, prob_bits or lut_bits. */
+ * dividing H or for 0 < kv_capacity < Skv, E_RANGE for lut_size, prob_bits or lut_bits,
+ * E_WORKSPACE for a workspace smaller than intattn_workspace_bytes or not
+ * 256-byte aligned. With a workspace, the call may queue several kernels. */
+/* Bytes of workspace intattn_forward_ex uses for this shape and variant
+ * (256-byte aligned; int32 scores per key and head, per-chunk maxima and
+ * sums, per-head accumulators), 0 when the shape does not use one (only
+ * Sq = 1 with Skv > 16384 does). Host only, pure. Returns 0 for an invalid
+ * shape as well. */
+uint64_t intattn_workspace_bytes(const intattn_shape* shape, const intattn_variant* variant);
+
 int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
                        const intattn_shape* shape, const intattn_scales* scales, float clip,
                        int causal, const intattn_variant* variant, void* stream,

@@ -19,7 +19,7 @@ INTATTN_OK = 0
 STATUS_NAMES = {
     0: "INTATTN_OK", -1: "INTATTN_E_NULL", -2: "INTATTN_E_SHAPE", -3: "INTATTN_E_DIM",
     -4: "INTATTN_E_SCALE", -5: "INTATTN_E_CLIP", -6: "INTATTN_E_RANGE", -7: "INTATTN_E_HIP",
-    -8: "INTATTN_E_ALIGN",
+    -8: "INTATTN_E_ALIGN", -9: "INTATTN_E_WORKSPACE",
 }
 DEFAULT_CLIP = float(ctypes.c_float(math.log(510.0)).value)
 
@@ -55,7 +55,8 @@ class ParamsEx(ctypes.Structure):
 
 class Variant(ctypes.Structure):
     _fields_ = [("lut_size", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("kv_capacity", ctypes.c_int32),
-                ("prob_bits", ctypes.c_int32), ("lut_bits", ctypes.c_int32)]
+                ("prob_bits", ctypes.c_int32), ("lut_bits", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_uint64)]
 
 
 def library_path() -> str:
@@ -92,6 +93,8 @@ def _load():
     lib.intattn_forward_ex.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), ctypes.POINTER(Scales), f32, i32,
                                        ctypes.POINTER(Variant), vp, vp, vp]
     lib.intattn_forward_ex.restype = i32
+    lib.intattn_workspace_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Variant)]
+    lib.intattn_workspace_bytes.restype = ctypes.c_uint64
     lib.intattn_kv_append.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp]
     lib.intattn_kv_append.restype = i32
     lib.intattn_qk_scores.argtypes = [vp, vp, vp, ctypes.POINTER(Shape), vp]
@@ -344,14 +347,25 @@ def pv(probs, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False, out=N
     return out
 
 
+def workspace_bytes(B: int, H: int, Sq: int, Skv: int, D: int) -> int:
+    """intattn_workspace_bytes: device workspace forward_ex uses for this shape (0: none)."""
+    return int(_lib.intattn_workspace_bytes(ctypes.byref(Shape(int(B), int(H), int(Sq), int(Skv), int(D))), None))
+
+
 def forward_ex(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False, lut_size: int = 32,
-               stats: bool = False, out=None, skv: int = None, prob_bits: int = 8, lut_bits: int = 16):
+               stats: bool = False, out=None, skv: int = None, prob_bits: int = 8, lut_bits: int = 16,
+               workspace=None):
     """intattn_forward_ex: q [B,H,Sq,D], k and v [B,Hkv,C,D] int8 CUDA tensors
     (Hkv divides H; query head h reads K/V head h // (H // Hkv)); the first
     skv rows of each K/V head are attended (default all C: a cache of capacity
     C holding skv tokens); a table of lut_size entries of lut_bits bits;
-    prob_bits-wide probabilities. Returns out, or (out, row_max, row_sum)
-    with stats (row_sum in Q15 units: 128 times the uint8 table's sum)."""
+    prob_bits-wide probabilities. Decode over a cache longer than the
+    single-workgroup decode kernel takes (Sq = 1, skv > 16384) splits its
+    keys over several workgroups per head in a device workspace: a uint8
+    tensor on q's device of at least workspace_bytes(...) bytes, allocated
+    here when not given (workspace=False: no workspace, the long-row kernel
+    runs). Returns out, or (out, row_max, row_sum) with stats (row_sum in Q15
+    units: 128 times the uint8 table's sum)."""
     import torch
     B, H, Sq, C, D = _check_tensors(q, k, v, grouped=True)
     skv = C if skv is None else int(skv)
@@ -362,6 +376,16 @@ def forward_ex(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False
         raise ValueError("out must be a contiguous int8 tensor shaped like q, on q's device")
     var = Variant(int(lut_size), int(k.shape[1]), int(C), int(prob_bits), int(lut_bits))
     sh, sc = _structs((B, H, Sq, skv, D), scales)
+    if workspace is not False:
+        need = int(_lib.intattn_workspace_bytes(ctypes.byref(sh), ctypes.byref(var)))
+        if need > 0:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            elif (workspace.dtype is not torch.uint8 or not workspace.is_contiguous()
+                  or workspace.device != q.device):
+                raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+            var.workspace = workspace.data_ptr()
+            var.workspace_bytes = workspace.numel()
     rm = rs = None
     if stats:
         rm = torch.empty((B, H, Sq), dtype=torch.int32, device=q.device)

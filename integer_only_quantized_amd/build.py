@@ -42,7 +42,7 @@ def _run(cmd):
 
 
 HOST_SOURCES = ["intattn_host.cpp", "intattn_api.cpp"]
-HIP_SOURCES = ["ia_general.hip", "ia_short.hip", "ia_long.hip", "ia_decode.hip", "ia_stages.hip",
+HIP_SOURCES = ["ia_general.hip", "ia_short.hip", "ia_long.hip", "ia_decode.hip", "ia_decode_split.hip", "ia_stages.hip",
                "ia_kvcache.hip"]
 # Per-source code-generation options: the long- and short-row kernels keep
 # their MFMA accumulators in ordinary VGPRs (no accumulator-register copies

@@ -91,10 +91,17 @@ int prepare(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
 
 long long rows_of(const IaKernelParams& kp) { return static_cast<long long>(kp.B) * kp.H * kp.Sq; }
 
+// Decode shapes past the single-workgroup decode kernel's key limit split
+// their keys over several workgroups when the caller gives a workspace.
+bool uses_split(int Sq, int Skv) { return Sq == 1 && Skv > ia::decode_max_keys(); }
+
 int dispatch(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
-             const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum) {
+             const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum,
+             void* workspace = nullptr) {
     if (kp.Sq == 1 && kp.Skv <= ia::decode_max_keys())
         return ia::launch_decode(q, k, v, out, D, kp, stream, row_max, row_sum);
+    if (workspace != nullptr && uses_split(kp.Sq, kp.Skv))
+        return ia::launch_decode_split(q, k, v, out, D, kp, stream, workspace, row_max, row_sum);
     // uint16 probabilities: the long-row kernel serves every other shape
     if (kp.Skv <= ia::short_max_keys(D) && kp.prob_bits == 8)
         return ia::launch_short(q, k, v, out, D, kp, stream, row_max, row_sum);
@@ -129,6 +136,14 @@ extern "C" int intattn_forward_debug(const int8_t* q, const int8_t* k, const int
     return dispatch(q, k, v, out, shape->D, kp, stream, row_max, row_sum);
 }
 
+extern "C" uint64_t intattn_workspace_bytes(const intattn_shape* shape, const intattn_variant* variant) {
+    (void)variant;   // the workspace does not depend on the table or probability width
+    if (!shape || intattn_validate_shape(shape, 0) != INTATTN_OK) return 0;
+    if (shape->D != 64 && shape->D != 128) return 0;
+    if (!uses_split(shape->Sq, shape->Skv)) return 0;
+    return ia::decode_split_workspace_bytes(static_cast<long long>(shape->B) * shape->H, shape->Skv, shape->D);
+}
+
 extern "C" int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
                                   const intattn_shape* shape, const intattn_scales* scales, float clip,
                                   int causal, const intattn_variant* variant, void* stream, int32_t* row_max,
@@ -143,9 +158,14 @@ extern "C" int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t
     const int st = prepare(q, k, v, out, shape, scales, clip, causal, &kp, lut_size, kv_heads, kv_capacity,
                            prob_bits, lut_bits);
     if (st != INTATTN_OK) return st;
+    void* ws = variant ? variant->workspace : nullptr;
+    if (ws != nullptr && uses_split(shape->Sq, shape->Skv)) {
+        const uint64_t need = intattn_workspace_bytes(shape, variant);
+        if (variant->workspace_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return INTATTN_E_WORKSPACE;
+    }
     if (rows_of(kp) == 0) return INTATTN_OK;
     ia::clear_pending_hip_error();
-    return dispatch(q, k, v, out, shape->D, kp, stream, row_max, row_sum);
+    return dispatch(q, k, v, out, shape->D, kp, stream, row_max, row_sum, ws);
 }
 
 extern "C" int intattn_qk_scores(const int8_t* q, const int8_t* k, int32_t* scores, const intattn_shape* shape,

@@ -178,6 +178,7 @@ extern "C" const char* intattn_strerror(int status) {
         case INTATTN_E_RANGE: return "scales outside the encodable range (index multiplier or output shift)";
         case INTATTN_E_HIP: return "the HIP runtime reported an error";
         case INTATTN_E_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case INTATTN_E_WORKSPACE: return "workspace too small for the shape, or not 256-byte aligned";
         default: return "unknown status";
     }
 }

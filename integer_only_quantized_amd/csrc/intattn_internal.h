@@ -67,6 +67,13 @@ int launch_short(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
 
 // Sq == 1 and Skv <= decode_max_keys(): one head per workgroup, HBM streaming.
 int decode_max_keys();
+
+// Decode over long caches, keys split into chunks over several workgroups
+// per head (Sq = 1): workspace bytes for B*H heads, and the launch (four
+// kernels; the workspace is caller-owned device memory of at least that size).
+size_t decode_split_workspace_bytes(long long heads, int Skv, int D);
+int launch_decode_split(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D, const IaKernelParams& kp,
+                        void* stream, void* workspace, int32_t* row_max, uint32_t* row_sum);
 int launch_decode(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
                   const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum);
 

@@ -25,7 +25,7 @@ B = pytest.importorskip("integer_only_quantized_amd._binding",
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(intattn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:int|uint64_t|const char\*)\s+(intattn_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
                             "intattn_forward_debug", "intattn_strerror", "intattn_qk_scores",
                             "intattn_index_softmax", "intattn_fp_softmax", "intattn_pv",
                             "intattn_build_lut_ex", "intattn_derive_params_ex", "intattn_forward_ex",
-                            "intattn_kv_append"])
+                            "intattn_kv_append", "intattn_workspace_bytes"])
     for n in names:
         assert hasattr(B._lib, n), n
 
@@ -323,3 +323,29 @@ def test_parameter_derivation_from_many_threads():
     for t in threads:
         t.join()
     assert not bad, bad[:3]
+
+
+def test_workspace_size_and_validation_before_any_device_call():
+    """Only decode past the decode kernel's 16384 keys takes a workspace: int32
+    scores per key and head, per-chunk maxima and sums (4096-key chunks) and
+    per-head accumulators, each region 256-byte aligned. A workspace below that
+    size, or not 256-byte aligned, is refused before any device work."""
+    E = {v: k for k, v in B.STATUS_NAMES.items()}
+    al = lambda n: (n + 255) // 256 * 256
+    assert B.workspace_bytes(16, 32, 1, 16384, 128) == 0
+    assert B.workspace_bytes(2, 32, 2, 40000, 128) == 0              # not a decode shape
+    for (b, h, skv, d) in [(16, 32, 16385, 128), (2, 32, 65535, 128), (1, 3, 20000, 64)]:
+        heads, nch = b * h, -(-skv // 4096)
+        assert B.workspace_bytes(b, h, 1, skv, d) == al(heads * skv * 4) + 2 * al(heads * nch * 4) + al(heads * d * 4)
+    assert B.workspace_bytes(1, 1, 1, 65536, 128) == 0               # invalid shape
+    sh = B.Shape(1, 4, 1, 20000, 128)
+    sc = B.Scales(0.05, 0.05, 0.05, 0.05)
+    need = B.workspace_bytes(1, 4, 1, 20000, 128)
+
+    def call(ws, nbytes):
+        var = B.Variant(32, 4, 0, 8, 16, ws, nbytes)
+        return B._lib.intattn_forward_ex(0x1000, 0x2000, 0x3000, 0x4000, ctypes.byref(sh), ctypes.byref(sc),
+                                         O.DEFAULT_CLIP, 0, ctypes.byref(var), None, None, None)
+    assert call(0x10000, need - 1) == E["INTATTN_E_WORKSPACE"]
+    assert call(0x10010, need) == E["INTATTN_E_WORKSPACE"]
+    assert B._lib.intattn_strerror(-9) != B._lib.intattn_strerror(-100)

@@ -244,3 +244,51 @@ def test_uint8_table_one_hot_rows(B, H, Sq, Skv, D, prob_bits):
     v = rng.integers(-127, 128, (B, H, Skv, D)).astype(np.int8)
     rs = _run8(q, k, v, (0.02, 0.02, 0.05, 0.05), False, 32, prob_bits, "lut8 one-hot")
     assert (rs == 128 * 255).all()
+
+
+# ---------------------------------------------------------------------------
+# Decode over long caches: keys split over several workgroups per head
+# ---------------------------------------------------------------------------
+SPLIT_CASES = [
+    # (B, H, Hkv, Skv, D, lut, prob_bits, lut_bits, cap_extra, seed, kind): one key past the
+    # decode kernel's limit, ragged last chunks, the largest cache, grouped
+    # heads, cache prefixes, every table and probability width
+    (2, 4, 4, 16385, 128, 32, 8, 16, 0, 900, "normal"),
+    (1, 2, 2, 65535, 128, 32, 8, 16, 0, 901, "channel_outliers"),
+    (2, 8, 2, 20000, 64, 64, 8, 16, 37, 902, "student_t_tail"),
+    (1, 4, 1, 33000, 128, 128, 16, 16, 0, 903, "normal"),
+    (2, 4, 2, 24577, 64, 32, 16, 8, 100, 904, "channel_outliers"),
+    (1, 2, 2, 40960, 128, 32, 8, 8, 0, 905, "student_t_tail"),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,Skv,D,lut,prob_bits,lut_bits,cap_extra,seed,kind", SPLIT_CASES)
+def test_split_decode_bit_exact(B, H, Hkv, Skv, D, lut, prob_bits, lut_bits, cap_extra, seed, kind):
+    w = W.make_random(B, H, 1, Skv + cap_extra, D, False, seed, kind, name="split")
+    k = np.ascontiguousarray(w.k[:, :Hkv])
+    v = np.ascontiguousarray(w.v[:, :Hkv])
+    _say(f"case split B={B} H={H} Hkv={Hkv} Skv={Skv} cap={Skv + cap_extra} D={D} lut={lut} "
+         f"prob_bits={prob_bits} lut_bits={lut_bits}")
+    assert IA.workspace_bytes(B, H, 1, Skv, D) > 0
+    out, rm, rs = IA.forward_ex(_dev(w.q), _dev(k), _dev(v), w.scales, O.DEFAULT_CLIP, False, lut, stats=True,
+                                skv=Skv, prob_bits=prob_bits, lut_bits=lut_bits)
+    torch.cuda.synchronize()
+    ref, m, E, _ = O.forward(w.q, k[:, :, :Skv], v[:, :, :Skv], w.scales, O.DEFAULT_CLIP, False, stats=True,
+                             lut_size=lut, kv_heads=Hkv, prob_bits=prob_bits, lut_bits=lut_bits)
+    _eq("split out", out.cpu().numpy(), ref)
+    _eq("split row_max", rm.cpu().numpy(), m)
+    _eq("split row_sum", rs.cpu().numpy().view(np.uint32), E * (128 if lut_bits == 8 else 1))
+    # the same call without a workspace (long-row kernel) agrees, and a second
+    # call through the same workspace gives the same result (accumulators cleared)
+    ws = torch.empty(IA.workspace_bytes(B, H, 1, Skv, D), dtype=torch.uint8, device="cuda")
+    qd, kd, vd = _dev(w.q), _dev(k), _dev(v)
+    a = IA.forward_ex(qd, kd, vd, w.scales, O.DEFAULT_CLIP, False, lut, skv=Skv, prob_bits=prob_bits,
+                      lut_bits=lut_bits, workspace=ws)
+    b = IA.forward_ex(qd, kd, vd, w.scales, O.DEFAULT_CLIP, False, lut, skv=Skv, prob_bits=prob_bits,
+                      lut_bits=lut_bits, workspace=ws)
+    c = IA.forward_ex(qd, kd, vd, w.scales, O.DEFAULT_CLIP, False, lut, skv=Skv, prob_bits=prob_bits,
+                      lut_bits=lut_bits, workspace=False)
+    torch.cuda.synchronize()
+    _eq("split repeat", b.cpu().numpy(), a.cpu().numpy())
+    _eq("split vs long-row kernel", c.cpu().numpy(), ref)
+    _eq("split through a given workspace", a.cpu().numpy(), ref)
