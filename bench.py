@@ -323,7 +323,9 @@ def variants(steps=None):
     uint16 also on the decode shape), grouped
     K/V heads on the batched decode shape (HBM GB/s of
     Q + K + V + O with K/V read once per K/V head), and the decode-step cache
-    update (HBM GB/s of 4 bytes read and 1 written per value). One JSON line."""
+    update (HBM GB/s of 4 bytes read and 1 written per value), and decode
+    over caches longer than 16384 keys (split over workgroups, against the
+    long-row kernel). One JSON line."""
     import torch
 
     from integer_only_quantized_amd import _binding as ia
@@ -425,6 +427,29 @@ def variants(steps=None):
     us = _time_calls(step, stream, steps or 100)
     res["decode_step"] = {"shape": {"B": Bc, "H": H, "Hkv": hkv, "Skv": filled + 1, "D": D},
                           "us_per_step": us, "steps_per_s": 1e6 / us}
+    del kc, vc, kn, vn
+    torch.cuda.empty_cache()
+
+    # decode over caches past the single-workgroup decode kernel's 16384 keys:
+    # keys split over several workgroups per head (workspace), HBM GB/s of
+    # K + V read once; the long-row kernel (no workspace) beside it
+    res["long_cache_decode"] = {}
+    for (Bc, Hc, Skv) in ((8, 32, 32768), (2, 32, 65535)):
+        ql = codes((Bc, Hc, 1, D))
+        kl = codes((Bc, Hc, Skv, D))
+        vl = codes((Bc, Hc, Skv, D))
+        ol = torch.empty_like(ql)
+        ws = torch.empty(ia.workspace_bytes(Bc, Hc, 1, Skv, D), dtype=torch.uint8, device=dev)
+        nbytes = 2 * Bc * Hc * Skv * D
+        row = {"workspace_bytes": ws.numel(), "bytes": nbytes}
+        for name, w in (("split", ws), ("long_row_kernel", False)):
+            fn = lambda w=w: ia.forward_ex(ql, kl, vl, scales, W.DEFAULT_CLIP, False, 32, out=ol, workspace=w)
+            us = _time_calls(fn, stream, steps or 30)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            row[name] = {"us_per_call": us, "GBs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+        res["long_cache_decode"][f"B={Bc} H={Hc} Skv={Skv}"] = row
+        del ql, kl, vl, ol, ws
+        torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
     return 0
 
