@@ -324,8 +324,8 @@ def variants(steps=None):
     K/V heads on the batched decode shape (HBM GB/s of
     Q + K + V + O with K/V read once per K/V head), and the decode-step cache
     update (HBM GB/s of 4 bytes read and 1 written per value), and decode
-    over caches longer than 16384 keys (split over workgroups, against the
-    long-row kernel). One JSON line."""
+    with keys split over workgroups (batch 1, and caches longer than 16384
+    keys) against the same calls without a workspace. One JSON line."""
     import torch
 
     from integer_only_quantized_amd import _binding as ia
@@ -430,11 +430,12 @@ def variants(steps=None):
     del kc, vc, kn, vn
     torch.cuda.empty_cache()
 
-    # decode over caches past the single-workgroup decode kernel's 16384 keys:
-    # keys split over several workgroups per head (workspace), HBM GB/s of
-    # K + V read once; the long-row kernel (no workspace) beside it
-    res["long_cache_decode"] = {}
-    for (Bc, Hc, Skv) in ((8, 32, 32768), (2, 32, 65535)):
+    # decode with keys split over several workgroups per head (workspace):
+    # batch 1 (32 heads: one workgroup each on the decode kernel) and caches
+    # past the decode kernel's 16384 keys (the long-row kernel without a
+    # workspace); HBM GB/s of K + V read once
+    res["split_decode"] = {}
+    for (Bc, Hc, Skv) in ((1, 32, 8192), (8, 32, 32768), (2, 32, 65535)):
         ql = codes((Bc, Hc, 1, D))
         kl = codes((Bc, Hc, Skv, D))
         vl = codes((Bc, Hc, Skv, D))
@@ -442,12 +443,12 @@ def variants(steps=None):
         ws = torch.empty(ia.workspace_bytes(Bc, Hc, 1, Skv, D), dtype=torch.uint8, device=dev)
         nbytes = 2 * Bc * Hc * Skv * D
         row = {"workspace_bytes": ws.numel(), "bytes": nbytes}
-        for name, w in (("split", ws), ("long_row_kernel", False)):
+        for name, w in (("split", ws), ("without_workspace", False)):
             fn = lambda w=w: ia.forward_ex(ql, kl, vl, scales, W.DEFAULT_CLIP, False, 32, out=ol, workspace=w)
             us = _time_calls(fn, stream, steps or 30)
             gbs = nbytes / (us * 1e-6) / 1e9
             row[name] = {"us_per_call": us, "GBs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
-        res["long_cache_decode"][f"B={Bc} H={Hc} Skv={Skv}"] = row
+        res["split_decode"][f"B={Bc} H={Hc} Skv={Skv}"] = row
         del ql, kl, vl, ol, ws
         torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)

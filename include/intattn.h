@@ -169,12 +169,14 @@ typedef struct intattn_variant {
                             above) or 16 (uint16 variant); 0 means 8         */
     int32_t lut_bits;    /* table entry width: 16 (Q15, the specification
                             above) or 8 (uint8 entries); 0 means 16          */
-    void*    workspace;  /* device memory, caller-owned, for decode over long
-                            caches (Sq = 1, Skv > 16384): keys are split into
-                            chunks over several workgroups per head (exact:
-                            the row max and sum are combined before any
-                            probability, and the P.V partials are integers).
-                            NULL: those shapes run on the long-row kernel   */
+    void*    workspace;  /* device memory, caller-owned, for decode (Sq = 1)
+                            with Skv > 16384, or with fewer than 128 heads
+                            (B*H) and Skv >= 4096: keys are split into chunks
+                            over several workgroups per head (exact: the row
+                            max and sum are combined before any probability,
+                            and the P.V partials are integers). NULL: those
+                            shapes run on the long-row kernel (Skv > 16384)
+                            or the decode kernel                              */
     uint64_t workspace_bytes; /* size of workspace                           */
 } intattn_variant;
 
@@ -219,8 +221,8 @@ int intattn_derive_params_ex(const intattn_shape* shape, const intattn_scales* s
 /* Bytes of workspace intattn_forward_ex uses for this shape and variant
  * (256-byte aligned; int32 scores per key and head, per-chunk maxima and
  * sums, per-head accumulators), 0 when the shape does not use one (only
- * Sq = 1 with Skv > 16384 does). Host only, pure. Returns 0 for an invalid
- * shape as well. */
+ * Sq = 1 with Skv > 16384, or B*H < 128 and Skv >= 4096, does). Host only,
+ * pure. Returns 0 for an invalid shape as well. */
 uint64_t intattn_workspace_bytes(const intattn_shape* shape, const intattn_variant* variant);
 
 int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,

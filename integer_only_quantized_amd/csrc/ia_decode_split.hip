@@ -1,6 +1,7 @@
-// Decode over long caches (Sq = 1): each head's keys are split into chunks of
-// kSplitChunk keys, one workgroup per (head, chunk), so that a few heads with
-// a long cache still fill the GPU and the key count is not bounded by the LDS.
+// Decode (Sq = 1) with each head's keys split into chunks of 512 to 4096 keys
+// (split_chunk: halved while the grid has fewer than 1024 workgroups), one
+// workgroup per (head, chunk), so that a few heads still fill the GPU and the
+// key count is not bounded by the LDS.
 //
 // Method: IntAttention digest pages (arXiv 2511.21513v1), "Methodology",
 // steps 2-3; integer widths and roundings as stated in include/intattn.h.
@@ -23,7 +24,8 @@
 namespace ia {
 namespace {
 
-constexpr int kSplitChunk = 4096;     // keys per workgroup
+constexpr int kSplitChunk = 4096;     // most keys per workgroup (LDS holds their P)
+constexpr int kSplitChunkMin = 512;   // a multiple of every key step below
 constexpr int kSplitThreads = 256;    // 4 waves
 constexpr int kSplitNW = kSplitThreads / 64;
 constexpr int kSplitUnroll = 2;       // key groups a lane loads before using them
@@ -42,10 +44,10 @@ struct SplitBlock {
     int k0, k1;
 };
 
-__device__ __forceinline__ SplitBlock split_block(const InvariantDiv& nchunks_div, int Skv) {
+__device__ __forceinline__ SplitBlock split_block(const InvariantDiv& nchunks_div, int Skv, int chunk) {
     const UDivMod hc = divmod_invariant(blockIdx.x, nchunks_div);
-    const int k0 = static_cast<int>(hc.r) * kSplitChunk;
-    return SplitBlock{hc.q, hc.r, k0, min(Skv, k0 + kSplitChunk)};
+    const int k0 = static_cast<int>(hc.r) * chunk;
+    return SplitBlock{hc.q, hc.r, k0, min(Skv, k0 + chunk)};
 }
 
 // Workgroup max / sum of a per-thread value (every thread gets the result).
@@ -86,14 +88,14 @@ __device__ __forceinline__ int32_t split_row_max(const SplitWs& ws, uint32_t hea
 template <int D>
 __global__ __launch_bounds__(kSplitThreads) void ia_dsplit_scores_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, const IaKernelParams P, InvariantDiv nchunks_div,
-    int nchunks, SplitWs ws) {
+    int nchunks, int chunk, SplitWs ws) {
     constexpr int CPR = D / 16;
     constexpr int GPW = 64 / CPR;
     constexpr int KEYS_IT = 4 * GPW * kSplitNW;
     __shared__ int32_t red[kSplitNW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane % CPR, g = lane / CPR;
-    const SplitBlock sb = split_block(nchunks_div, P.Skv);
+    const SplitBlock sb = split_block(nchunks_div, P.Skv, chunk);
     const size_t kvhead = divmod_invariant(sb.head, P.kvg_div).q;
     const int8_t* kh = k + kvhead * P.kv_rows * D;
     const v4i qv = *reinterpret_cast<const v4i*>(q + static_cast<size_t>(sb.head) * D + 16 * c);
@@ -136,12 +138,12 @@ __global__ __launch_bounds__(kSplitThreads) void ia_dsplit_scores_kernel(
 // ---- 2: table entries and their sum over a chunk ---------------------------------
 __global__ __launch_bounds__(kSplitThreads) void ia_dsplit_sums_kernel(const IaKernelParams P,
                                                                        InvariantDiv nchunks_div, int nchunks,
-                                                                       SplitWs ws) {
+                                                                       int chunk, SplitWs ws) {
     __shared__ uint16_t s_lut[kIaMaxLut];
     __shared__ int32_t red[kSplitNW];
     const int tid = threadIdx.x;
     if (tid < 64) fill_lut_u16(P, s_lut, tid);
-    const SplitBlock sb = split_block(nchunks_div, P.Skv);
+    const SplitBlock sb = split_block(nchunks_div, P.Skv, chunk);
     const int32_t m = split_row_max(ws, sb.head, nchunks);
     const int32_t lo = m - P.x_clip;
     const uint32_t Cm = static_cast<uint32_t>(m) * static_cast<uint32_t>(P.idx_mul) + (1u << 23);
@@ -160,13 +162,13 @@ __global__ __launch_bounds__(kSplitThreads) void ia_dsplit_sums_kernel(const IaK
 // ---- 3: probabilities and P.V over a chunk ------------------------------------------
 template <int D, bool P16>
 __global__ __launch_bounds__(kSplitThreads) void ia_dsplit_pv_kernel(
-    const int8_t* __restrict__ v, const IaKernelParams P, InvariantDiv nchunks_div, int nchunks, SplitWs ws,
-    int32_t* __restrict__ row_max, uint32_t* __restrict__ row_sum) {
+    const int8_t* __restrict__ v, const IaKernelParams P, InvariantDiv nchunks_div, int nchunks, int chunk,
+    SplitWs ws, int32_t* __restrict__ row_max, uint32_t* __restrict__ row_sum) {
     constexpr int CPR = D / 16;
     constexpr int GPW = 64 / CPR;
     constexpr int KEYS_IT = 4 * GPW * kSplitNW;
     constexpr int STEP = kSplitUnroll * KEYS_IT;
-    static_assert(kSplitChunk % STEP == 0, "chunks hold whole key steps");
+    static_assert(kSplitChunkMin % STEP == 0, "chunks hold whole key steps");
     __shared__ uint16_t s_lut[kIaMaxLut];
     __shared__ __attribute__((aligned(16))) uint8_t s_p[kSplitChunk * (P16 ? 2 : 1)];
     __shared__ int32_t s_red[P16 ? 2 : 1][kSplitNW][D];
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(kSplitThreads) void ia_dsplit_pv_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane % CPR, g = lane / CPR;
     if (tid < 64) fill_lut_u16(P, s_lut, tid);
-    const SplitBlock sb = split_block(nchunks_div, P.Skv);
+    const SplitBlock sb = split_block(nchunks_div, P.Skv, chunk);
     const size_t kvhead = divmod_invariant(sb.head, P.kvg_div).q;
     const int8_t* vh = v + kvhead * P.kv_rows * D;
     const int32_t m = split_row_max(ws, sb.head, nchunks);
@@ -319,10 +321,17 @@ inline size_t split_align(size_t n) { return (n + 255) & ~static_cast<size_t>(25
 
 }  // namespace
 
-int split_max_chunks() { return (65535 + kSplitChunk - 1) / kSplitChunk; }
+// Keys per chunk for B*H heads: 4096, halved (down to 512) while the grid
+// would have fewer than 1024 workgroups.
+int split_chunk(long long heads, int Skv) {
+    int chunk = kSplitChunk;
+    while (chunk > kSplitChunkMin && heads * ((Skv + chunk - 1) / chunk) < 1024) chunk /= 2;
+    return chunk;
+}
 
 size_t decode_split_workspace_bytes(long long heads, int Skv, int D) {
-    const int nchunks = (Skv + kSplitChunk - 1) / kSplitChunk;
+    const int chunk = split_chunk(heads, Skv);
+    const int nchunks = (Skv + chunk - 1) / chunk;
     return split_align(static_cast<size_t>(heads) * Skv * 4) + 2 * split_align(static_cast<size_t>(heads) * nchunks * 4) +
            split_align(static_cast<size_t>(heads) * D * 4);
 }
@@ -331,7 +340,8 @@ int launch_decode_split(const int8_t* q, const int8_t* k, const int8_t* v, int8_
                         void* stream, void* workspace, int32_t* row_max, uint32_t* row_sum) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const long long heads = static_cast<long long>(kp.B) * kp.H;
-    const int nchunks = (kp.Skv + kSplitChunk - 1) / kSplitChunk;
+    const int chunk = split_chunk(heads, kp.Skv);
+    const int nchunks = (kp.Skv + chunk - 1) / chunk;
     const long long blocks = heads * nchunks;
     if (blocks > INT_MAX || heads * D > INT_MAX) return INTATTN_E_SHAPE;
     char* base = static_cast<char*>(workspace);
@@ -345,16 +355,16 @@ int launch_decode_split(const int8_t* q, const int8_t* k, const int8_t* v, int8_
     ws.acc = reinterpret_cast<int32_t*>(base);
     const InvariantDiv ndiv = invariant_div(static_cast<uint32_t>(nchunks));
     const dim3 grid(static_cast<unsigned>(blocks)), block(kSplitThreads);
-    if (D == 64) hipLaunchKernelGGL((ia_dsplit_scores_kernel<64>), grid, block, 0, s, q, k, kp, ndiv, nchunks, ws);
-    else hipLaunchKernelGGL((ia_dsplit_scores_kernel<128>), grid, block, 0, s, q, k, kp, ndiv, nchunks, ws);
-    hipLaunchKernelGGL(ia_dsplit_sums_kernel, grid, block, 0, s, kp, ndiv, nchunks, ws);
+    if (D == 64) hipLaunchKernelGGL((ia_dsplit_scores_kernel<64>), grid, block, 0, s, q, k, kp, ndiv, nchunks, chunk, ws);
+    else hipLaunchKernelGGL((ia_dsplit_scores_kernel<128>), grid, block, 0, s, q, k, kp, ndiv, nchunks, chunk, ws);
+    hipLaunchKernelGGL(ia_dsplit_sums_kernel, grid, block, 0, s, kp, ndiv, nchunks, chunk, ws);
     const bool p16 = kp.prob_bits == 16;
     if (D == 64) {
-        if (p16) hipLaunchKernelGGL((ia_dsplit_pv_kernel<64, true>), grid, block, 0, s, v, kp, ndiv, nchunks, ws, row_max, row_sum);
-        else hipLaunchKernelGGL((ia_dsplit_pv_kernel<64, false>), grid, block, 0, s, v, kp, ndiv, nchunks, ws, row_max, row_sum);
+        if (p16) hipLaunchKernelGGL((ia_dsplit_pv_kernel<64, true>), grid, block, 0, s, v, kp, ndiv, nchunks, chunk, ws, row_max, row_sum);
+        else hipLaunchKernelGGL((ia_dsplit_pv_kernel<64, false>), grid, block, 0, s, v, kp, ndiv, nchunks, chunk, ws, row_max, row_sum);
     } else {
-        if (p16) hipLaunchKernelGGL((ia_dsplit_pv_kernel<128, true>), grid, block, 0, s, v, kp, ndiv, nchunks, ws, row_max, row_sum);
-        else hipLaunchKernelGGL((ia_dsplit_pv_kernel<128, false>), grid, block, 0, s, v, kp, ndiv, nchunks, ws, row_max, row_sum);
+        if (p16) hipLaunchKernelGGL((ia_dsplit_pv_kernel<128, true>), grid, block, 0, s, v, kp, ndiv, nchunks, chunk, ws, row_max, row_sum);
+        else hipLaunchKernelGGL((ia_dsplit_pv_kernel<128, false>), grid, block, 0, s, v, kp, ndiv, nchunks, chunk, ws, row_max, row_sum);
     }
     const int total = static_cast<int>(heads * D);
     hipLaunchKernelGGL(ia_dsplit_out_kernel, dim3(static_cast<unsigned>((total + kSplitThreads - 1) / kSplitThreads)),

@@ -91,17 +91,23 @@ int prepare(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
 
 long long rows_of(const IaKernelParams& kp) { return static_cast<long long>(kp.B) * kp.H * kp.Sq; }
 
-// Decode shapes past the single-workgroup decode kernel's key limit split
-// their keys over several workgroups when the caller gives a workspace.
-bool uses_split(int Sq, int Skv) { return Sq == 1 && Skv > ia::decode_max_keys(); }
+// Decode shapes split their keys over several workgroups per head when the
+// caller gives a workspace: past the single-workgroup decode kernel's key
+// limit, and when fewer than 128 heads (a workgroup each) would leave most of
+// the GPU idle, from 4096 keys on (the split's four launches cost about
+// 17 us; one workgroup per head at 32 heads takes 29 us for 4096 keys).
+bool uses_split(int B, int H, int Sq, int Skv) {
+    const long long heads = static_cast<long long>(B) * H;
+    return Sq == 1 && (Skv > ia::decode_max_keys() || (heads < 128 && Skv >= 4096));
+}
 
 int dispatch(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
              const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum,
              void* workspace = nullptr) {
+    if (workspace != nullptr && uses_split(kp.B, kp.H, kp.Sq, kp.Skv))
+        return ia::launch_decode_split(q, k, v, out, D, kp, stream, workspace, row_max, row_sum);
     if (kp.Sq == 1 && kp.Skv <= ia::decode_max_keys())
         return ia::launch_decode(q, k, v, out, D, kp, stream, row_max, row_sum);
-    if (workspace != nullptr && uses_split(kp.Sq, kp.Skv))
-        return ia::launch_decode_split(q, k, v, out, D, kp, stream, workspace, row_max, row_sum);
     // uint16 probabilities: the long-row kernel serves every other shape
     if (kp.Skv <= ia::short_max_keys(D) && kp.prob_bits == 8)
         return ia::launch_short(q, k, v, out, D, kp, stream, row_max, row_sum);
@@ -140,7 +146,7 @@ extern "C" uint64_t intattn_workspace_bytes(const intattn_shape* shape, const in
     (void)variant;   // the workspace does not depend on the table or probability width
     if (!shape || intattn_validate_shape(shape, 0) != INTATTN_OK) return 0;
     if (shape->D != 64 && shape->D != 128) return 0;
-    if (!uses_split(shape->Sq, shape->Skv)) return 0;
+    if (!uses_split(shape->B, shape->H, shape->Sq, shape->Skv)) return 0;
     return ia::decode_split_workspace_bytes(static_cast<long long>(shape->B) * shape->H, shape->Skv, shape->D);
 }
 
@@ -159,7 +165,7 @@ extern "C" int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t
                            prob_bits, lut_bits);
     if (st != INTATTN_OK) return st;
     void* ws = variant ? variant->workspace : nullptr;
-    if (ws != nullptr && uses_split(shape->Sq, shape->Skv)) {
+    if (ws != nullptr && uses_split(shape->B, shape->H, shape->Sq, shape->Skv)) {
         const uint64_t need = intattn_workspace_bytes(shape, variant);
         if (variant->workspace_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return INTATTN_E_WORKSPACE;
     }

@@ -326,16 +326,24 @@ def test_parameter_derivation_from_many_threads():
 
 
 def test_workspace_size_and_validation_before_any_device_call():
-    """Only decode past the decode kernel's 16384 keys takes a workspace: int32
-    scores per key and head, per-chunk maxima and sums (4096-key chunks) and
-    per-head accumulators, each region 256-byte aligned. A workspace below that
-    size, or not 256-byte aligned, is refused before any device work."""
+    """Decode takes a workspace past the decode kernel's 16384 keys, and with
+    fewer than 128 heads from 4096 keys on: int32 scores per key and head,
+    per-chunk maxima and sums and per-head accumulators, each region 256-byte
+    aligned; chunks of 4096 keys, halved down to 512 while the grid has fewer
+    than 1024 workgroups. A workspace below that size, or not 256-byte
+    aligned, is refused before any device work."""
     E = {v: k for k, v in B.STATUS_NAMES.items()}
     al = lambda n: (n + 255) // 256 * 256
-    assert B.workspace_bytes(16, 32, 1, 16384, 128) == 0
+    assert B.workspace_bytes(16, 32, 1, 16384, 128) == 0             # 512 heads: one workgroup each
+    assert B.workspace_bytes(4, 32, 1, 8192, 128) == 0               # 128 heads
+    assert B.workspace_bytes(1, 32, 1, 4095, 128) == 0               # too few keys to split
     assert B.workspace_bytes(2, 32, 2, 40000, 128) == 0              # not a decode shape
-    for (b, h, skv, d) in [(16, 32, 16385, 128), (2, 32, 65535, 128), (1, 3, 20000, 64)]:
-        heads, nch = b * h, -(-skv // 4096)
+    for (b, h, skv, d) in [(16, 32, 16385, 128), (2, 32, 65535, 128), (1, 3, 20000, 64), (1, 32, 8192, 128),
+                           (1, 32, 4096, 64)]:
+        heads, chunk = b * h, 4096
+        while chunk > 512 and heads * -(-skv // chunk) < 1024:
+            chunk //= 2
+        nch = -(-skv // chunk)
         assert B.workspace_bytes(b, h, 1, skv, d) == al(heads * skv * 4) + 2 * al(heads * nch * 4) + al(heads * d * 4)
     assert B.workspace_bytes(1, 1, 1, 65536, 128) == 0               # invalid shape
     sh = B.Shape(1, 4, 1, 20000, 128)

@@ -259,6 +259,11 @@ SPLIT_CASES = [
     (1, 4, 1, 33000, 128, 128, 16, 16, 0, 903, "normal"),
     (2, 4, 2, 24577, 64, 32, 16, 8, 100, 904, "channel_outliers"),
     (1, 2, 2, 40960, 128, 32, 8, 8, 0, 905, "student_t_tail"),
+    # few heads over shorter caches: the decode kernel would run one
+    # workgroup per head, so the keys are split (chunks down to 512 keys)
+    (1, 32, 8, 8192, 128, 32, 8, 16, 0, 906, "normal"),
+    (1, 4, 4, 5000, 128, 64, 16, 16, 0, 907, "channel_outliers"),
+    (1, 2, 1, 4100, 64, 32, 8, 8, 7, 908, "student_t_tail"),
 ]
 
 
