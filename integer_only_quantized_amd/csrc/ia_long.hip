@@ -89,8 +89,8 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     const int bid = blockIdx.x;
     int head_i, qb;
     if (P.causal && (nheads & 7) == 0) {
-        const int hpx = nheads >> 3, j = bid >> 3;
-        const UDivMod t = divmod_invariant(static_cast<uint32_t>(j), map_div);   // by hpx
+        const int j = bid >> 3;
+        const UDivMod t = divmod_invariant(static_cast<uint32_t>(j), map_div);   // by nheads / 8
         head_i = (bid & 7) + 8 * static_cast<int>(t.r);
         qb = nqb - 1 - static_cast<int>(t.q);
     } else if (P.causal) {
