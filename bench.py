@@ -13,12 +13,19 @@ Work counted (algorithmic only): 4*d integer ops per allowed score (2*d for
 Q.K^T, 2*d for P.V; causal counts the lower triangle with the diagonal), and
 Q + K + V + O bytes of int8 read or written once.
 
-Timing: W untimed calls, then K calls bracketed by synchronisation and HIP
-events recorded on the stream the library launches on (the caller's current
+Timing: 0.3 s of untimed calls (the GPU leaves its idle clocks), W untimed
+calls, then exactly K calls bracketed by synchronisation and HIP events
+recorded on the stream the library launches on (the caller's current
 stream). The same events give the kernel's average duration per launch used
 for the roofline fraction. Five more blocks of K calls give the median, and
 one block cycling through copies of the inputs (more than 512 MB in all, so
 they do not stay in the caches) gives the cold-input rate.
+
+The default run (BERT) also times every other workload in the same process
+(key "workloads": tiny, BERT, ViT, causal prefill and batched decode, the
+last one giving the metric's decode GB/s), each with both roofline fractions,
+its outputs on a sample of heads compared with the oracle, and the oracle's
+own rate on a short sample.
 
     python bench.py --calibrate peaks   # measured copy GB/s, int8 MFMA TOPS, VALU ops/s
     python bench.py --calibrate copy    # three 256 MiB device copies (counter scaling run)
@@ -51,7 +58,8 @@ DEFAULT_STEPS = {"tiny": 2000, "bert": 500, "vit": 500, "llama_prefill": 50, "de
 # untimed calls before the timed region: about 0.4 s of work, so the GPU has
 # left its idle clocks (shorter warm-ups measure the clock ramp-up)
 DEFAULT_WARMUP = {"tiny": 50000, "bert": 30000, "vit": 25000, "llama_prefill": 2000, "decode": 2000}
-BOUND = {"tiny": "mfma", "bert": "mfma", "vit": "mfma", "llama_prefill": "mfma", "decode": "hbm"}
+# binding roofline per workload (ViT: 197 keys a row, arithmetic intensity 197 ops/byte, HBM)
+BOUND = {"tiny": "mfma", "bert": "mfma", "vit": "hbm", "llama_prefill": "mfma", "decode": "hbm"}
 # kernel the library dispatches for each workload, and its source file
 KERNEL = {"tiny": ("ia_short_kernel", "ia_short.hip"), "bert": ("ia_short_kernel", "ia_short.hip"),
           "vit": ("ia_short_kernel", "ia_short.hip"), "llama_prefill": ("ia_long_kernel", "ia_long.hip"),
@@ -455,71 +463,69 @@ def variants(steps=None):
     return 0
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="bert",
-                    choices=["tiny", "bert", "vit", "llama_prefill", "decode"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--calibrate", choices=["peaks", "copy"], default=None)
-    ap.add_argument("--breakdown", action="store_true",
-                    help="per-stage times of the unfused pipelines (integer and float32 softmax)")
-    ap.add_argument("--variants", action="store_true",
-                    help="finer exp tables, grouped K/V heads and the cache update (one JSON line)")
-    ap.add_argument("--no-extra-timing", action="store_true",
-                    help="skip the median-of-5 and cold-input blocks")
-    args = ap.parse_args(argv)
+CLOCK_SETTLE_S = 0.3
+# parity sample per workload: (b, h) heads compared with the oracle
+PARITY_HEADS = {"tiny": [(0, 0)], "bert": [(0, 0), (3, 7), (5, 2), (7, 11)],
+                "vit": [(0, 0), (13, 5), (31, 11)], "llama_prefill": [(0, 0), (0, 31)],
+                "decode": [(0, 0), (7, 19), (15, 31)]}
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: attention heads are independent, so a "
-              "multi-GPU run is the same kernel on each GPU's share of the heads, and this "
-              "library runs on one GPU. Run with --gpus 1.", file=sys.stderr)
-        return 2
 
-    if args.calibrate:
-        return calibrate(args.calibrate)
-    if args.breakdown:
-        return breakdown(args.config, args.steps)
-    if args.variants:
-        return variants(args.steps)
-
+def np_equal(a, b):
     import numpy as np
+    return bool(np.array_equal(a, b))
+
+
+def roofline(config, tops, gbs):
+    """Roofline of a workload: its binding unit (int8 MFMA or HBM) and both
+    fractions, from the algorithmic ops and bytes per call."""
+    bound = BOUND[config]
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": tops, "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                "frac": tops / PEAK_INT8_TOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS}
+    roof["mfma_frac"] = tops / PEAK_INT8_TOPS
+    roof["hbm_frac"] = gbs / PEAK_HBM_GBS
+    return roof
+
+
+def measure(w, steps, warmup, extra_timing=False, settle_s=CLOCK_SETTLE_S):
+    """Times intattn_forward over workload w with inputs resident in HBM.
+
+    First settle_s seconds of untimed calls (the GPU leaves its idle clocks),
+    then `warmup` untimed calls, then exactly `steps` calls bracketed by
+    synchronisation and HIP events recorded on the stream the library
+    launches on (the caller's current stream). Returns ms_per_step, the wall
+    time of the timed region, the output (numpy) and, with extra_timing,
+    five more blocks (median) and one block over input copies totalling more
+    than 512 MB (cold caches).
+    """
     import torch
 
     from integer_only_quantized_amd import _binding as ia
-    from integer_only_quantized_amd import workloads as W
 
-    steps = args.steps or DEFAULT_STEPS[args.config]
-    warmup = DEFAULT_WARMUP[args.config] if args.warmup is None else args.warmup
-    w = W.make_config(args.config)
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     q, k, v = (torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
-
+    call = lambda: ia.forward(q, k, v, w.scales, w.clip, w.causal, out=out)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        call()
     for _ in range(warmup):
-        ia.forward(q, k, v, w.scales, w.clip, w.causal, out=out)
+        call()
     torch.cuda.synchronize(dev)
-
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dev)
     t_wall0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(steps):
-        ia.forward(q, k, v, w.scales, w.clip, w.causal, out=out)
+        call()
     ev1.record(stream)
     torch.cuda.synchronize(dev)
-    t_wall = time.perf_counter() - t_wall0
-    ms_total = ev0.elapsed_time(ev1)
-    ms_per_step = ms_total / steps
-
-    timing = None
-    if not args.no_extra_timing:
+    res = {"wall_s": time.perf_counter() - t_wall0, "ms_per_step": ev0.elapsed_time(ev1) / steps}
+    if extra_timing:
         def timed_block(sets):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -540,23 +546,108 @@ def main(argv=None):
         cold_sets = warm + [(q.clone(), k.clone(), v.clone(), torch.empty_like(out)) for _ in range(n_sets - 1)]
         cold = timed_block(cold_sets)
         del cold_sets
-        timing = {"repeats_ms_per_step": reps, "median_ms_per_step": sorted(reps)[2],
-                  "cold_ms_per_step": cold, "cold_input_sets": n_sets,
-                  "cold_input_bytes": n_sets * per_set}
+        res["timing"] = {"repeats_ms_per_step": reps, "median_ms_per_step": sorted(reps)[2],
+                         "cold_ms_per_step": cold, "cold_input_sets": n_sets,
+                         "cold_input_bytes": n_sets * per_set}
+    res["out"] = out.cpu().numpy()
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return res
 
+
+def all_workloads(bert_w, args):
+    """Every workload of the metric timed in this run (exactly
+    DEFAULT_STEPS[name] calls each after the same clock settle and
+    DEFAULT_WARMUP-capped warm-up), with the rates, both roofline fractions
+    and the output of a sample of heads compared with the oracle, plus the
+    oracle's own rate on a short sample of the same workload."""
+    from oracle import intattn_oracle as O
+    from integer_only_quantized_amd import workloads as W
+
+    res = {}
+    for name in ("tiny", "bert", "vit", "llama_prefill", "decode"):
+        w = bert_w if name == "bert" else W.make_config(name)
+        steps = DEFAULT_STEPS[name]
+        warmup = min(DEFAULT_WARMUP[name], 200)
+        m = measure(w, steps, warmup)
+        ops, nbytes, scores = algorithmic_work(w)
+        sec = m["ms_per_step"] / 1e3
+        tops, gbs = ops / sec / 1e12, nbytes / sec / 1e9
+        prm = O.derive_params(w.D, *w.scales, w.clip)
+        heads = PARITY_HEADS[name]
+        parity = all(np_equal(m["out"][b, h], O.head_forward(w.q[b, h], w.k[b, h], w.v[b, h], prm, w.causal)[0])
+                     for b, h in heads)
+        entry = {
+            "shape": {"B": w.B, "H": w.H, "Sq": w.Sq, "Skv": w.Skv, "D": w.D, "causal": w.causal},
+            "kernel": KERNEL[name][0], "steps": steps, "warmup": warmup,
+            "ms_per_step": m["ms_per_step"], "calls_per_s": 1.0 / sec,
+            "int8_tops": tops, "gb_per_s": gbs, "roofline": roofline(name, tops, gbs),
+            "parity_on_sample": parity, "parity_heads": [list(bh) for bh in heads],
+        }
+        if not args.no_cpu_baseline:
+            cpu, _ = cpu_baseline(w, min(args.cpu_budget, 2.0))
+            entry["cpu_oracle"] = {"TOPS": cpu["value"], "calls_per_s": cpu["calls_per_s"],
+                                   "GB_per_s": nbytes * cpu["calls_per_s"] / 1e9, "cores": cpu["cores"],
+                                   "seconds": cpu["seconds"]}
+        res[name] = entry
+        print(f"# workload {name}: {m['ms_per_step'] * 1e3:.2f} us/call, parity {parity}",
+              file=sys.stderr, flush=True)
+        del m
+        if name != "bert":
+            del w
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default="bert",
+                    choices=["tiny", "bert", "vit", "llama_prefill", "decode"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibrate", choices=["peaks", "copy"], default=None)
+    ap.add_argument("--breakdown", action="store_true",
+                    help="per-stage times of the unfused pipelines (integer and float32 softmax)")
+    ap.add_argument("--variants", action="store_true",
+                    help="finer exp tables, grouped K/V heads and the cache update (one JSON line)")
+    ap.add_argument("--no-extra-timing", action="store_true",
+                    help="skip the median-of-5 and cold-input blocks")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="time the headline workload only (default: also every other workload)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: attention heads are independent, so a "
+              "multi-GPU run is the same kernel on each GPU's share of the heads, and this "
+              "library runs on one GPU. Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    if args.calibrate:
+        return calibrate(args.calibrate)
+    if args.breakdown:
+        return breakdown(args.config, args.steps)
+    if args.variants:
+        return variants(args.steps)
+
+    import torch
+
+    from integer_only_quantized_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    steps = args.steps or DEFAULT_STEPS[args.config]
+    warmup = DEFAULT_WARMUP[args.config] if args.warmup is None else args.warmup
+    w = W.make_config(args.config)
+    m = measure(w, steps, warmup, extra_timing=not args.no_extra_timing)
+    ms_per_step = m["ms_per_step"]
     ops, nbytes, scores = algorithmic_work(w)
     sec = ms_per_step / 1e3
     tops = ops / sec / 1e12
     gbs = nbytes / sec / 1e9
-    calls = 1.0 / sec
 
-    bound = BOUND[args.config]
-    if bound == "mfma":
-        roof = {"bound": "mfma", "achieved": tops, "peak": PEAK_INT8_TOPS, "unit": "TOPS",
-                "frac": tops / PEAK_INT8_TOPS}
-    else:
-        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": gbs / PEAK_HBM_GBS}
+    roof = roofline(args.config, tops, gbs)
     roof["kernel"] = KERNEL[args.config][0]
     roof["per_launch"] = {"ops": ops, "bytes": nbytes, "scores": scores,
                           "avg_launch_us": ms_per_step * 1e3}
@@ -571,12 +662,10 @@ def main(argv=None):
                 "source": f"profiles/valu_{KERNEL[args.config][0]}_{args.config}.txt"}
 
     cpu = None
-    parity = None
     if not args.no_cpu_baseline:
         cpu, ref = cpu_baseline(w, args.cpu_budget)
-        got = out.cpu().numpy()
-        parity = all(np.array_equal(got[b, h], r) for (b, h), r in ref.items())
-        cpu["parity_on_sample"] = parity
+        cpu["parity_on_sample"] = all(
+            np_equal(m["out"][b, h], r) for (b, h), r in ref.items())
 
     if args.config == "decode":
         metric_value, unit = gbs, "GB/s"
@@ -598,15 +687,21 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": args.config, "description": w.meta.get("description"),
                    "B": w.B, "H": w.H, "Sq": w.Sq, "Skv": w.Skv, "D": w.D, "causal": w.causal},
-        "calls_per_s": calls,
+        "calls_per_s": 1.0 / sec,
         "int8_tops": tops,
         "gb_per_s": gbs,
-        "wall_s_timed_region": t_wall,
+        "clock_settle_s": CLOCK_SETTLE_S,
+        "wall_s_timed_region": m["wall_s"],
         "roofline": roof,
         "valu_roofline": valu,
-        "timing": timing,
+        "timing": m.get("timing"),
         "cpu_baseline": cpu,
     }
+    del m
+    if args.config == "bert" and not args.no_workloads:
+        # the rest of the metric (decode GB/s) and every other workload, timed
+        # in the same run
+        line["workloads"] = all_workloads(w, args)
     print(json.dumps(line), flush=True)
     return 0
 

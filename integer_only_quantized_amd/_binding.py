@@ -359,13 +359,18 @@ def forward_ex(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False
     (Hkv divides H; query head h reads K/V head h // (H // Hkv)); the first
     skv rows of each K/V head are attended (default all C: a cache of capacity
     C holding skv tokens); a table of lut_size entries of lut_bits bits;
-    prob_bits-wide probabilities. Decode over a cache longer than the
-    single-workgroup decode kernel takes (Sq = 1, skv > 16384) splits its
-    keys over several workgroups per head in a device workspace: a uint8
-    tensor on q's device of at least workspace_bytes(...) bytes, allocated
-    here when not given (workspace=False: no workspace, the long-row kernel
-    runs). Returns out, or (out, row_max, row_sum) with stats (row_sum in Q15
-    units: 128 times the uint8 table's sum)."""
+    prob_bits-wide probabilities. Decode shapes (Sq = 1) split their keys
+    over several workgroups per head, in a device workspace, in two cases:
+    a cache longer than the single-workgroup decode kernel takes
+    (skv > 16384), and fewer than 128 heads (B*H < 128) with skv >= 4096.
+    The workspace is a uint8 tensor on q's device of at least
+    workspace_bytes(...) bytes; when not given it is allocated here on every
+    such call (pass one to avoid that). workspace=False runs without one:
+    skv > 16384 then falls to the long-row kernel (about 0.46 TB/s on a
+    65535-key cache, against about 5 TB/s split), and the few-heads case
+    runs the decode kernel with one workgroup per head. Returns out, or
+    (out, row_max, row_sum) with stats (row_sum in Q15 units: 128 times the
+    uint8 table's sum)."""
     import torch
     B, H, Sq, C, D = _check_tensors(q, k, v, grouped=True)
     skv = C if skv is None else int(skv)

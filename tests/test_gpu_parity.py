@@ -190,21 +190,23 @@ def test_config_full_bit_exact(name):
     _check_full(W.make_config(name), probs=False)
 
 
-def test_llama_prefill_full_size_sampled_heads():
-    """Full-size causal prefill on the GPU; the oracle recomputes three heads
-    (each head is independent) including all their row statistics."""
+def test_llama_prefill_full_size_all_heads():
+    """Full-size causal prefill (B=1, H=32, S=4096, d=128) on the GPU, every
+    head compared with the oracle: the output of the plain launch, and the
+    output and row state (m_i, E_i) of one debug launch over the same
+    full-size workload (the launch configuration the benchmark times)."""
     w = W.make_config("llama_prefill")
     _say(f"case llama_prefill shape={w.shape}")
     out = _run(w)
-    heads = [(0, 0), (0, 13), (0, 31)]
-    sub = W.slice_heads(w, heads)
-    ref, m, E, P = O.forward(sub.q, sub.k, sub.v, sub.scales, sub.clip, True, stats=True)
-    for i, (b, h) in enumerate(heads):
-        _assert_equal(f"out head {h}", out[b, h], ref[i, 0])
-    o2, rm, rs, _ = _run(sub, debug=True)
-    _assert_equal("row_max", rm, m)
-    _assert_equal("row_sum", rs, E)
-    _assert_equal("out(debug)", o2, ref)
+    o2, rm, rs, _ = _run(w, debug=True)
+    prm = O.derive_params(w.D, *w.scales, w.clip)
+    for h in range(w.H):
+        ref, m, E, _P = O.head_forward(w.q[0, h], w.k[0, h], w.v[0, h], prm, True)
+        _assert_equal(f"out head {h}", out[0, h], ref)
+        _assert_equal(f"out(debug) head {h}", o2[0, h], ref)
+        _assert_equal(f"row_max head {h}", rm[0, h], m)
+        _assert_equal(f"row_sum head {h}", rs[0, h], E)
+    _say(f"llama_prefill: {w.H} of {w.H} heads bit-exact")
 
 
 def test_decode_full_size_bit_exact():

@@ -75,8 +75,8 @@ def test_tiny_stages():
     _check(W.make_config("tiny"))
 
 
-def test_bert_stages_sampled_heads():
-    _check(W.make_config("bert"), heads=[(0, 0), (3, 7), (7, 11)])
+def test_bert_stages_all_heads():
+    _check(W.make_config("bert"))
 
 
 STAGE_CASES = [
