@@ -354,7 +354,7 @@ def variants(steps=None):
             try:
                 ia.derive_params_ex(w.D, w.scales, w.clip, n)
             except ia.IntAttnError:
-                row[str(n)] = {"refused": "index multiplier outside [2^-16, 2^-1) for this table"}
+                row[str(n)] = {"refused": "index multiplier outside [2^-24, 2^14) for this table"}
                 continue
             fn = lambda n=n: ia.forward_ex(q, k, v, w.scales, w.clip, w.causal, n, out=out)
             us = _time_calls(fn, stream, steps or (200 if cfg == "bert" else 30))

@@ -17,10 +17,12 @@
  * is the reading the library implements, bit for bit):
  *   alpha = s_q*s_k/sqrt(D), delta = clip/31, mu = alpha/delta   (binary64)
  *   lut[k] = rint(2^15 * exp(-k*delta)) for k < 31, lut[31] = 0
- *   M = rint(mu * 2^24), required 2^-16 <= mu < 2^-1
+ *   required 2^-24 <= mu < 2^14; M = rint(mu * 2^sh) with sh = 24 for
+ *   mu < 1/2, else sh = 23 - e for mu = m 2^e, m in [1/2, 1) (frexp), so
+ *   that M <= 2^23 always (M in [2^22, 2^23] from mu = 1/2 on)
  *   s_ij = sum_d q_id k_jd                        (int32)
  *   m_i = max over allowed j of s_ij
- *   idx_ij = min(31, ((m_i - s_ij)*M + 2^23) >> 24), 31 for masked keys
+ *   idx_ij = min(31, ((m_i - s_ij)*M + 2^(sh-1)) >> sh), 31 for masked keys
  *   E_i = sum_j lut[idx_ij]                        (< 2^31)
  *   R_i = (255*2^23 + E_i/2) / E_i                  (integer division)
  *   p_ij = (lut[idx_ij]*R_i + 2^22) >> 23           (uint8)
@@ -76,7 +78,7 @@ typedef struct intattn_scales {
 typedef struct intattn_params {
     uint16_t lut[32];   /* exp table, lut[0] = 32768, lut[31] = 0           */
     int32_t  idx_mul;   /* M                                                 */
-    int32_t  idx_shift; /* always 24                                         */
+    int32_t  idx_shift; /* sh: 24 for mu < 1/2, 9..23 from mu = 1/2 on       */
     int32_t  x_clip;    /* smallest m - s that lands in slot 31              */
     int32_t  req_shift; /* sh_o, 1 .. 63                                     */
     int64_t  req_mul;   /* M_o                                               */
@@ -90,7 +92,7 @@ enum {
     INTATTN_E_DIM   = -3,  /* D not supported by the device kernels         */
     INTATTN_E_SCALE = -4,  /* a scale is not finite and > 0                  */
     INTATTN_E_CLIP  = -5,  /* clip is not finite and > 0                     */
-    INTATTN_E_RANGE = -6,  /* mu outside [2^-16, 2^-1) or sh_o outside 1..63 */
+    INTATTN_E_RANGE = -6,  /* mu outside [2^-24, 2^14) or sh_o outside 1..63 */
     INTATTN_E_HIP   = -7,  /* the HIP runtime reported an error              */
     INTATTN_E_ALIGN = -8,  /* a tensor pointer is not 16-byte aligned        */
     INTATTN_E_WORKSPACE = -9  /* workspace smaller than intattn_workspace_bytes,
@@ -136,9 +138,10 @@ int intattn_forward_debug(const int8_t* q, const int8_t* k, const int8_t* v, int
  * memory and say very large attention heads may need finer tables. With
  * lut_size N in {32, 64, 128} every step above is unchanged except
  *   delta = clip/(N-1), lut[k] = rint(2^15 exp(-k delta)) for k < N-1,
- *   lut[N-1] = 0, idx = min(N-1, ((m - s)*M + 2^23) >> 24),
- * with mu = alpha/delta (still required in [2^-16, 2^-1), so a finer table
- * admits proportionally smaller alpha). N = 32 is the specification above.
+ *   lut[N-1] = 0, idx = min(N-1, ((m - s)*M + 2^(sh-1)) >> sh),
+ * with (M, sh) from mu = alpha/delta as above (mu grows with N, so a finer
+ * table reaches the narrower-fraction form at smaller alpha). N = 32 is the
+ * specification above.
  * Grouped K/V heads (decoder serving: grouped-query and multi-query
  * attention; the pages do not describe this step): k and v hold kv_heads
  * heads, [B, kv_heads, Skv, D], and query head h reads K/V head
@@ -189,7 +192,7 @@ typedef struct intattn_params_ex {
                            lut_bits 8; entry lut_size-1 is 0); the rest 0   */
     int32_t  lut_size;
     int32_t  idx_mul;   /* M                                                 */
-    int32_t  idx_shift; /* always 24                                         */
+    int32_t  idx_shift; /* sh: 24 for mu < 1/2, 9..23 from mu = 1/2 on       */
     int32_t  x_clip;    /* smallest m - s that lands in slot lut_size-1      */
     int32_t  req_shift; /* sh_o, 1 .. 63                                     */
     int64_t  req_mul;   /* M_o                                               */

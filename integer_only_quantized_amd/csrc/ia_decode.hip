@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kDecodeThreads * QH) void ia_decode_kernel(
     // then skv_pad bytes of P (uint16 P: 2 per key)
     int32_t* const s_score = dsm;
     uint8_t* const s_p = reinterpret_cast<uint8_t*>(dsm + QH * skv_pad);
-    __shared__ uint16_t s_lut[kIaMaxLut];     // exp table (N <= 128 entries, rest 0)
+    __shared__ uint16_t s_lut[kIaTabEntries];  // exp table by slot, or the direct table by gap (rest 0)
     __shared__ int32_t s_red[P16 ? 2 : QH][NW][D];
     __shared__ int32_t s_scal[QH][3 * NW];     // per wave: row max, row sum, sum of p (uint16 P: low bytes)
 
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kDecodeThreads * QH) void ia_decode_kernel(
         if (lane == 0) s_scal[h][wave] = tmax[h];
     }
     __syncthreads();
-    int32_t m[QH], lo[QH], negM = -P.idx_mul;
+    int32_t m[QH], lo[QH], negM = -P.tab_mul;
     uint32_t Cm[QH];
 #pragma unroll
     for (int h = 0; h < QH; ++h) {
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kDecodeThreads * QH) void ia_decode_kernel(
 #pragma unroll
         for (int w = 1; w < NW; ++w) m[h] = max(m[h], s_scal[h][w]);
         lo[h] = m[h] - P.x_clip;
-        Cm[h] = static_cast<uint32_t>(m[h]) * static_cast<uint32_t>(P.idx_mul) + (1u << 23);
+        Cm[h] = static_cast<uint32_t>(m[h]) * static_cast<uint32_t>(P.tab_mul) + P.tab_half;
     }
 
     // ---- C: slots and row sum, then probabilities ------------------------------
@@ -130,8 +130,7 @@ __global__ __launch_bounds__(kDecodeThreads * QH) void ia_decode_kernel(
     for (int j = tid; j < P.Skv; j += NT) {
 #pragma unroll
         for (int h = 0; h < QH; ++h) {
-            const int32_t sp = max(s_score[h * skv_pad + j], lo[h]);
-            const uint32_t slot = (Cm[h] + static_cast<uint32_t>(__mul24(sp, negM))) >> 24;
+            const uint32_t slot = slot_of(s_score[h * skv_pad + j], lo[h], Cm[h], negM, P.tab_shift);
             E[h] += s_lut[slot];
             s_score[h * skv_pad + j] = static_cast<int32_t>(slot);
         }

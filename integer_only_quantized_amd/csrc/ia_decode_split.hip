@@ -139,21 +139,21 @@ __global__ __launch_bounds__(kSplitThreads) void ia_dsplit_scores_kernel(
 __global__ __launch_bounds__(kSplitThreads) void ia_dsplit_sums_kernel(const IaKernelParams P,
                                                                        InvariantDiv nchunks_div, int nchunks,
                                                                        int chunk, SplitWs ws) {
-    __shared__ uint16_t s_lut[kIaMaxLut];
+    __shared__ uint16_t s_lut[kIaTabEntries];
     __shared__ int32_t red[kSplitNW];
     const int tid = threadIdx.x;
     if (tid < 64) fill_lut_u16(P, s_lut, tid);
     const SplitBlock sb = split_block(nchunks_div, P.Skv, chunk);
     const int32_t m = split_row_max(ws, sb.head, nchunks);
     const int32_t lo = m - P.x_clip;
-    const uint32_t Cm = static_cast<uint32_t>(m) * static_cast<uint32_t>(P.idx_mul) + (1u << 23);
-    const int32_t negM = -P.idx_mul;
+    const uint32_t Cm = static_cast<uint32_t>(m) * static_cast<uint32_t>(P.tab_mul) + P.tab_half;
+    const int32_t negM = -P.tab_mul;
     __syncthreads();
     const int32_t* srow = ws.scores + static_cast<size_t>(sb.head) * P.Skv;
     uint32_t E = 0;
     for (int j = sb.k0 + tid; j < sb.k1; j += kSplitThreads) {
         const int32_t sp = max(srow[j], lo);
-        E += s_lut[(Cm + static_cast<uint32_t>(__mul24(sp, negM))) >> 24];
+        E += s_lut[(Cm + static_cast<uint32_t>(__mul24(sp, negM))) >> P.tab_shift];
     }
     E = block_sum(E, red);
     if (tid == 0) ws.csum[static_cast<size_t>(sb.head) * nchunks + sb.chunk] = E;
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kSplitThreads) void ia_dsplit_pv_kernel(
     constexpr int KEYS_IT = 4 * GPW * kSplitNW;
     constexpr int STEP = kSplitUnroll * KEYS_IT;
     static_assert(kSplitChunkMin % STEP == 0, "chunks hold whole key steps");
-    __shared__ uint16_t s_lut[kIaMaxLut];
+    __shared__ uint16_t s_lut[kIaTabEntries];
     __shared__ __attribute__((aligned(16))) uint8_t s_p[kSplitChunk * (P16 ? 2 : 1)];
     __shared__ int32_t s_red[P16 ? 2 : 1][kSplitNW][D];
     __shared__ int32_t red[kSplitNW];
@@ -188,8 +188,8 @@ __global__ __launch_bounds__(kSplitThreads) void ia_dsplit_pv_kernel(
         row_sum[sb.head] = E;
     }
     const int32_t lo = m - P.x_clip;
-    const uint32_t Cm = static_cast<uint32_t>(m) * static_cast<uint32_t>(P.idx_mul) + (1u << 23);
-    const int32_t negM = -P.idx_mul;
+    const uint32_t Cm = static_cast<uint32_t>(m) * static_cast<uint32_t>(P.tab_mul) + P.tab_half;
+    const int32_t negM = -P.tab_mul;
     __syncthreads();
     // p of the chunk's keys into LDS (0 past the last key, up to whole steps)
     const int n = sb.k1 - sb.k0;
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kSplitThreads) void ia_dsplit_pv_kernel(
         uint32_t p = 0;
         if (j < n) {
             const int32_t sp = max(srow[j], lo);
-            const uint32_t e = s_lut[(Cm + static_cast<uint32_t>(__mul24(sp, negM))) >> 24];
+            const uint32_t e = s_lut[(Cm + static_cast<uint32_t>(__mul24(sp, negM))) >> P.tab_shift];
             p = P16 ? (e * R + (1u << 15)) >> 16 : (e * R + (1u << 22)) >> 23;
         }
         if constexpr (P16) {

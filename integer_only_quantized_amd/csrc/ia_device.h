@@ -71,13 +71,17 @@ __device__ __forceinline__ int xcd_local_block(int bid, int n) {
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int i) { return (w >> (8 * i)) & 0xffu; }
 
-// Slot index of a score under the row constants: the clip is s' = max(s, lo)
-// with lo = m - x_clip; then idx = ((m - s')*M + 2^23) >> 24, computed as
-// (C - s'*M) mod 2^32 with C = m*M + 2^23 mod 2^32 (the true value is below
-// 2^30, and every operand fits the 24-bit signed multiplier).
-__device__ __forceinline__ uint32_t slot_of(int32_t s, int32_t lo, uint32_t C, int32_t negM) {
+// Table index of a score under the row constants: the clip is s' = max(s, lo)
+// with lo = m - x_clip, so the gap x' = m - s' is at most x_clip; then
+// idx = (x' * tab_mul + tab_half) >> tab_shift, computed as
+// (C - s' * tab_mul) mod 2^32 >> tab_shift with C = m * tab_mul + tab_half
+// mod 2^32 and negM = -tab_mul (the true value is below 2^31, and every
+// operand fits the 24-bit signed multiplier). With (M, 2^23, 24) this is the
+// slot (x'*M + 2^23) >> 24, for the exp table by slot; with (1, 0, 0) it is
+// x' itself, for the direct table by gap (from mu = 1/2 on).
+__device__ __forceinline__ uint32_t slot_of(int32_t s, int32_t lo, uint32_t C, int32_t negM, uint32_t shift) {
     const int32_t sp = max(s, lo);
-    return (C + static_cast<uint32_t>(__mul24(sp, negM))) >> 24;
+    return (C + static_cast<uint32_t>(__mul24(sp, negM))) >> shift;
 }
 
 // Saturating slot word for a table of N entries: with y = s - m <= 0, a
@@ -105,6 +109,8 @@ __device__ __forceinline__ uint32_t slot_word_sat(int32_t y, int32_t negMk, int3
 //   KM = 1: u16[128], byte = slot, address 2 * byte.
 // u16 entries past slot N - 1 are 0 (the clipped tail); a saturated byte
 // (127) always lands on such an entry or on slot N - 1.
+//   KM = 0 (from mu = 1/2 on, see entry_addr): u16[256] indexed by the
+//          clipped gap itself.
 template <int KM>
 __device__ __forceinline__ uint32_t lut_byte_addr(uint32_t t) {
     uint32_t a;
@@ -117,6 +123,25 @@ __device__ __forceinline__ uint32_t lut_byte_addr(uint32_t t) {
             : "=v"(a) : "v"(t), "s"(m));
     }
     return a;
+}
+
+// LDS address of the table entry of a relative score y = s - m <= 0 (a
+// masked key has y = -2^23), for layout KM with a = P.ent_a, b = P.ent_b:
+//   KM = 4, 2, 1: the top byte of the saturating slot word (a = -kM,
+//     b = k 2^23), two VALU ops;
+//   KM = 0: from mu = 1/2 on a score unit moves half a bin or more, so the
+//     clip point x_clip is at most 2N - 3 units from the row max and the
+//     table is indexed by the clipped gap x' = min(-y, x_clip) itself
+//     (u16 entries, entry x' = lut[slot(x')], entry x_clip = 0): a = -x_clip,
+//     address 2 x' = -2 max(y, a), again two VALU ops.
+template <int KM>
+__device__ __forceinline__ uint32_t entry_addr(int32_t y, int32_t a, int32_t b) {
+    if constexpr (KM == 0) {
+        (void)b;
+        return static_cast<uint32_t>(__mul24(max(y, a), -2));
+    } else {
+        return lut_byte_addr<KM>(slot_word_sat(y, a, b));
+    }
 }
 
 // int32 accumulator -> int8: sign(a) * min(127, (|a|*M_o + 2^(sh_o-1)) >> sh_o).
@@ -163,12 +188,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 // registers); writing them lane by lane keeps a per-lane index from turning
 // into a vector load of the argument segment (whose wait would also cover any
 // loads issued before it).
-template <int NW = kIaMaxLut / 2>
+template <int NW = kIaMaxLut / 2, int OFF = 0>
 __device__ __forceinline__ uint32_t lut_words(const IaKernelParams& P) {
-    static_assert(NW % 16 == 0 && NW <= kIaMaxLut / 2, "words come in groups of 16");
+    static_assert(NW % 16 == 0 && NW <= 64 && OFF + NW <= kIaTabEntries / 2, "words come in groups of 16");
     uint32_t all = 0;
     // the lane number must be an inline constant (one scalar operand per VOP3)
-#define IA_WL(i) asm volatile("v_writelane_b32 %0, %1, " #i : "+v"(all) : "s"(P.lut2[i]));
+#define IA_WL(i) asm volatile("v_writelane_b32 %0, %1, " #i : "+v"(all) : "s"(P.lut2[OFF + i]));
     IA_WL(0) IA_WL(1) IA_WL(2) IA_WL(3) IA_WL(4) IA_WL(5) IA_WL(6) IA_WL(7)
     IA_WL(8) IA_WL(9) IA_WL(10) IA_WL(11) IA_WL(12) IA_WL(13) IA_WL(14) IA_WL(15)
     if constexpr (NW > 16) {
@@ -193,22 +218,28 @@ __device__ __forceinline__ uint32_t lut_value(const IaKernelParams& P, uint32_t 
     return idx < P.lut_size ? e : 0u;
 }
 
-// Fills the u16[128] exp table at t (LDS) from one whole wave.
+// Fills the u16 table at t (LDS, kIaTabEntries entries) from one whole wave:
+// the exp table by slot (entries 0..127; the host leaves entries past N - 1
+// zero), and entries 128..255 as well for the direct table (slot_k = 0).
 __device__ __forceinline__ void fill_lut_u16(const IaKernelParams& P, uint16_t* t, int lane) {
-    const uint32_t words = lut_words(P);
-    t[lane] = static_cast<uint16_t>(lut_value(P, words, lane));
-    t[64 + lane] = static_cast<uint16_t>(lut_value(P, words, 64 + lane));
+    uint32_t* t32 = reinterpret_cast<uint32_t*>(t);
+    t32[lane] = lut_words<64, 0>(P);
+    if (P.slot_k == 0) t32[64 + lane] = lut_words<64, 64>(P);
 }
 
-// Fills the exp table of layout KM (see lut_byte_addr) at LDS t (256 bytes)
-// from one whole wave.
+// Fills the table of layout KM (see lut_byte_addr, entry_addr) at LDS t
+// (512 bytes) from one whole wave.
 template <int KM>
 __device__ __forceinline__ void fill_lut_table(const IaKernelParams& P, void* t, int lane) {
+    uint32_t* t32 = static_cast<uint32_t*>(t);
     if constexpr (KM == 4) {
         const uint32_t v = lut_value(P, lut_words<16>(P), lane & 31);   // N = 32: words 0..15
-        if (lane < 32) static_cast<uint32_t*>(t)[lane] = v;
+        if (lane < 32) t32[lane] = v;
+    } else if constexpr (KM == 0) {
+        t32[lane] = lut_words<64, 0>(P);
+        t32[64 + lane] = lut_words<64, 64>(P);
     } else {
-        fill_lut_u16(P, static_cast<uint16_t*>(t), lane);
+        t32[lane] = lut_words<64, 0>(P);
     }
 }
 
@@ -281,7 +312,7 @@ __device__ __forceinline__ uint32_t lds_u16(uint32_t addr) {
     return *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(static_cast<uintptr_t>(addr));
 }
 
-// Table entry at a byte address produced by lut_byte_addr<KM>.
+// Table entry at a byte address produced by entry_addr<KM>.
 template <int KM>
 __device__ __forceinline__ uint32_t lut_load(uint32_t addr) {
     if constexpr (KM == 4) return lds_u32(addr);

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void ia_general_kernel(
 
     __shared__ __attribute__((aligned(16))) int8_t sk[kKeyTile * KStride];
     __shared__ __attribute__((aligned(16))) int8_t svt[D * kVtStride];
-    __shared__ uint16_t slut[kIaMaxLut];      // exp table (N <= 128 entries, rest 0)
+    __shared__ uint16_t slut[kIaTabEntries];  // exp table by slot, or the direct table by gap (rest 0)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -154,8 +154,13 @@ __global__ __launch_bounds__(256) void ia_general_kernel(
     }
     mrow = max(mrow, __shfl_xor(mrow, 32));
     const int32_t lo = mrow - P.x_clip;
-    const uint32_t C = static_cast<uint32_t>(mrow) * static_cast<uint32_t>(P.idx_mul) + (1u << 23);
-    const int32_t negM = -P.idx_mul;
+    const uint32_t C = static_cast<uint32_t>(mrow) * static_cast<uint32_t>(P.tab_mul) + P.tab_half;
+    const int32_t negM = -P.tab_mul;
+    const uint32_t tsh = static_cast<uint32_t>(P.tab_shift);
+    // table entry of a score; a masked key (INT_MIN, never an int8 product)
+    // has entry 0 outright: with a very small bin multiplier the clip point
+    // lies beyond any score gap, and lo need not fit the 24-bit multiply
+    auto entry = [&](int32_t sc) -> uint32_t { return sc == INT_MIN ? 0u : slut[slot_of(sc, lo, C, negM, tsh)]; };
 
     // ---- pass 2: slot index, table lookup, row sum ----------------------
     uint32_t E = 0;
@@ -167,8 +172,8 @@ __global__ __launch_bounds__(256) void ia_general_kernel(
         scores(t, s0, s1);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            E += slut[slot_of(s0[r], lo, C, negM)];
-            E += slut[slot_of(s1[r], lo, C, negM)];
+            E += entry(s0[r]);
+            E += entry(s1[r]);
         }
     }
     E += __shfl_xor(E, 32);
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(256) void ia_general_kernel(
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int r = 4 * w4 + c;
-                    const uint32_t e = slut[slot_of(s[kb][r], lo, C, negM)];
+                    const uint32_t e = entry(s[kb][r]);
                     const uint32_t p = (e * R + (1u << 22)) >> 23;
                     word |= p << (8 * c);
                     if (kDebug && probs != nullptr) {

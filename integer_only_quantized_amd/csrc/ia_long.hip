@@ -54,12 +54,14 @@ constexpr int kLongWaves = 4;
 constexpr int kLongRows = 32 * kLongWaves;   // query rows per workgroup
 constexpr int kLongTile = 64;                // keys per tile
 constexpr int kStages = 3;                   // LDS ring depth
-constexpr int kLutEntries = 128;
+// Table words in LDS for layout KM: 64 (u32[32] or u16[128]), 128 for the
+// direct table (u16[256]).
+constexpr int table_words(int KM) { return KM == 0 ? kIaTabEntries / 2 : kIaMaxLut / 2; }
 
-template <int D>
+template <int D, int KM>
 struct LongLds {
     static constexpr int TB = kLongTile * D;        // bytes per K or V tile
-    uint32_t lut[kLutEntries / 2];                  // exp table (layout KM); first member: LDS address 0
+    uint32_t lut[table_words(KM)];                  // exp table (layout KM); first member: LDS address 0
     int32_t colsum[kLongWaves][D];
     int8_t k[kStages][TB];
     int8_t v[kStages][TB];
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, const int8_t* __restrict__ v,
     int8_t* __restrict__ out, const IaKernelParams P, int nqb, InvariantDiv map_div, int32_t* __restrict__ row_max,
     uint32_t* __restrict__ row_sum) {
-    using L = LongLds<D>;
+    using L = LongLds<D, KM>;
     constexpr int KS = D / 32;
     constexpr int DB = D / 32;
     constexpr int CPR = D / 16;                              // 16-byte chunks per row
@@ -267,11 +269,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     v16i cinit;
 #pragma unroll
     for (int r = 0; r < 16; ++r) cinit[r] = -mrow;
-    const int32_t negMs = -P.slot_k * P.idx_mul;
-    const int32_t halfs = P.slot_k << 23;
-    auto table_entry = [&](int32_t y) -> uint32_t {
-        return lut_load<KM>(lut_byte_addr<KM>(slot_word_sat(y, negMs, halfs)));
-    };
+    auto table_entry = [&](int32_t y) -> uint32_t { return lut_load<KM>(entry_addr<KM>(y, P.ent_a, P.ent_b)); };
     constexpr int32_t kMasked = -(1 << 23);   // y of a masked key: saturates to the last slot
 
     // ---- pass 2: row sum of the table entries ------------------------------
@@ -417,7 +415,7 @@ template <int D, int KM, bool P16>
 int launch_long_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, const IaKernelParams& kp,
                   hipStream_t s, int nqb, unsigned blocks, int32_t* row_max, uint32_t* row_sum) {
     static std::atomic<uint64_t> lds_set{0};
-    const size_t shm = sizeof(LongLds<D>);
+    const size_t shm = sizeof(LongLds<D, KM>);
     const int st = ensure_dynamic_lds(reinterpret_cast<const void*>(&ia_long_kernel<D, KM, P16>),
                                       static_cast<int>(shm), lds_set);
     if (st != INTATTN_OK) return st;
@@ -443,7 +441,8 @@ int launch_long(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, 
         constexpr bool PP = decltype(p16_c)::value;
         if (kp.slot_k == 4) return launch_long_t<DD, 4, PP>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
         if (kp.slot_k == 2) return launch_long_t<DD, 2, PP>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
-        return launch_long_t<DD, 1, PP>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
+        if (kp.slot_k == 1) return launch_long_t<DD, 1, PP>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
+        return launch_long_t<DD, 0, PP>(q, k, v, out, kp, s, nqb, nb, row_max, row_sum);
     };
     using D64 = std::integral_constant<int, 64>;
     using D128 = std::integral_constant<int, 128>;

@@ -52,13 +52,17 @@ namespace {
 template <int NBH, bool SKIP>
 constexpr bool split_k_staging() { return NBH >= 8 && !SKIP; }
 
-template <int D, int NBH>
+// Table words in LDS for layout KM: 64 (u32[32] or u16[128]), 128 for the
+// direct table (u16[256]).
+constexpr int table_words(int KM) { return KM == 0 ? kIaTabEntries / 2 : kIaMaxLut / 2; }
+
+template <int D, int NBH, int KM>
 struct ShortLds {
     static constexpr int DB = D / 32;
     static constexpr int KVBytes = 2 * NBH * 32 * D;                 // K (later V) of both halves
     static constexpr int XOBytes = 4 * (DB / 2) * 16 * 64 * 4;       // output partials, 4 waves
     static constexpr int Region = KVBytes > XOBytes ? KVBytes : XOBytes;
-    uint32_t lut[kIaMaxLut / 2];             // exp table (layout KM); first member: LDS address 0
+    uint32_t lut[table_words(KM)];           // exp table (layout KM); first member: LDS address 0
     int32_t xm[2][2][32];                    // row max exchange [query group][half][row]
     uint32_t xe[2][2][32];                   // row sum exchange
     int32_t xcs[4][D];                       // column-sum partials, one per wave
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, const int8_t* __restrict__ v,
     int8_t* __restrict__ out, const IaKernelParams P, int nqb, int32_t* __restrict__ row_max,
     uint32_t* __restrict__ row_sum) {
-    using L = ShortLds<D, NBH>;
+    using L = ShortLds<D, NBH, KM>;
     constexpr int KS = D / 32;
     constexpr int DB = D / 32;
     constexpr int HDB = DB / 2;                        // output column blocks finished per wave
@@ -283,8 +287,6 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     mrow = max(mrow, lds.xm[qg][half ^ 1][l32]);
 
     // ---- pass 2: slots, table entries, row sum; slot bytes kept ------------
-    const int32_t negMs = -P.slot_k * P.idx_mul;
-    const int32_t halfs = P.slot_k << 23;
     constexpr int32_t kMasked = -(1 << 23);   // y of a masked key: saturates to the last slot
     uint32_t ew[NBH][8];                 // table entries of this wave's keys, two a word
     uint32_t E = 0;
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
             mask(cur, kb0 + j, kMasked);
             uint32_t e[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) e[i] = lut_load<KM>(lut_byte_addr<KM>(slot_word_sat(cur[i], negMs, halfs)));
+            for (int i = 0; i < 16; ++i) e[i] = lut_load<KM>(entry_addr<KM>(cur[i], P.ent_a, P.ent_b));
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 ew[j][i] = entry_pair(e[2 * i], e[2 * i + 1]);
@@ -496,9 +498,11 @@ int launch_short_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* ou
     using K4 = std::integral_constant<int, 4>;
     using K2 = std::integral_constant<int, 2>;
     using K1 = std::integral_constant<int, 1>;
+    using K0 = std::integral_constant<int, 0>;
     if (kp.slot_k == 4) skip ? go(T{}, K4{}) : go(F{}, K4{});
     else if (kp.slot_k == 2) skip ? go(T{}, K2{}) : go(F{}, K2{});
-    else skip ? go(T{}, K1{}) : go(F{}, K1{});
+    else if (kp.slot_k == 1) skip ? go(T{}, K1{}) : go(F{}, K1{});
+    else skip ? go(T{}, K0{}) : go(F{}, K0{});
     return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
 }
 

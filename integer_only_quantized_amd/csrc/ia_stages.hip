@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void ia_index_softmax_kernel(const int32_t* __
                                                                uint32_t* __restrict__ row_sum,
                                                                const IaKernelParams P, long long rows,
                                                                InvariantDiv sq_div) {
-    __shared__ uint32_t lut[kIaMaxLut / 2];    // exp table, layout KM
+    __shared__ uint32_t lut[kIaTabEntries / 2];   // exp table, layout KM
     const int tid = threadIdx.x;
     if (tid < 64) fill_lut_table<KM>(P, lut, tid);   // wave 0, whole
     __syncthreads();
@@ -147,15 +147,12 @@ __global__ __launch_bounds__(256) void ia_index_softmax_kernel(const int32_t* __
         if (64 * c + lane < kend) m = max(m, s[c]);
     m = wave_max(m);
 
-    const int32_t negMs = -P.slot_k * P.idx_mul;
-    const int32_t halfs = P.slot_k << 23;
     uint32_t e[NCH];
     uint32_t E = 0;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int32_t y = 64 * c + lane < kend ? max(s[c] - m, -(1 << 23)) : -(1 << 23);
-        const uint32_t t = slot_word_sat(y, negMs, halfs);
-        e[c] = lut_load<KM>(lds_addr(lut) + lut_byte_addr<KM>(t));
+        e[c] = lut_load<KM>(lds_addr(lut) + entry_addr<KM>(y, P.ent_a, P.ent_b));
         E += e[c];
     }
     E = wave_sum(E);
@@ -381,8 +378,11 @@ int launch_isoftmax_n(int nch, const int32_t* scores, uint8_t* probs, int32_t* r
         else if (kp.slot_k == 2)
             hipLaunchKernelGGL((ia_index_softmax_kernel<NCH, 2>), dim3(blocks), dim3(256), 0, s, scores, probs,
                                row_max, row_sum, kp, rows, invariant_div(static_cast<uint32_t>(kp.Sq)));
-        else
+        else if (kp.slot_k == 1)
             hipLaunchKernelGGL((ia_index_softmax_kernel<NCH, 1>), dim3(blocks), dim3(256), 0, s, scores, probs,
+                               row_max, row_sum, kp, rows, invariant_div(static_cast<uint32_t>(kp.Sq)));
+        else
+            hipLaunchKernelGGL((ia_index_softmax_kernel<NCH, 0>), dim3(blocks), dim3(256), 0, s, scores, probs,
                                row_max, row_sum, kp, rows, invariant_div(static_cast<uint32_t>(kp.Sq)));
         return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
     }

@@ -43,10 +43,10 @@ int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scale
     const int rows = kv_capacity == 0 ? shape->Skv : kv_capacity;
     if (static_cast<double>(shape->B) * hkv * rows * shape->D > 9.0e15) return INTATTN_E_SHAPE;
     uint16_t lut[kIaMaxLut] = {};
-    int32_t idx_mul = 0, x_clip = 0, req_shift = 0;
+    int32_t idx_mul = 0, idx_shift = 0, x_clip = 0, req_shift = 0;
     int64_t req_mul = 0;
-    st = intattn_derive_core(shape, scales, clip, lut_size, lut, &idx_mul, &x_clip, &req_shift, &req_mul,
-                             prob_bits, lut_bits);
+    st = intattn_derive_core(shape, scales, clip, lut_size, lut, &idx_mul, &idx_shift, &x_clip, &req_shift,
+                             &req_mul, prob_bits, lut_bits);
     if (st != INTATTN_OK) return st;
     kp->B = shape->B;
     kp->H = shape->H;
@@ -54,26 +54,65 @@ int derive_kernel_params(const intattn_shape* shape, const intattn_scales* scale
     kp->Skv = shape->Skv;
     kp->causal = causal ? 1 : 0;
     kp->idx_mul = idx_mul;
+    kp->idx_shift = idx_shift;
     kp->x_clip = x_clip;
     kp->req_shift = req_shift;
     kp->req_mul = static_cast<uint32_t>(req_mul);
     kp->lut_size = lut_size;
-    // slot word t = sat(y * -kM + k * 2^23): the largest k in {4, 2, 1} with
-    // k <= 128/N (the byte holds k * (N - 1) + k - 1) and kM within the
-    // 24-bit signed operand; k = 4 only for the 32-entry table
-    const int64_t m = idx_mul;
-    int k = 1;
-    if (lut_size == 32 && 4 * m < (int64_t(1) << 23)) k = 4;
-    else if (lut_size <= 64 && 2 * m < (int64_t(1) << 23)) k = 2;
-    kp->slot_k = k;
-    kp->slot_k_log2 = k == 4 ? 2 : k - 1;
+    uint16_t tab[kIaTabEntries] = {};
+    if (idx_shift == 24) {
+        // slot word t = sat(y * -kM + k * 2^23): the largest k in {4, 2, 1}
+        // with k <= 128/N (the byte holds k * (N - 1) + k - 1) and kM within
+        // the 24-bit signed operand (M <= 2^23 and -M >= -2^23 for k = 1);
+        // k = 4 only for the 32-entry table
+        const int64_t m = idx_mul;
+        int k = 1;
+        if (lut_size == 32 && 4 * m < (int64_t(1) << 23)) k = 4;
+        else if (lut_size <= 64 && 2 * m < (int64_t(1) << 23)) k = 2;
+        kp->slot_k = k;
+        kp->slot_k_log2 = k == 4 ? 2 : k - 1;
+        kp->ent_a = -k * idx_mul;
+        kp->ent_b = k << 23;
+        kp->tab_mul = idx_mul;
+        kp->tab_half = 1u << 23;
+        kp->tab_shift = 24;
+        for (int i = 0; i < kIaMaxLut; ++i) tab[i] = lut[i];
+        // Masked keys enter the slot word as y = -2^23. When k(M + 1) >= 256
+        // the word saturates (slot N - 1 or past it: entry 0). Below that
+        // (M < 64 for N = 32) it lands on slot floor((M + 1) / 2), which no
+        // allowed key reaches: an int8 score gap is at most 2 * 128 * 127^2,
+        // whose slot floor((4129024 M + 2^23) / 2^24) is smaller for every
+        // M >= 1 (checked for each M below 256). Those unreachable entries are
+        // made 0, so masked keys drop out of the sum as the specification
+        // says.
+        if (k * (static_cast<int64_t>(idx_mul) + 1) < 256)
+            for (int i = (idx_mul + 1) / 2; i < lut_size; ++i) tab[i] = 0;
+    } else {
+        // From mu = 1/2 on a score unit moves half a bin or more, so the
+        // clip point is at most 2N - 3 units from the row max: the table is
+        // indexed by the clipped gap x' = min(m - s, x_clip) itself,
+        // entry x' = lut[min(N-1, (x'*M + 2^(sh-1)) >> sh)], and entry
+        // x_clip is 0 (the sparse tail).
+        if (x_clip < 1 || x_clip >= kIaTabEntries) return INTATTN_E_RANGE;   // not reached (x_clip <= 2N-3)
+        for (int x = 0; x <= x_clip; ++x) {
+            const int64_t slot = (static_cast<int64_t>(x) * idx_mul + (int64_t(1) << (idx_shift - 1))) >> idx_shift;
+            tab[x] = lut[slot < lut_size - 1 ? slot : lut_size - 1];
+        }
+        kp->slot_k = 0;
+        kp->slot_k_log2 = 0;
+        kp->ent_a = -x_clip;
+        kp->ent_b = 0;
+        kp->tab_mul = 1;
+        kp->tab_half = 0;
+        kp->tab_shift = 0;
+    }
     kp->kv_group = shape->H > 0 ? shape->H / hkv : 1;
     kp->kvg_div = ia::invariant_div(static_cast<uint32_t>(kp->kv_group));
     kp->h_div = ia::invariant_div(static_cast<uint32_t>(shape->H > 0 ? shape->H : 1));
     kp->kv_rows = rows;
     kp->prob_bits = prob_bits;
-    for (int i = 0; i < kIaMaxLut / 2; ++i)
-        kp->lut2[i] = static_cast<uint32_t>(lut[2 * i]) | (static_cast<uint32_t>(lut[2 * i + 1]) << 16);
+    for (int i = 0; i < kIaTabEntries / 2; ++i)
+        kp->lut2[i] = static_cast<uint32_t>(tab[2 * i]) | (static_cast<uint32_t>(tab[2 * i + 1]) << 16);
     return INTATTN_OK;
 }
 

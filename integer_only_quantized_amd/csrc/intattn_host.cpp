@@ -26,7 +26,8 @@ constexpr int kLutSize = 32;
 constexpr double kLutOne = 32768.0;   // Q15 entry for a zero relative score
 constexpr double kLut8One = 255.0;    // uint8 entry for a zero relative score
 constexpr int kLut8Scale = 128;       // uint8 entries in Q15 units
-constexpr int kIdxShift = 24;
+constexpr int kIdxShift = 24;        // bin-multiplier fraction bits below mu = 1/2
+constexpr int kIdxMulBits = 23;      // from mu = 1/2 on: the widest multiplier M <= 2^23
 constexpr int kReqFrac = 31;
 
 bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
@@ -92,9 +93,9 @@ int intattn_validate_shape(const intattn_shape* s, int causal) {
 }
 
 int intattn_derive_core(const intattn_shape* shape, const intattn_scales* sc, float clip, int lut_size,
-                        uint16_t* lut, int32_t* idx_mul, int32_t* x_clip, int32_t* req_shift, int64_t* req_mul,
-                        int prob_bits, int lut_bits) {
-    if (!shape || !sc || !lut || !idx_mul || !x_clip || !req_shift || !req_mul) return INTATTN_E_NULL;
+                        uint16_t* lut, int32_t* idx_mul, int32_t* idx_shift, int32_t* x_clip, int32_t* req_shift,
+                        int64_t* req_mul, int prob_bits, int lut_bits) {
+    if (!shape || !sc || !lut || !idx_mul || !idx_shift || !x_clip || !req_shift || !req_mul) return INTATTN_E_NULL;
     if (!valid_lut_size(lut_size) || !valid_lut_bits(lut_bits)) return INTATTN_E_RANGE;
     if (prob_bits != 8 && prob_bits != 16) return INTATTN_E_RANGE;
     if (shape->D < 1) return INTATTN_E_SHAPE;
@@ -110,11 +111,20 @@ int intattn_derive_core(const intattn_shape* shape, const intattn_scales* sc, fl
                          std::sqrt(static_cast<double>(shape->D));
     const double delta = c / static_cast<double>(n - 1);
     const double mu = alpha / delta;
-    if (!(mu >= std::ldexp(1.0, -16) && mu < 0.5)) return INTATTN_E_RANGE;
+    if (!(mu >= std::ldexp(1.0, -24) && mu < std::ldexp(1.0, 14))) return INTATTN_E_RANGE;
 
-    const int64_t M = static_cast<int64_t>(std::rint(std::ldexp(mu, kIdxShift)));
-    // x*M >= (2n-3)*2^23  <=>  slot >= n-1
-    const int64_t num = int64_t(2 * n - 3) << (kIdxShift - 1);
+    // M = rint(mu * 2^sh): sh = 24 below mu = 1/2 (M in [1, 2^23]); from
+    // 1/2 on, with mu = m 2^e (m in [1/2, 1)), sh = 23 - e so that
+    // M = rint(m 2^23) lies in [2^22, 2^23]
+    int sh = kIdxShift;
+    if (mu >= 0.5) {
+        int e = 0;
+        (void)std::frexp(mu, &e);
+        sh = kIdxMulBits - e;
+    }
+    const int64_t M = static_cast<int64_t>(std::rint(std::ldexp(mu, sh)));
+    // x*M >= (2n-3)*2^(sh-1)  <=>  slot >= n-1
+    const int64_t num = int64_t(2 * n - 3) << (sh - 1);
 
     // output multiplier: s_v / (P_one * s_o), P_one = 255 (uint8 P) or 65535
     const double p_one = prob_bits == 16 ? 65535.0 : 255.0;
@@ -133,6 +143,7 @@ int intattn_derive_core(const intattn_shape* shape, const intattn_scales* sc, fl
     if (lut_bits == 8)
         for (int i = 0; i < n; ++i) lut[i] = static_cast<uint16_t>(lut[i] * kLut8Scale);
     *idx_mul = static_cast<int32_t>(M);
+    *idx_shift = sh;
     *x_clip = static_cast<int32_t>((num + M - 1) / M);
     *req_shift = sh_o;
     *req_mul = Mo;
@@ -143,10 +154,9 @@ extern "C" int intattn_derive_params(const intattn_shape* shape, const intattn_s
                                      float clip, intattn_params* out) {
     if (!shape || !sc || !out) return INTATTN_E_NULL;
     intattn_params p{};
-    const int st = intattn_derive_core(shape, sc, clip, kLutSize, p.lut, &p.idx_mul, &p.x_clip, &p.req_shift,
-                                       &p.req_mul);
+    const int st = intattn_derive_core(shape, sc, clip, kLutSize, p.lut, &p.idx_mul, &p.idx_shift, &p.x_clip,
+                                       &p.req_shift, &p.req_mul);
     if (st != INTATTN_OK) return st;
-    p.idx_shift = kIdxShift;
     *out = p;
     return INTATTN_OK;
 }
@@ -156,13 +166,12 @@ extern "C" int intattn_derive_params_ex(const intattn_shape* shape, const intatt
                                         intattn_params_ex* out) {
     if (!shape || !sc || !out) return INTATTN_E_NULL;
     intattn_params_ex p{};
-    const int st = intattn_derive_core(shape, sc, clip, lut_size, p.lut, &p.idx_mul, &p.x_clip, &p.req_shift,
-                                       &p.req_mul, prob_bits, lut_bits);
+    const int st = intattn_derive_core(shape, sc, clip, lut_size, p.lut, &p.idx_mul, &p.idx_shift, &p.x_clip,
+                                       &p.req_shift, &p.req_mul, prob_bits, lut_bits);
     if (st != INTATTN_OK) return st;
     p.lut_size = lut_size;
     p.prob_bits = prob_bits;
     p.lut_bits = lut_bits;
-    p.idx_shift = kIdxShift;
     *out = p;
     return INTATTN_OK;
 }

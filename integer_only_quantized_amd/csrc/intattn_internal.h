@@ -13,37 +13,54 @@ int intattn_validate_shape(const intattn_shape* s, int causal);
 
 // Largest exp table of the variants (32 is the pages' table).
 constexpr int kIaMaxLut = 128;
+// Entries of the table the kernels receive: the exp table by slot (N <= 128
+// entries), or, from mu = 1/2 on, the direct table by clipped score gap
+// (X_clip + 1 <= 2N - 2 entries); the rest 0.
+constexpr int kIaTabEntries = 256;
 
 // Everything a kernel needs besides the tensor pointers, passed by value so
 // that it lands in kernel-argument (scalar) registers.
 struct IaKernelParams {
     int32_t B, H, Sq, Skv;
     int32_t causal;
-    int32_t idx_mul;     // M, < 2^23
+    int32_t idx_mul;     // M, <= 2^23
+    int32_t idx_shift;   // sh: slot = (x*M + 2^(sh-1)) >> sh, 24 below mu = 1/2, 9..23 above
     int32_t x_clip;      // smallest relative score that lands in the last slot
+    // Table index of a gap x' = min(m - s, x_clip) as the row-constant kernels
+    // (decode, general) compute it: (x' * tab_mul + tab_half) >> tab_shift,
+    // i.e. the slot (M, 2^23, 24), or x' itself for the direct table (1, 0, 0).
+    int32_t tab_mul;
+    uint32_t tab_half;
+    int32_t tab_shift;
+    // Operands of the table address for the layout slot_k (entry_addr):
+    // slot_k > 0: -k*M and k*2^23 (saturating slot word); 0: -x_clip and 0.
+    int32_t ent_a;
+    int32_t ent_b;
     int32_t req_shift;   // sh_o, 1..63
     uint32_t req_mul;    // M_o, in [2^30, 2^31)
     int32_t lut_size;    // N: 32, 64 or 128 entries; entry N-1 is 0
     int32_t slot_k;      // slot-word scale k and table layout: 4 (N = 32, 4M < 2^23),
-                         // 2 (N <= 64, 2M < 2^23) or 1
-    int32_t slot_k_log2; // log2(k)
+                         // 2 (N <= 64, 2M < 2^23), 1 (below mu = 1/2), or 0: the
+                         // direct table by clipped score gap (from mu = 1/2 on)
+    int32_t slot_k_log2; // log2(k) (0 for the direct table)
     int32_t kv_group;    // query heads per K/V head (1: one K/V head each)
     int32_t kv_rows;     // rows per K/V head in memory (>= Skv: a cache of that capacity)
     int32_t prob_bits;   // 8: uint8 probabilities; 16: the uint16 variant
     ia::InvariantDiv kvg_div;   // division by kv_group (query head -> K/V head)
     ia::InvariantDiv h_div;     // division by H (batch, head of a flat head index)
     ia::InvariantDiv qb_div;    // division by the launch's query-block count (set by the launcher)
-    uint32_t lut2[kIaMaxLut / 2];   // exp table, entries 2i and 2i+1 packed lo/hi
+    uint32_t lut2[kIaTabEntries / 2];   // table entries 2i and 2i+1 packed lo/hi (slot_k > 0:
+                                        // the exp table by slot; 0: by score gap 0..x_clip)
 };
 
 // Host derivation of every integer the kernels receive, for a table of
 // lut_size entries (32, 64 or 128) of lut_bits bits (16 or 8): the exp
-// table in Q15 units (8-bit entries times 128), M, the clip point and the
-// requantisation pair. Errors as intattn_derive_params (E_RANGE also for an
+// table in Q15 units (8-bit entries times 128), M and its shift, the clip
+// point and the requantisation pair. Errors as intattn_derive_params (E_RANGE also for an
 // unsupported lut_size, prob_bits or lut_bits).
 int intattn_derive_core(const intattn_shape* shape, const intattn_scales* sc, float clip, int lut_size,
-                        uint16_t* lut, int32_t* idx_mul, int32_t* x_clip, int32_t* req_shift, int64_t* req_mul,
-                        int prob_bits = 8, int lut_bits = 16);
+                        uint16_t* lut, int32_t* idx_mul, int32_t* idx_shift, int32_t* x_clip, int32_t* req_shift,
+                        int64_t* req_mul, int prob_bits = 8, int lut_bits = 16);
 
 namespace ia {
 

@@ -37,8 +37,8 @@ default):
     table a trade-off between accuracy and memory and says very large
     attention heads may need finer tables. lut_size N in {32, 64, 128}: bin
     width delta = clip/(N-1), entries for slots 0..N-2 as for N = 32, the
-    last slot N-1 the sparse tail (entry 0), idx = min(N-1, (x*M + 2^23) >> 24)
-    with M from mu = alpha/delta; everything after the table is unchanged.
+    last slot N-1 the sparse tail (entry 0), idx = min(N-1, (x*M + 2^(sh-1)) >> sh)
+    with (M, sh) from mu = alpha/delta; everything after the table is unchanged.
   * grouped K/V heads: kv_heads K/V heads shared by the H query heads in
     consecutive groups of G = H/kv_heads (query head h reads K/V head h//G);
     kv_heads = H is ordinary multi-head attention, 1 is multi-query.
@@ -76,7 +76,8 @@ import numpy as np
 LUT_SIZE = 32                 # the pages: a 32-entry exp table
 LUT_SIZES = (32, 64, 128)     # the finer-table variants
 LUT_ONE = 1 << 15             # Q15: table entry for a zero relative score
-IDX_SHIFT = 24                # fixed-point fraction bits of the bin multiplier
+IDX_SHIFT = 24                # fraction bits of the bin multiplier for mu < 1/2
+IDX_MUL_BITS = 23             # above: the widest multiplier, M <= 2^23
 P_ONE = 255                   # uint8 probabilities, target row sum 255
 R_SHIFT = 23                  # reciprocal fixed point: R = round(255*2^23 / E)
 P16_ONE = 65535               # uint16 probabilities (variant), target row sum 65535
@@ -86,8 +87,8 @@ LUT8_ONE = 255                # uint8 table variant: entry for a zero relative s
 LUT_BITS = (16, 8)            # table entry width: Q15 (the specification) or uint8
 REQ_FRAC = 31                 # requantisation multiplier normalised to [2^30, 2^31)
 SKV_MAX = 65535               # keeps E < 2^31 and every int32 accumulator exact
-MU_MIN = 2.0 ** -16           # bin multiplier range (index units per score unit)
-MU_MAX = 2.0 ** -1
+MU_MIN = 2.0 ** -24           # bin multiplier range (index units per score unit)
+MU_MAX = 2.0 ** 14
 REQ_SHIFT_MIN = 1
 REQ_SHIFT_MAX = 63
 
@@ -106,8 +107,8 @@ class OracleRangeError(ValueError):
 class Params:
     """Integers frozen on the host before any score is computed."""
     lut: tuple            # lut_size table entries (Q15, or uint8 when lut_bits = 8), the last one 0
-    idx_mul: int          # M: bin multiplier, idx = (x*M + 2^23) >> 24
-    idx_shift: int        # always IDX_SHIFT
+    idx_mul: int          # M: bin multiplier, idx = (x*M + 2^(sh-1)) >> sh
+    idx_shift: int        # sh: 24 for mu < 1/2, else 23 - e with mu = m 2^e, m in [1/2, 1)
     x_clip: int           # smallest relative score x that lands in slot 31
     req_mul: int          # M_o in [2^30, 2^31)
     req_shift: int        # sh_o
@@ -156,6 +157,26 @@ def build_lut(clip: float, lut_size: int = LUT_SIZE, lut_bits: int = 16) -> tupl
     return tuple(lut)
 
 
+def index_multiplier(mu: float):
+    """(M, sh) with M * 2^-sh the encoded bin multiplier mu (slots per score unit).
+
+    For mu < 1/2: a fixed 24-bit fraction, M = round(mu * 2^24), sh = 24
+    (M from 1 at mu = 2^-24 up to 2^23). From mu = 1/2 on a 24-bit fraction
+    would need M >= 2^23, so the fraction narrows instead: with
+    mu = m * 2^e (m in [1/2, 1), frexp), sh = 23 - e and
+    M = round(mu * 2^sh) = round(m * 2^23) in [2^22, 2^23], i.e. the widest
+    multiplier of at most 2^23, 22 significant bits or more. The two rules
+    meet at mu = 1/2 (2^23 / 2^24 = 2^22 / 2^23). At the top of the range,
+    mu < 2^14, sh >= 9.
+    """
+    if mu < 0.5:
+        sh = IDX_SHIFT
+    else:
+        _m, e = math.frexp(mu)
+        sh = IDX_MUL_BITS - e
+    return int(round(math.ldexp(mu, sh))), sh
+
+
 def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
                   clip: float, lut_size: int = LUT_SIZE, prob_bits: int = 8,
                   lut_bits: int = 16) -> Params:
@@ -163,7 +184,7 @@ def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
 
     alpha = s_q*s_k/sqrt(D) folds the 1/sqrt(d) attention scale into the
     index multiplier; mu = alpha/delta converts an integer score gap into
-    table slots; M = round(mu * 2^24).
+    table slots; M = round(mu * 2^sh) (index_multiplier).
     """
     n = _check_lut_size(lut_size)
     lut_bits = _check_lut_bits(lut_bits)
@@ -180,10 +201,10 @@ def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
     delta = c / float(n - 1)
     mu = alpha / delta
     if not (MU_MIN <= mu < MU_MAX):
-        raise OracleRangeError("index multiplier outside [2^-16, 2^-1)")
-    idx_mul = int(round(math.ldexp(mu, IDX_SHIFT)))
-    # smallest x with (x*M + 2^23) >> 24 >= N-1, i.e. x*M >= (2N-3) * 2^23
-    num = (2 * n - 3) << (IDX_SHIFT - 1)
+        raise OracleRangeError("index multiplier outside [2^-24, 2^14)")
+    idx_mul, idx_shift = index_multiplier(mu)
+    # smallest x with (x*M + 2^(sh-1)) >> sh >= N-1, i.e. x*M >= (2N-3) * 2^(sh-1)
+    num = (2 * n - 3) << (idx_shift - 1)
     x_clip = -(-num // idx_mul)
     mu_o = sv / ((255.0 if prob_bits == 8 else 65535.0) * so)
     m_o, e_o = math.frexp(mu_o)
@@ -194,7 +215,7 @@ def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
     req_shift = REQ_FRAC - e_o
     if not (REQ_SHIFT_MIN <= req_shift <= REQ_SHIFT_MAX):
         raise OracleRangeError("output multiplier outside the encodable range")
-    return Params(lut=lut, idx_mul=idx_mul, idx_shift=IDX_SHIFT, x_clip=x_clip,
+    return Params(lut=lut, idx_mul=idx_mul, idx_shift=idx_shift, x_clip=x_clip,
                   req_mul=req_mul, req_shift=req_shift, alpha=alpha, delta=delta,
                   mu=mu, mu_o=mu_o, lut_size=n, prob_bits=prob_bits, lut_bits=lut_bits)
 
@@ -205,7 +226,7 @@ def derive_params(D: int, s_q: float, s_k: float, s_v: float, s_o: float,
 def slot_index(x, prm: Params):
     """Table slot of a relative score x = m - s >= 0.
 
-    Uniform bins of width delta, nearest bin: idx = (x*M + 2^23) >> 24,
+    Uniform bins of width delta, nearest bin: idx = (x*M + 2^(sh-1)) >> sh,
     clipped to the last slot N-1 (the sparsity-aware clip).
     """
     x = np.asarray(x, dtype=np.int64)

@@ -12,7 +12,7 @@ operand, a wrong axis, an off-by-one in a rounding) shows up as a mismatch:
 
   * the slot of a relative score x is found as the nearest bin centre by
     exact rational comparison (|x*mu_q - k| minimal, ties to the upper bin),
-    where mu_q = M / 2^24 is the encoded multiplier, not by a shift formula;
+    where mu_q = M / 2^sh is the encoded multiplier, not by a shift formula;
   * probabilities (uint8, or the uint16 variant) and the requantised output
     are rounded with Fractions (floor(v + 1/2)), not with add-and-shift.
 

@@ -79,6 +79,35 @@ def test_hand_worked_parameters():
     assert p.req_shift == 30
 
 
+def test_hand_worked_parameters_large_multiplier():
+    """mu >= 1/2, derived by hand.
+
+    s_q = s_k = 2^-2, D = 64 -> alpha = 2^-4 / 8 = 2^-7; clip = 31 * 2^-9
+    -> delta = 2^-9, mu = 2^2 = 0.5 * 2^3 -> sh = 23 - 3 = 20,
+    M = 2^2 * 2^20 = 2^22. X_clip = ceil(61 * 2^19 / 2^22) = ceil(7.625) = 8:
+    x = 7 gives (7 * 2^22 + 2^19) >> 20 = 28, x = 8 gives 32 (slot 31).
+    """
+    p = O.derive_params(64, 2 ** -2, 2 ** -2, 255 * 2 ** -10, 2 ** -10, 31 * 2 ** -9)
+    assert p.mu == 4.0
+    assert (p.idx_mul, p.idx_shift, p.x_clip) == (2 ** 22, 20, 8)
+    assert list(O.slot_index(np.arange(10), p)) == [0, 4, 8, 12, 16, 20, 24, 28, 31, 31]
+
+
+def test_hand_worked_parameters_small_multiplier():
+    """mu < 2^-16, derived by hand.
+
+    s_q = s_k = 2^-13, D = 64 -> alpha = 2^-26 / 8 = 2^-29; clip = 31 * 2^-9
+    -> mu = 2^-20 -> sh = 24, M = 2^4. X_clip = ceil(61 * 2^23 / 2^4) =
+    61 * 2^19 = 31981568 (beyond any int8 score gap: no key is clipped);
+    slot(x) = (16 x + 2^23) >> 24 = round(x / 2^20).
+    """
+    p = O.derive_params(64, 2 ** -13, 2 ** -13, 255 * 2 ** -10, 2 ** -10, 31 * 2 ** -9)
+    assert p.mu == 2.0 ** -20
+    assert (p.idx_mul, p.idx_shift, p.x_clip) == (16, 24, 61 * 2 ** 19)
+    x = np.array([0, 2 ** 19 - 1, 2 ** 19, 3 * 2 ** 19, 2 * 64 * 127 * 127])
+    assert list(O.slot_index(x, p)) == [0, 0, 1, 2, 2]
+
+
 SCALE_SETS = [
     # (D, s_q, s_k, s_v, s_o, clip)
     (64, 0.0307, 0.0317, 0.0354, 0.0101, O.DEFAULT_CLIP),   # tiny-like
@@ -87,6 +116,15 @@ SCALE_SETS = [
     (128, 0.0326, 0.0471, 0.0473, 0.00073, O.DEFAULT_CLIP), # decode
     (64, 0.01, 0.01, 0.02, 0.02, 3.0),
     (128, 0.05, 0.02, 0.001, 0.5, 6.0),
+    # from mu = 1/2 on (large scales: a gap of one score unit moves half a
+    # bin or more) and below mu = 2^-16 (small scales)
+    (64, 0.7, 0.9, 0.05, 0.05, O.DEFAULT_CLIP),             # mu ~ 0.39
+    (64, 1.0, 1.0, 0.05, 0.05, O.DEFAULT_CLIP),              # mu ~ 0.62
+    (128, 3.0, 2.5, 0.05, 0.05, O.DEFAULT_CLIP),             # mu ~ 3.3
+    (64, 40.0, 50.0, 0.05, 0.05, O.DEFAULT_CLIP),            # mu ~ 1.2e3
+    (64, 100.0, 150.0, 0.05, 0.05, O.DEFAULT_CLIP),          # mu ~ 9.3e3
+    (64, 0.002, 0.003, 0.05, 0.05, O.DEFAULT_CLIP),          # mu ~ 3.7e-6 (below 2^-16)
+    (128, 4e-4, 4e-4, 0.05, 0.05, O.DEFAULT_CLIP),           # mu ~ 7.0e-8 (near 2^-24)
 ]
 
 
@@ -98,12 +136,19 @@ def test_multiplier_rounding_is_exact(D, sq, sk, sv, so, clip):
     exact_alpha_sq = (f(sq) * f(sk)) ** 2 / D          # alpha^2 exactly (sqrt irrational)
     assert abs(Fraction(p.alpha) ** 2 - exact_alpha_sq) <= exact_alpha_sq * Fraction(1, 2 ** 49)
     mu = Fraction(p.mu)
-    # M is the nearest integer to mu * 2^24
-    assert abs(p.idx_mul - mu * 2 ** 24) <= Fraction(1, 2)
-    assert 256 <= p.idx_mul < 2 ** 23
+    sh = p.idx_shift
+    # M is the nearest integer to mu * 2^sh: sh = 24 below mu = 1/2, and
+    # from there the multiplier is kept at 22 or 23 significant bits
+    assert abs(p.idx_mul - mu * 2 ** sh) <= Fraction(1, 2)
+    if mu < Fraction(1, 2):
+        assert sh == 24 and 1 <= p.idx_mul <= 2 ** 23
+    else:
+        assert 9 <= sh <= 23 and 2 ** 22 <= p.idx_mul <= 2 ** 23
     # clip point: smallest x with slot 31
-    assert (p.x_clip * p.idx_mul + 2 ** 23) >> 24 == 31
-    assert ((p.x_clip - 1) * p.idx_mul + 2 ** 23) >> 24 == 30
+    assert (p.x_clip * p.idx_mul + 2 ** (sh - 1)) >> sh >= 31
+    assert p.x_clip >= 1 and ((p.x_clip - 1) * p.idx_mul + 2 ** (sh - 1)) >> sh <= 30
+    if mu <= 1:     # a score unit moves at most one bin: every slot is reached
+        assert ((p.x_clip - 1) * p.idx_mul + 2 ** (sh - 1)) >> sh == 30
     # requantisation multiplier normalised and nearest
     assert 2 ** 30 <= p.req_mul < 2 ** 31
     mu_o = Fraction(p.mu_o)
@@ -114,9 +159,17 @@ def test_multiplier_rounding_is_exact(D, sq, sk, sv, so, clip):
 
 def test_range_refusals():
     with pytest.raises(O.OracleRangeError):
-        O.derive_params(64, 1e-4, 1e-4, 1.0, 1.0, 6.0)      # mu < 2^-16
+        O.derive_params(64, 1e-4, 1e-4, 1.0, 1.0, 6.0)      # mu ~ 2^-27 < 2^-24
     with pytest.raises(O.OracleRangeError):
-        O.derive_params(64, 2.0, 2.0, 1.0, 1.0, 6.0)        # mu >= 1/2
+        O.derive_params(64, 200.0, 300.0, 1.0, 1.0, 6.0)    # mu ~ 3.9e4 >= 2^14
+    # the edges of [2^-24, 2^14) themselves, exactly: s_q = s_k = s, D = 64,
+    # clip = 31 * 2^-9 (delta = 2^-9), so mu = s^2 / 8 / 2^-9 = 64 s^2
+    p = O.derive_params(64, 2.0 ** -15, 2.0 ** -15, 1.0, 1.0, 31 * 2 ** -9)
+    assert p.mu == 2.0 ** -24 and p.idx_mul == 1 and p.idx_shift == 24
+    with pytest.raises(O.OracleRangeError):
+        O.derive_params(64, 2.0 ** 4, 2.0 ** 4, 1.0, 1.0, 31 * 2 ** -9)   # mu = 2^14
+    p = O.derive_params(64, 15.9, 15.9, 1.0, 1.0, 31 * 2 ** -9)          # mu just below 2^14
+    assert p.idx_shift == 9 and 2 ** 22 <= p.idx_mul <= 2 ** 23
     for bad in (0.0, -1.0, float("inf"), float("nan")):
         with pytest.raises(O.OracleRangeError):
             O.derive_params(64, bad, 0.01, 0.01, 0.01, 6.0)
@@ -134,24 +187,29 @@ def test_slot_index_exhaustive(D, sq, sk, sv, so, clip):
 
     * slot(0) = 0; slots are monotone and never skip a slot;
     * slot is the nearest bin under the encoded multiplier:
-      |slot * 2^24 - x * M| <= 2^23 for x below the clip point;
+      |slot * 2^sh - x * M| <= 2^(sh-1) for x below the clip point;
     * the encoded multiplier tracks the exact one: the slot is within
-      1/2 + x*|mu - M/2^24| of x*mu;
+      1/2 + x*|mu - M/2^sh| of x*mu;
     * everything from the clip point on is slot 31.
+    Relative scores stop at 2*D*127^2 (no int8 product reaches further), so
+    for tiny multipliers the sweep ends there instead of at the clip point.
     """
     p = O.derive_params(D, sq, sk, sv, so, clip)
-    x = np.arange(0, p.x_clip + 3, dtype=np.int64)
+    sh = p.idx_shift
+    x = np.arange(0, min(p.x_clip + 3, 2 * D * 127 * 127 + 1), dtype=np.int64)
     s = O.slot_index(x, p)
     assert s[0] == 0
     d = np.diff(s)
-    assert ((d == 0) | (d == 1)).all()
+    assert (d >= 0).all()
+    if p.mu <= 1:   # at most one bin per score unit: no slot is skipped
+        assert ((d == 0) | (d == 1)).all()
     assert (s[p.x_clip:] == 31).all()
     assert (s[:p.x_clip] <= 30).all()
     below = x[:p.x_clip]
     sb = s[:p.x_clip]
-    assert (np.abs(sb * (1 << 24) - below * p.idx_mul) <= (1 << 23)).all()
+    assert (np.abs(sb * (1 << sh) - below * p.idx_mul) <= (1 << (sh - 1))).all()
     mu = Fraction(p.mu)
-    err_m = abs(mu - Fraction(p.idx_mul, 1 << 24))
+    err_m = abs(mu - Fraction(p.idx_mul, 1 << sh))
     worst = max(abs(Fraction(int(xx)) * mu - int(ss)) - int(xx) * err_m
                 for xx, ss in zip(below[:: max(1, len(below) // 4000)], sb[:: max(1, len(below) // 4000)]))
     assert worst <= Fraction(1, 2)

@@ -119,7 +119,7 @@ def _ref_softmax(qh, kh, alpha, causal):
 
 def _beta(prm):
     """Per-key multiplicative error bound of e_j against exp(-alpha x_j), log units."""
-    err_m = abs(prm.mu - prm.idx_mul / 2 ** 24)
+    err_m = abs(prm.mu - prm.idx_mul / 2 ** prm.idx_shift)
     lut30 = min(e for e in prm.lut[:31] if e > 0)
     return (prm.delta / 2 + prm.delta * prm.x_clip * err_m
             - math.log(1.0 - 0.5 / lut30))
@@ -194,11 +194,13 @@ def test_probabilities_monotone_in_score():
             assert (P[0, h, i, ~allow[i]] == 0).all()
 
 
-def test_two_key_rows_exhaustive():
+@pytest.mark.parametrize("scale", [0.3, 1.5, 6.0, 40.0])   # mu 0.06, 1.4, 22, 995
+def test_two_key_rows_exhaustive(scale):
     """Two keys with score gap x, for every x up to past the clip point:
     p0 >= p1, p0 + p1 within one of 255, and p1/255 within the derived
-    tolerance of the logistic 1 / (1 + e^(alpha x))."""
-    prm = O.derive_params(64, 0.3, 0.3, 0.1, 0.1, O.DEFAULT_CLIP)
+    tolerance of the logistic 1 / (1 + e^(alpha x)); from mu = 1/2 on, with
+    the narrower multiplier fraction, as below it."""
+    prm = O.derive_params(64, scale, scale, 0.1, 0.1, O.DEFAULT_CLIP)
     tb = math.tanh(_beta(prm) / 2)
     lut = np.asarray(prm.lut, dtype=np.int64)
     x = np.arange(0, prm.x_clip + 2, dtype=np.int64)

@@ -70,19 +70,16 @@ SCALE_SETS = [
 @pytest.mark.parametrize("n", FINE)
 @pytest.mark.parametrize("D,sq,sk,sv,so,clip", SCALE_SETS)
 def test_fine_slot_index_exhaustive(n, D, sq, sk, sv, so, clip):
-    """slot(0) = 0, no skipped slot, nearest bin under the encoded multiplier
-    below the clip point, slot N-1 from the clip point on; the multiplier is
-    the nearest integer to mu 2^24 with mu = alpha (N-1) / clip."""
+    """slot(0) = 0, monotone (no skipped slot while mu <= 1), nearest bin
+    under the encoded multiplier below the clip point, slot N-1 from the clip
+    point on; the multiplier is the nearest integer to mu 2^sh with
+    mu = alpha (N-1) / clip (sh = 24 below mu = 1/2; finer bins raise mu with
+    N, and from 1/2 on the fraction narrows so that M <= 2^23)."""
     f = lambda x: Fraction(float(np.float32(x)))
-    mu_est = float(f(sq) * f(sk)) / math.sqrt(D) * (n - 1) / float(f(clip))
-    if mu_est >= 0.5 * (1 - 1e-9):
-        # finer bins raise mu with N; past 1/2 the multiplier no longer fits
-        # the device's 24-bit operand, and the call is refused
-        with pytest.raises(O.OracleRangeError):
-            O.derive_params(D, sq, sk, sv, so, clip, n)
-        return
     p = O.derive_params(D, sq, sk, sv, so, clip, n)
-    assert abs(p.idx_mul - Fraction(p.mu) * 2 ** 24) <= Fraction(1, 2)
+    sh = p.idx_shift
+    assert abs(p.idx_mul - Fraction(p.mu) * 2 ** sh) <= Fraction(1, 2)
+    assert (sh == 24) == (p.mu < 0.5) and p.idx_mul <= 2 ** 23
     # mu tracks alpha (N-1)/c: compare squares (sqrt(D) is irrational)
     mu_sq = (f(sq) * f(sk)) ** 2 / D * Fraction(n - 1) ** 2 / f(clip) ** 2
     assert abs(Fraction(p.mu) ** 2 - mu_sq) <= mu_sq * Fraction(1, 2 ** 48)
@@ -90,14 +87,17 @@ def test_fine_slot_index_exhaustive(n, D, sq, sk, sv, so, clip):
     s = O.slot_index(x, p)
     assert s[0] == 0
     d = np.diff(s)
-    assert ((d == 0) | (d == 1)).all()
+    assert (d >= 0).all()
+    if p.mu <= 1:
+        assert ((d == 0) | (d == 1)).all()
     assert (s[p.x_clip:] == n - 1).all() and (s[:p.x_clip] <= n - 2).all()
-    assert (np.abs(s[:p.x_clip] * (1 << 24) - x[:p.x_clip] * p.idx_mul) <= (1 << 23)).all()
+    assert (np.abs(s[:p.x_clip] * (1 << sh) - x[:p.x_clip] * p.idx_mul) <= (1 << (sh - 1))).all()
 
 
-def test_fine_twin_slot_agrees_everywhere():
+@pytest.mark.parametrize("scale", [0.3, 1.1, 4.0])   # mu below 1/2, just above, several bins a unit
+def test_fine_twin_slot_agrees_everywhere(scale):
     for n in FINE:
-        prm = O.derive_params(64, 0.3, 0.3, 0.1, 0.1, O.DEFAULT_CLIP, n)
+        prm = O.derive_params(64, scale, scale, 0.1, 0.1, O.DEFAULT_CLIP, n)
         xs = np.arange(0, prm.x_clip + 5)
         a = O.slot_index(xs, prm)
         b = [T.nearest_slot(int(xx), prm.idx_mul, prm.idx_shift, n) for xx in xs]
@@ -126,6 +126,32 @@ def test_fine_twin_agrees_on_tiny_shapes(n, Sq, Skv, D, causal, seed, scales):
     assert E[0, 0].tolist() == tE and P[0, 0].tolist() == tP
 
 
+LARGE_MU_TWIN = [
+    # (Sq, Skv, D, causal, seed, scales): mu from just above 1/2 to several
+    # bins per score unit; small integer inputs keep score gaps near the clip
+    (5, 9, 16, False, 20, (0.8, 0.6, 0.05, 0.02)),     # mu 0.6 (32 entries) .. 2.4 (128)
+    (7, 7, 8, True, 21, (1.2, 0.95, 0.05, 0.01)),      # mu 2 .. 8
+    (4, 12, 4, False, 22, (2.0, 1.2, 0.05, 0.03)),     # mu 6 .. 24
+]
+
+
+@pytest.mark.parametrize("n", [32] + list(FINE))
+@pytest.mark.parametrize("Sq,Skv,D,causal,seed,scales", LARGE_MU_TWIN)
+def test_twin_agrees_at_large_multipliers(n, Sq, Skv, D, causal, seed, scales):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-3, 4, (1, 1, Sq, D)).astype(np.int8)
+    k = rng.integers(-3, 4, (1, 1, Skv, D)).astype(np.int8)
+    v = rng.integers(-127, 128, (1, 1, Skv, D)).astype(np.int8)
+    prm = O.derive_params(D, *scales, O.DEFAULT_CLIP, n)
+    assert prm.mu >= 0.5 and prm.idx_shift < 24
+    out, m, E, P = O.forward(q, k, v, scales, O.DEFAULT_CLIP, causal, stats=True, lut_size=n)
+    tout, tm, tE, tP = T.head_forward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), prm, causal)
+    assert out[0, 0].tolist() == tout and m[0, 0].tolist() == tm
+    assert E[0, 0].tolist() == tE and P[0, 0].tolist() == tP
+    # rows are not all one-hot: some key other than the max has p > 0
+    assert (P[0, 0] > 0).sum() > Sq
+
+
 def _ref_softmax(qh, kh, alpha, causal):
     S = qh.astype(np.float64) @ kh.astype(np.float64).T
     allow = O.allowed_mask(qh.shape[0], kh.shape[0], causal)
@@ -137,7 +163,7 @@ def _ref_softmax(qh, kh, alpha, causal):
 
 def _beta(prm):
     """Per-key multiplicative error bound of e_j against exp(-alpha x_j), log units."""
-    err_m = abs(prm.mu - prm.idx_mul / 2 ** 24)
+    err_m = abs(prm.mu - prm.idx_mul / 2 ** prm.idx_shift)
     smallest = min(e for e in prm.lut[:-1] if e > 0)
     return prm.delta / 2 + prm.delta * prm.x_clip * err_m - math.log(1.0 - 0.5 / smallest)
 
