@@ -95,8 +95,10 @@ enum {
     INTATTN_E_RANGE = -6,  /* mu outside [2^-24, 2^14) or sh_o outside 1..63 */
     INTATTN_E_HIP   = -7,  /* the HIP runtime reported an error              */
     INTATTN_E_ALIGN = -8,  /* a tensor pointer is not 16-byte aligned        */
-    INTATTN_E_WORKSPACE = -9  /* workspace smaller than intattn_workspace_bytes,
+    INTATTN_E_WORKSPACE = -9, /* workspace smaller than intattn_workspace_bytes,
                                  or not 256-byte aligned                    */
+    INTATTN_E_SCRATCH = -10   /* intattn_forward_ex_noalloc: the shape needs
+                                 more than INTATTN_NOALLOC_SCRATCH_BYTES     */
 };
 
 /* The 32-entry exp table for a clip threshold (in logit units): lut_out[k] =
@@ -236,6 +238,28 @@ int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t* v, int8_t
                        const intattn_shape* shape, const intattn_scales* scales, float clip,
                        int causal, const intattn_variant* variant, void* stream,
                        int32_t* row_max, uint32_t* row_sum);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ * intattn_forward_ex with the same arguments and results, except that the
+ * shapes that split their keys over several workgroups per head (those for
+ * which intattn_workspace_bytes is nonzero) use the library's own device
+ * scratch, a static array of INTATTN_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends, instead of a caller
+ * workspace; variant->workspace must be NULL and workspace_bytes 0. Calls no
+ * allocating function. Every call on a GPU shares that GPU's scratch, so
+ * calls that overlap on one GPU (other streams or threads) race; the kernels
+ * clear what must start at zero, so earlier contents never matter. The
+ * scratch's device address is looked up once per device on the first call
+ * that needs it (hipGetSymbolAddress, with that device current).
+ * Errors: those of intattn_forward_ex (all checked before any HIP call),
+ * E_WORKSPACE for a caller workspace, E_SCRATCH when intattn_workspace_bytes
+ * exceeds the scratch size, E_HIP if the scratch address lookup fails. */
+#define INTATTN_NOALLOC_SCRATCH_BYTES (32ull << 20)
+int intattn_forward_ex_noalloc(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
+                               const intattn_shape* shape, const intattn_scales* scales, float clip,
+                               int causal, const intattn_variant* variant, void* stream,
+                               int32_t* row_max, uint32_t* row_sum);
 
 /* Decode-step cache update (the step before attention in a decoder's decode
  * step; the pages do not describe it): the keys and values of T new tokens,

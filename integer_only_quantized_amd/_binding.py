@@ -19,7 +19,7 @@ INTATTN_OK = 0
 STATUS_NAMES = {
     0: "INTATTN_OK", -1: "INTATTN_E_NULL", -2: "INTATTN_E_SHAPE", -3: "INTATTN_E_DIM",
     -4: "INTATTN_E_SCALE", -5: "INTATTN_E_CLIP", -6: "INTATTN_E_RANGE", -7: "INTATTN_E_HIP",
-    -8: "INTATTN_E_ALIGN", -9: "INTATTN_E_WORKSPACE",
+    -8: "INTATTN_E_ALIGN", -9: "INTATTN_E_WORKSPACE", -10: "INTATTN_E_SCRATCH",
 }
 DEFAULT_CLIP = float(ctypes.c_float(math.log(510.0)).value)
 
@@ -93,6 +93,8 @@ def _load():
     lib.intattn_forward_ex.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Shape), ctypes.POINTER(Scales), f32, i32,
                                        ctypes.POINTER(Variant), vp, vp, vp]
     lib.intattn_forward_ex.restype = i32
+    lib.intattn_forward_ex_noalloc.argtypes = lib.intattn_forward_ex.argtypes
+    lib.intattn_forward_ex_noalloc.restype = i32
     lib.intattn_workspace_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Variant)]
     lib.intattn_workspace_bytes.restype = ctypes.c_uint64
     lib.intattn_kv_append.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp]
@@ -400,6 +402,37 @@ def forward_ex(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False
                                    rm.data_ptr() if stats else None, rs.data_ptr() if stats else None)
     _check(code, "intattn_forward_ex")
     return (out, rm, rs) if stats else out
+
+
+def forward_ex_noalloc(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False, lut_size: int = 32,
+                       stats: bool = False, out=None, skv: int = None, prob_bits: int = 8, lut_bits: int = 16):
+    """intattn_forward_ex_noalloc: forward_ex whose split-decode shapes use the
+    library's static device scratch (no workspace argument, nothing
+    allocated by the library). out, and row_max / row_sum with stats, are
+    allocated here unless given."""
+    import torch
+    B, H, Sq, C, D = _check_tensors(q, k, v, grouped=True)
+    skv = C if skv is None else int(skv)
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype is not torch.int8 or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError("out must be a contiguous int8 tensor shaped like q, on q's device")
+    var = Variant(int(lut_size), int(k.shape[1]), int(C), int(prob_bits), int(lut_bits))
+    sh, sc = _structs((B, H, Sq, skv, D), scales)
+    rm = rs = None
+    if stats:
+        rm = torch.empty((B, H, Sq), dtype=torch.int32, device=q.device)
+        rs = torch.empty((B, H, Sq), dtype=torch.int32, device=q.device)
+    code = _lib.intattn_forward_ex_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                           ctypes.byref(sh), ctypes.byref(sc), float(clip), int(bool(causal)),
+                                           ctypes.byref(var), _stream(q), rm.data_ptr() if stats else None,
+                                           rs.data_ptr() if stats else None)
+    _check(code, "intattn_forward_ex_noalloc")
+    return (out, rm, rs) if stats else out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20     # INTATTN_NOALLOC_SCRATCH_BYTES
 
 
 def kv_append(k_new, v_new, k_cache, v_cache, pos: int, s_k: float, s_v: float):

@@ -43,7 +43,7 @@ def _run(cmd):
 
 HOST_SOURCES = ["intattn_host.cpp", "intattn_api.cpp"]
 HIP_SOURCES = ["ia_general.hip", "ia_short.hip", "ia_long.hip", "ia_decode.hip", "ia_decode_split.hip", "ia_stages.hip",
-               "ia_kvcache.hip"]
+               "ia_kvcache.hip", "ia_noalloc.hip"]
 # Per-source code-generation options: the long- and short-row kernels keep
 # their MFMA accumulators in ordinary VGPRs (no accumulator-register copies
 # when the scores are post-processed on the VALU).

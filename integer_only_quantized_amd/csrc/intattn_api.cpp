@@ -189,18 +189,19 @@ extern "C" uint64_t intattn_workspace_bytes(const intattn_shape* shape, const in
     return ia::decode_split_workspace_bytes(static_cast<long long>(shape->B) * shape->H, shape->Skv, shape->D);
 }
 
-extern "C" int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
-                                  const intattn_shape* shape, const intattn_scales* scales, float clip,
-                                  int causal, const intattn_variant* variant, void* stream, int32_t* row_max,
-                                  uint32_t* row_sum) {
+namespace {
+
+// Every check of intattn_forward_ex (no HIP call), and its kernel parameters.
+int check_forward_ex(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, const intattn_shape* shape,
+                     const intattn_scales* scales, float clip, int causal, const intattn_variant* variant,
+                     int32_t* row_max, uint32_t* row_sum, IaKernelParams* kp) {
     if ((row_max == nullptr) != (row_sum == nullptr)) return INTATTN_E_NULL;
     const int lut_size = variant && variant->lut_size != 0 ? variant->lut_size : 32;
     const int kv_heads = variant ? variant->kv_heads : 0;
     const int kv_capacity = variant ? variant->kv_capacity : 0;
     const int prob_bits = variant && variant->prob_bits != 0 ? variant->prob_bits : 8;
     const int lut_bits = variant && variant->lut_bits != 0 ? variant->lut_bits : 16;
-    IaKernelParams kp;
-    const int st = prepare(q, k, v, out, shape, scales, clip, causal, &kp, lut_size, kv_heads, kv_capacity,
+    const int st = prepare(q, k, v, out, shape, scales, clip, causal, kp, lut_size, kv_heads, kv_capacity,
                            prob_bits, lut_bits);
     if (st != INTATTN_OK) return st;
     void* ws = variant ? variant->workspace : nullptr;
@@ -208,6 +209,26 @@ extern "C" int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t
         const uint64_t need = intattn_workspace_bytes(shape, variant);
         if (variant->workspace_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return INTATTN_E_WORKSPACE;
     }
+    return INTATTN_OK;
+}
+
+}  // namespace
+
+int intattn_validate_forward_ex(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
+                                const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
+                                const intattn_variant* variant, int32_t* row_max, uint32_t* row_sum) {
+    IaKernelParams kp;
+    return check_forward_ex(q, k, v, out, shape, scales, clip, causal, variant, row_max, row_sum, &kp);
+}
+
+extern "C" int intattn_forward_ex(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
+                                  const intattn_shape* shape, const intattn_scales* scales, float clip,
+                                  int causal, const intattn_variant* variant, void* stream, int32_t* row_max,
+                                  uint32_t* row_sum) {
+    IaKernelParams kp;
+    const int st = check_forward_ex(q, k, v, out, shape, scales, clip, causal, variant, row_max, row_sum, &kp);
+    if (st != INTATTN_OK) return st;
+    void* ws = variant ? variant->workspace : nullptr;
     if (rows_of(kp) == 0) return INTATTN_OK;
     ia::clear_pending_hip_error();
     return dispatch(q, k, v, out, shape->D, kp, stream, row_max, row_sum, ws);

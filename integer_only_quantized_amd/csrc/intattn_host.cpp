@@ -188,6 +188,7 @@ extern "C" const char* intattn_strerror(int status) {
         case INTATTN_E_HIP: return "the HIP runtime reported an error";
         case INTATTN_E_ALIGN: return "a tensor pointer is not 16-byte aligned";
         case INTATTN_E_WORKSPACE: return "workspace too small for the shape, or not 256-byte aligned";
+        case INTATTN_E_SCRATCH: return "the shape needs more device scratch than the library's static scratch holds";
         default: return "unknown status";
     }
 }

@@ -11,6 +11,12 @@
 // Shape checks common to every entry point (no device access).
 int intattn_validate_shape(const intattn_shape* s, int causal);
 
+// Every argument check of intattn_forward_ex, without queueing anything (no
+// HIP call): the status intattn_forward_ex would return before any launch.
+int intattn_validate_forward_ex(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
+                                const intattn_shape* shape, const intattn_scales* scales, float clip, int causal,
+                                const intattn_variant* variant, int32_t* row_max, uint32_t* row_sum);
+
 // Largest exp table of the variants (32 is the pages' table).
 constexpr int kIaMaxLut = 128;
 // Entries of the table the kernels receive: the exp table by slot (N <= 128

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
                             "intattn_forward_debug", "intattn_strerror", "intattn_qk_scores",
                             "intattn_index_softmax", "intattn_fp_softmax", "intattn_pv",
                             "intattn_build_lut_ex", "intattn_derive_params_ex", "intattn_forward_ex",
-                            "intattn_kv_append", "intattn_workspace_bytes"])
+                            "intattn_kv_append", "intattn_workspace_bytes", "intattn_forward_ex_noalloc"])
     for n in names:
         assert hasattr(B._lib, n), n
 
