@@ -152,9 +152,9 @@ int intattn_forward_debug(const int8_t* q, const int8_t* k, const int8_t* v, int
  * uint16 probabilities: the same section warns of underflow on skewed score
  * distributions; a uint8 row of 513 or more uniform keys is all zeros. With
  * prob_bits = 16: R16 = (65535*2^16 + E/2) / E, p = (lut[idx]*R16 + 2^15)
- * >> 16 (uint16, target row sum 65535), and mu_o = s_v/(65535*s_o); the
- * long-row and decode kernels run it (P.V as two int8 products, high and
- * low probability bytes).
+ * >> 16 (uint16, target row sum 65535), and mu_o = s_v/(65535*s_o); every
+ * kernel runs it (P.V as two int8 products, high and low probability
+ * bytes).
  * uint8 table entries: the lookup-table granularity item frames the table as
  * an accuracy/memory trade; lut_bits = 8 stores e8[k] = rint(255 exp(-k
  * delta)) for k < N-1 and e8[N-1] = 0 (any N), and with E8 = sum_j e8

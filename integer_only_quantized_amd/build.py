@@ -43,12 +43,13 @@ def _run(cmd):
 
 HOST_SOURCES = ["intattn_host.cpp", "intattn_api.cpp"]
 HIP_SOURCES = ["ia_general.hip", "ia_short.hip", "ia_long.hip", "ia_decode.hip", "ia_decode_split.hip", "ia_stages.hip",
-               "ia_kvcache.hip", "ia_noalloc.hip"]
+               "ia_kvcache.hip", "ia_noalloc.hip", "ia_short16.hip"]
 # Per-source code-generation options: the long- and short-row kernels keep
 # their MFMA accumulators in ordinary VGPRs (no accumulator-register copies
 # when the scores are post-processed on the VALU).
 _VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-HIP_EXTRA = {"ia_long.hip": _VGPR_MFMA, "ia_short.hip": _VGPR_MFMA, "ia_stages.hip": _VGPR_MFMA}
+HIP_EXTRA = {"ia_long.hip": _VGPR_MFMA, "ia_short.hip": _VGPR_MFMA, "ia_short16.hip": _VGPR_MFMA,
+             "ia_stages.hip": _VGPR_MFMA}
 
 
 def build(verbose: bool = True, jobs: int = 8) -> str:

@@ -147,8 +147,7 @@ int dispatch(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int
         return ia::launch_decode_split(q, k, v, out, D, kp, stream, workspace, row_max, row_sum);
     if (kp.Sq == 1 && kp.Skv <= ia::decode_max_keys())
         return ia::launch_decode(q, k, v, out, D, kp, stream, row_max, row_sum);
-    // uint16 probabilities: the long-row kernel serves every other shape
-    if (kp.Skv <= ia::short_max_keys(D) && kp.prob_bits == 8)
+    if (kp.Skv <= ia::short_max_keys(D))
         return ia::launch_short(q, k, v, out, D, kp, stream, row_max, row_sum);
     return ia::launch_long(q, k, v, out, D, kp, stream, row_max, row_sum);
 }

@@ -87,6 +87,10 @@ int launch_general(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* ou
 int short_max_keys(int D);
 int launch_short(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
                  const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum);
+// The uint16-probability instances of the short-row kernel (launch_short
+// calls it for kp.prob_bits == 16).
+int launch_short16(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
+                   const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum);
 
 // Sq == 1 and Skv <= decode_max_keys(): one head per workgroup, HBM streaming.
 int decode_max_keys();

@@ -152,6 +152,16 @@ P16_CASES = [
     # one key past it (a single query row on the long-row kernel)
     (1, 2, 2, 1, 16384, 128, False, 32, 608, "normal"),
     (1, 2, 1, 1, 16385, 64, False, 32, 609, "student_t_tail"),
+    # the short-row kernel (Skv <= 512 at d = 64, <= 256 at d = 128): full
+    # rows, ragged tails, causal block skipping, grouped K/V heads, every
+    # table size
+    (2, 3, 3, 512, 512, 64, False, 32, 610, "channel_outliers"),
+    (1, 4, 2, 197, 197, 64, False, 32, 611, "normal"),
+    (2, 2, 2, 300, 300, 64, True, 128, 612, "student_t_tail"),
+    (1, 2, 2, 33, 40, 128, True, 64, 613, "normal"),
+    (2, 2, 1, 256, 256, 128, False, 32, 614, "channel_outliers"),
+    (1, 2, 2, 70, 197, 64, False, 32, 615, "normal"),
+    (1, 1, 1, 1000, 480, 64, False, 32, 616, "normal"),
 ]
 
 
@@ -169,6 +179,23 @@ def test_uint16_probabilities_bit_exact(B, H, Hkv, Sq, Skv, D, causal, lut, seed
     _eq("p16 out", out.cpu().numpy(), ref)
     _eq("p16 row_max", rm.cpu().numpy(), m)
     _eq("p16 row_sum", rs.cpu().numpy().view(np.uint32), E)
+
+
+def test_uint16_probabilities_bert_size_all_heads():
+    """BERT shape (8 x 12 x 512 x 64) with uint16 probabilities on the
+    short-row kernel, every head against the oracle."""
+    w = W.make_config("bert")
+    _say("case bert prob_bits=16")
+    s16 = w.scales
+    out, rm, rs = IA.forward_ex(_dev(w.q), _dev(w.k), _dev(w.v), s16, w.clip, False, 32, stats=True, prob_bits=16)
+    torch.cuda.synchronize()
+    out, rm, rs = out.cpu().numpy(), rm.cpu().numpy(), rs.cpu().numpy().view(np.uint32)
+    prm = O.derive_params(w.D, *s16, w.clip, 32, 16)
+    for b, h in [(b, h) for b in range(w.B) for h in range(w.H)]:
+        ref, m, E, _ = O.head_forward(w.q[b, h], w.k[b, h], w.v[b, h], prm, False)
+        _eq(f"bert p16 out {b},{h}", out[b, h], ref)
+        _eq(f"bert p16 m {b},{h}", rm[b, h], m)
+        _eq(f"bert p16 E {b},{h}", rs[b, h], E)
 
 
 def test_uint16_probabilities_single_key_returns_v():
@@ -199,6 +226,8 @@ LUT8_CASES = [
     (16, 32, 8, 1, 3000, 128, False, 32, 8, 706, "student_t_tail"),
     (1, 2, 2, 300, 1100, 128, True, 32, 16, 707, "normal"),
     (4, 8, 2, 1, 4096, 128, False, 64, 16, 708, "channel_outliers"),
+    (2, 2, 2, 200, 512, 64, False, 32, 16, 709, "channel_outliers"),
+    (1, 2, 2, 130, 130, 128, True, 128, 16, 710, "student_t_tail"),
 ]
 
 
