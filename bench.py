@@ -61,16 +61,18 @@ DEFAULT_WARMUP = {"tiny": 50000, "bert": 30000, "vit": 25000, "llama_prefill": 2
 # binding roofline per workload (ViT: 197 keys a row, arithmetic intensity 197 ops/byte, HBM)
 BOUND = {"tiny": "mfma", "bert": "mfma", "vit": "hbm", "llama_prefill": "mfma", "decode": "hbm"}
 # kernel the library dispatches for each workload, and its source file
-KERNEL = {"tiny": ("ia_short_kernel", "ia_short.hip"), "bert": ("ia_short_kernel", "ia_short.hip"),
-          "vit": ("ia_short_kernel", "ia_short.hip"), "llama_prefill": ("ia_long_kernel", "ia_long.hip"),
-          "decode": ("ia_decode_kernel", "ia_decode.hip")}
+# (the sources a summary's kernel_source_sha256 covers: the kernel's own files and ia_device.h)
+_SHORT = ("ia_short.hip", "ia_short_impl.h")
+KERNEL = {"tiny": ("ia_short_kernel", _SHORT), "bert": ("ia_short_kernel", _SHORT),
+          "vit": ("ia_short_kernel", _SHORT), "llama_prefill": ("ia_long_kernel", ("ia_long.hip",)),
+          "decode": ("ia_decode_kernel", ("ia_decode.hip",))}
 
 
-def kernel_source_sha(src: str) -> str:
+def kernel_source_sha(srcs) -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "integer_only_quantized_amd", "csrc")
-    for f in (src, "ia_device.h"):
+    for f in (*srcs, "ia_device.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
