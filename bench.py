@@ -512,14 +512,18 @@ def measure(w, steps, warmup, extra_timing=False, settle_s=CLOCK_SETTLE_S):
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
     call = lambda: ia.forward(q, k, v, w.scales, w.clip, w.causal, out=out)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < settle_s:
         call()
+    # the warm-up calls run between the same two events as the timed region,
+    # so the events' first-use cost falls outside it
+    ev0.record(stream)
     for _ in range(warmup):
         call()
+    ev1.record(stream)
     torch.cuda.synchronize(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
     t_wall0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(steps):
