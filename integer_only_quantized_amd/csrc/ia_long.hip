@@ -164,14 +164,23 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
         return reinterpret_cast<int8_t*>(&lds) + offsetof(L, k) + static_cast<size_t>(st) * L::TB;
     };
 
-    // S^T block kb (0 or 1) of the K tile in stage st, from accumulator c0
-    auto scores = [&](int st, int kb, const v16i& c0) {
+    // S^T block kb (0 or 1) of the K tile in stage ST, from accumulator c0.
+    // The swizzle of row 32 kb + l32 depends on l32 alone, so each fragment's
+    // address is a per-lane register (kfo) plus a constant that folds into the
+    // instruction's offset field: the stages are compile-time constants (the
+    // tile loops below are unrolled over the ring), and no address is
+    // recomputed per tile.
+    uint32_t kfo[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        kfo[ks] = static_cast<uint32_t>(l32 * D + 16 * ((2 * ks + hh) ^ k_swz<D>(l32)));
+    auto scores = [&](auto st_c, int kb, const v16i& c0) {
+        constexpr int ST = decltype(st_c)::value;
         v16i s = c0;
-        const int r = 32 * kb + l32;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int c = (2 * ks + hh) ^ k_swz<D>(r);
-            const v4i a = *reinterpret_cast<const v4i*>(kstage(st) + r * D + 16 * c);
+            const v4i a = *reinterpret_cast<const v4i*>(lds_raw + kfo[ks] + (offsetof(L, k) + ST * L::TB) +
+                                                        32 * kb * D);
             s = mfma_i8_32x32x32(a, qf[ks], s);
         }
         return s;
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     };
 
     // P.V B operand addresses for stage 0, key block 0 (see tr8_lane_addr);
-    // the stage adds a register offset, key block 1 the immediate 32*D
+    // the stage and key block add immediate offsets
     uint32_t vaddr[2 * DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -212,18 +221,22 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
             wait_vmcnt(0);
         }
         lds_barrier();
-        for (int t = 0; t < ntiles; ++t) {
-            const int st = t % kStages;
-            if (t + 2 < ntiles) {
-                const int st2 = (t + 2) % kStages;
-                issue(kh, lds.k[st2], koff, t + 2);
-                issue(vh, lds.v[st2], voff, t + 2);
-            }
-            body(t, st);
-            // tile t+1 must have landed; tile t+2 may stay in flight
-            if (t + 2 < ntiles) wait_vmcnt(per_tile);
-            else wait_vmcnt(0);
-            lds_barrier();
+        for (int t0 = 0; t0 < ntiles; t0 += kStages) {
+            static_for<kStages>([&](auto sc) {
+                constexpr int ST = decltype(sc)::value;
+                const int t = t0 + ST;
+                if (t >= ntiles) return;
+                if (t + 2 < ntiles) {
+                    constexpr int ST2 = (ST + 2) % kStages;
+                    issue(kh, lds.k[ST2], koff, t + 2);
+                    issue(vh, lds.v[ST2], voff, t + 2);
+                }
+                body(t, sc);
+                // tile t+1 must have landed; tile t+2 may stay in flight
+                if (t + 2 < ntiles) wait_vmcnt(per_tile);
+                else wait_vmcnt(0);
+                lds_barrier();
+            });
         }
     };
 
@@ -237,25 +250,32 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
         for (int t = 0; t < pre; ++t) issue(kh, kstage(t), koff, t);
         wait_vmcnt(max(0, pre - 2) * LOADS);  // tiles 0 and 1 landed
         lds_barrier();
-        for (int t = 0; t < ntiles; t += 2) {
-            int issued = 0;
-            for (int u = 4; u < 6; ++u) {
-                if (t + u < ntiles) {
-                    issue(kh, kstage((t + u) % (2 * kStages)), koff, t + u);
+        for (int t0 = 0; t0 < ntiles; t0 += 2 * kStages) {
+            static_for<kStages>([&](auto pc) {
+                constexpr int S0 = 2 * decltype(pc)::value;   // stages of tiles t and t+1
+                const int t = t0 + S0;
+                if (t >= ntiles) return;
+                int issued = 0;
+                if (t + 4 < ntiles) {
+                    issue(kh, kstage((S0 + 4) % (2 * kStages)), koff, t + 4);
                     ++issued;
                 }
-            }
-            body(t, t % (2 * kStages));
-            if (t + 1 < ntiles) body(t + 1, (t + 1) % (2 * kStages));
-            wait_vmcnt(issued * LOADS);
-            lds_barrier();
+                if (t + 5 < ntiles) {
+                    issue(kh, kstage((S0 + 5) % (2 * kStages)), koff, t + 5);
+                    ++issued;
+                }
+                body(t, std::integral_constant<int, S0>{});
+                if (t + 1 < ntiles) body(t + 1, std::integral_constant<int, S0 + 1>{});
+                wait_vmcnt(issued * LOADS);
+                lds_barrier();
+            });
         }
     };
 
     // ---- pass 1: row max ---------------------------------------------------
     const v16i zero16 = v16i{};
     int32_t mrow = INT_MIN;
-    run_k_tiles([&](int t, int st) {
+    run_k_tiles([&](int t, auto st) {
         v16i s0 = scores(st, 0, zero16);
         v16i s1 = scores(st, 1, zero16);
         mask(s0, t * kLongTile, INT_MIN);
@@ -274,7 +294,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
 
     // ---- pass 2: row sum of the table entries ------------------------------
     uint32_t E = 0;
-    run_k_tiles([&](int t, int st) {
+    run_k_tiles([&](int t, auto st) {
         v16i s0 = scores(st, 0, cinit);
         v16i s1 = scores(st, 1, cinit);
         mfma_result_guard(s0, s1);           // the slot word (inline asm) reads them
@@ -321,13 +341,12 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
         hi = static_cast<int>(h);
         lo = static_cast<int>(l ^ 0x80808080u);
     };
-    run_kv_tiles([&](int t, int st) {
+    run_kv_tiles([&](int t, auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
         const bool colsum_turn = (t % kLongWaves) == wave;
-        uint32_t va[2 * DB];
-#pragma unroll
-        for (int i = 0; i < 2 * DB; ++i) va[i] = vaddr[i] + static_cast<uint32_t>(st * L::TB);
         auto kblock = [&](auto kbc) {
             constexpr int kb = decltype(kbc)::value;
+            auto& st = st_c;
             v16i s = scores(st, kb, cinit);
             mfma_result_guard(s);            // the slot word (inline asm) reads them
             mask(s, t * kLongTile + 32 * kb, kMasked);
@@ -344,7 +363,7 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
                 pa = v4i{pack(s, 0), pack(s, 1), pack(s, 2), pack(s, 3)};
             }
             v4i vb[DB];
-            tr8_operands<DB, kb * 32 * D>(va, vb);
+            tr8_operands<DB, ST * L::TB + kb * 32 * D>(vaddr, vb);
 #pragma unroll
             for (int db = 0; db < DB; ++db) o[db] = mfma_i8_32x32x32(pa, vb[db], o[db]);
             if constexpr (P16) {
