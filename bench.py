@@ -492,13 +492,40 @@ def roofline(config, tops, gbs):
     return roof
 
 
+_SLEEP_CYCLES_PER_US = None
+
+
+def hold_gpu(stream):
+    """Queue a 150 us spin kernel ahead of a timed region, so that the host
+    has enqueued the first dozen or so calls (about 8 us each through the
+    Python binding) when the first event is reached: the region then starts
+    with the GPU's first call, not with the host's submission of it. Later
+    calls are submitted while earlier ones run, so a workload whose calls
+    are shorter than their submission still measures the host-bound rate. A
+    longer hold would idle the GPU (one spinning wave) long enough for its
+    clock to drop."""
+    import torch
+
+    global _SLEEP_CYCLES_PER_US
+    if _SLEEP_CYCLES_PER_US is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record(stream)
+        torch.cuda._sleep(1_000_000)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_US = 1_000_000 / max(1.0, e0.elapsed_time(e1) * 1e3)
+    torch.cuda._sleep(int(150.0 * _SLEEP_CYCLES_PER_US))
+
+
 def measure(w, steps, warmup, extra_timing=False, settle_s=CLOCK_SETTLE_S):
     """Times intattn_forward over workload w with inputs resident in HBM.
 
     First settle_s seconds of untimed calls (the GPU leaves its idle clocks),
     then `warmup` untimed calls, then exactly `steps` calls bracketed by
     synchronisation and HIP events recorded on the stream the library
-    launches on (the caller's current stream). Returns ms_per_step, the wall
+    launches on (the caller's current stream); a spin kernel queued before
+    the first event keeps the GPU busy while the host enqueues the calls. Returns ms_per_step, the wall
     time of the timed region, the output (numpy) and, with extra_timing,
     five more blocks (median) and one block over input copies totalling more
     than 512 MB (cold caches).
@@ -525,6 +552,7 @@ def measure(w, steps, warmup, extra_timing=False, settle_s=CLOCK_SETTLE_S):
     ev1.record(stream)
     torch.cuda.synchronize(dev)
     t_wall0 = time.perf_counter()
+    hold_gpu(stream)
     ev0.record(stream)
     for _ in range(steps):
         call()
@@ -536,6 +564,7 @@ def measure(w, steps, warmup, extra_timing=False, settle_s=CLOCK_SETTLE_S):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize(dev)
+            hold_gpu(stream)
             e0.record(stream)
             for i in range(steps):
                 qs, ks, vs, os_ = sets[i % len(sets)]
