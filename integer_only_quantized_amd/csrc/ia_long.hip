@@ -185,6 +185,30 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
         }
         return s;
     };
+    // Both S^T blocks of the tile in stage ST: all eight fragment reads are
+    // issued before the first MFMA (one LDS round trip per tile, not one per
+    // pair of fragments)
+    auto scores2 = [&](auto st_c, const v16i& c0, v16i& s0, v16i& s1) {
+        constexpr int ST = decltype(st_c)::value;
+        v4i a[2][KS];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                a[kb][ks] = *reinterpret_cast<const v4i*>(lds_raw + kfo[ks] + (offsetof(L, k) + ST * L::TB) +
+                                                          32 * kb * D);
+        // every fragment is an operand here, so all reads are issued (and
+        // waited for once) before the MFMAs
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(a[0][ks]), "+v"(a[1][ks]));
+        s0 = c0;
+        s1 = c0;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s0 = mfma_i8_32x32x32(a[0][ks], qf[ks], s0);
+            s1 = mfma_i8_32x32x32(a[1][ks], qf[ks], s1);
+        }
+    };
     // key j0 + acc_row(r, hh) is allowed iff 8(r/4) + (r%4) < kend_row - j0 - 4hh
     auto mask = [&](v16i& s, int j0, int32_t fill) {
         if (j0 + 32 > kend_wave) {
@@ -276,8 +300,8 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     const v16i zero16 = v16i{};
     int32_t mrow = INT_MIN;
     run_k_tiles([&](int t, auto st) {
-        v16i s0 = scores(st, 0, zero16);
-        v16i s1 = scores(st, 1, zero16);
+        v16i s0, s1;
+        scores2(st, zero16, s0, s1);
         mask(s0, t * kLongTile, INT_MIN);
         mask(s1, t * kLongTile + 32, INT_MIN);
 #pragma unroll
@@ -295,8 +319,8 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     // ---- pass 2: row sum of the table entries ------------------------------
     uint32_t E = 0;
     run_k_tiles([&](int t, auto st) {
-        v16i s0 = scores(st, 0, cinit);
-        v16i s1 = scores(st, 1, cinit);
+        v16i s0, s1;
+        scores2(st, cinit, s0, s1);
         mfma_result_guard(s0, s1);           // the slot word (inline asm) reads them
         mask(s0, t * kLongTile, kMasked);
         mask(s1, t * kLongTile + 32, kMasked);
