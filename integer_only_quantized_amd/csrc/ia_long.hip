@@ -407,8 +407,65 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
                 }
             }
         };
-        kblock(std::integral_constant<int, 0>{});
-        kblock(std::integral_constant<int, 1>{});
+        if constexpr (P16) {
+            kblock(std::integral_constant<int, 0>{});
+            kblock(std::integral_constant<int, 1>{});
+        } else {
+            // uint8 P, the two blocks interleaved in four steps so that each
+            // step's MFMAs run under the other block's integer work and LDS
+            // waits: (A) block 0's scores and table reads; (B) block 1's
+            // scores while block 0's P operand is formed and its V operands
+            // read; (C) block 0's P.V while block 1's table reads go out;
+            // (D) block 1's P operand and P.V
+            const int j0 = t * kLongTile;
+            auto& st = st_c;
+            uint32_t e[16];
+            v16i s = scores(st, 0, cinit);
+            mfma_result_guard(s);            // the slot word (inline asm) reads them
+            mask(s, j0, kMasked);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) e[i] = table_entry(s[i]);
+            __builtin_amdgcn_sched_barrier(0);
+            s = scores(st, 1, cinit);
+            v4i pa0;
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4)
+                pa0[w4] = static_cast<int>(pack_top_bytes(prob_word(e[4 * w4], R2), prob_word(e[4 * w4 + 1], R2),
+                                                          prob_word(e[4 * w4 + 2], R2),
+                                                          prob_word(e[4 * w4 + 3], R2)));
+            auto colsum_add = [&](const v4i (&vb)[DB]) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    asm volatile("" : "+v"(cs[db]));
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) cs[db] = __builtin_amdgcn_sdot4(vb[db][w], 0x01010101, cs[db], false);
+                }
+            };
+            {
+                v4i vb0[DB];
+                tr8_operands<DB, ST * L::TB>(vaddr, vb0);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) o[db] = mfma_i8_32x32x32(pa0, vb0[db], o[db]);
+                if (colsum_turn) colsum_add(vb0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_result_guard(s);
+            mask(s, j0 + 32, kMasked);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) e[i] = table_entry(s[i]);
+            __builtin_amdgcn_sched_barrier(0);
+            v4i pa1;
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4)
+                pa1[w4] = static_cast<int>(pack_top_bytes(prob_word(e[4 * w4], R2), prob_word(e[4 * w4 + 1], R2),
+                                                          prob_word(e[4 * w4 + 2], R2),
+                                                          prob_word(e[4 * w4 + 3], R2)));
+            v4i vb1[DB];
+            tr8_operands<DB, ST * L::TB + 32 * D>(vaddr, vb1);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db] = mfma_i8_32x32x32(pa1, vb1[db], o[db]);
+            if (colsum_turn) colsum_add(vb1);
+        }
     });
     // column sums: lanes l and l^32 hold the two key halves; waves hold tiles
 #pragma unroll
