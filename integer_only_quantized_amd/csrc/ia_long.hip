@@ -68,7 +68,7 @@ struct LongLds {
 };
 
 template <int D, int KM, bool P16>
-__global__ __launch_bounds__(256) void ia_long_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(P16 ? 2 : 3))) void ia_long_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, const int8_t* __restrict__ v,
     int8_t* __restrict__ out, const IaKernelParams P, int nqb, InvariantDiv map_div, int32_t* __restrict__ row_max,
     uint32_t* __restrict__ row_sum) {
@@ -297,17 +297,78 @@ __global__ __launch_bounds__(256) void ia_long_kernel(
     };
 
     // ---- pass 1: row max ---------------------------------------------------
+    // Wave w takes the 64 rows of row groups g0 = 2 (w & 1) and g0 + 1 (the
+    // 32-row groups of waves g0 and g0 + 1 in the other passes) and key block
+    // kbw = w >> 1 of every tile: each K fragment set feeds two MFMA chains,
+    // so a wave reads half the fragments that its own 32 rows over both key
+    // blocks would need. The two key blocks' maxima of a row meet through
+    // LDS (the column-sum area, unused until the end).
     const v16i zero16 = v16i{};
-    int32_t mrow = INT_MIN;
-    run_k_tiles([&](int t, auto st) {
-        v16i s0, s1;
-        scores2(st, zero16, s0, s1);
-        mask(s0, t * kLongTile, INT_MIN);
-        mask(s1, t * kLongTile + 32, INT_MIN);
+    const int g0 = 2 * (wave & 1);
+    const int kbw = wave >> 1;
+    v4i qg[2][KS];
+    int kend_gw[2], kend_gr[2], kend_gl[2];
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mrow = max(mrow, max(max(s0[r], s0[r + 1]), max(s1[r], s1[r + 1])));
+    for (int gi = 0; gi < 2; ++gi) {
+        const int qa = q0 + 32 * (g0 + gi);
+        const int row = qa + l32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (row < P.Sq)
+                qg[gi][ks] = *reinterpret_cast<const v4i*>(qh + static_cast<size_t>(row) * D + 32 * ks + 16 * hh);
+            else
+                qg[gi][ks] = v4i{0, 0, 0, 0};
+        }
+        kend_gw[gi] = P.causal ? min(P.Skv, qa + shift + 1) : P.Skv;
+        kend_gr[gi] = P.causal ? min(P.Skv, row + shift + 1) : P.Skv;
+        kend_gl[gi] = P.causal ? min(P.Skv, qa + 31 + shift + 1) : P.Skv;
+    }
+    uint32_t kfw[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kfw[ks] = kfo[ks] + static_cast<uint32_t>(32 * kbw * D);
+    auto mask_g = [&](v16i& sc, int j0, int kw, int kr) {
+        if (j0 + 32 > kw) {
+            const int lim = kr - j0 - 4 * hh;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + (r & 3) >= lim) sc[r] = INT_MIN;
+        }
+    };
+    int32_t mg0 = INT_MIN, mg1 = INT_MIN;
+    run_k_tiles([&](int t, auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        const int jb = t * kLongTile + 32 * kbw;
+        if (jb >= kend_gl[1]) return;        // no row of either group attends this block
+        v4i a[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            a[ks] = *reinterpret_cast<const v4i*>(lds_raw + kfw[ks] + (offsetof(L, k) + ST * L::TB));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(a[ks]));
+        v16i s0 = zero16, s1 = zero16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s0 = mfma_i8_32x32x32(a[ks], qg[0][ks], s0);
+            s1 = mfma_i8_32x32x32(a[ks], qg[1][ks], s1);
+        }
+        mask_g(s0, jb, kend_gw[0], kend_gr[0]);
+        mask_g(s1, jb, kend_gw[1], kend_gr[1]);
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            mg0 = max(max(mg0, s0[r]), s0[r + 1]);
+            mg1 = max(max(mg1, s1[r]), s1[r + 1]);
+        }
     });
-    mrow = max(mrow, __shfl_xor(mrow, 32));
+    mg0 = max(mg0, __shfl_xor(mg0, 32));
+    mg1 = max(mg1, __shfl_xor(mg1, 32));
+    int32_t* const xm = &lds.colsum[0][0];   // [row group][key block][row]
+    static_assert(sizeof(lds.colsum) >= 4 * 2 * 32 * sizeof(int32_t), "row-max exchange fits");
+    if (hh == 0) {
+        xm[(g0 * 2 + kbw) * 32 + l32] = mg0;
+        xm[((g0 + 1) * 2 + kbw) * 32 + l32] = mg1;
+    }
+    lds_barrier();
+    const int32_t mrow = max(xm[(wave * 2) * 32 + l32], xm[(wave * 2 + 1) * 32 + l32]);
 
     // row constants of the slot arithmetic
     v16i cinit;
