@@ -7,9 +7,11 @@
 // steps 2-3; integer widths and roundings as stated in include/intattn.h.
 //
 // Structure:
-//   * one workgroup = 4 waves = 128 query rows of one (b, h); each wave owns
-//     32 rows, holds their Q fragments, and produces S^T blocks (32 keys x
-//     32 queries) on v_mfma_i32_32x32x32_i8, so each lane holds one row;
+//   * one workgroup = 4 waves = 128 query rows of one (b, h); in the row-sum
+//     and P.V passes each wave owns 32 rows, holds their Q fragments, and
+//     produces S^T blocks (32 keys x 32 queries) on v_mfma_i32_32x32x32_i8,
+//     so each lane holds one row; in the row-max pass each wave takes 64
+//     rows and one of the tile's two key blocks;
 //   * keys and values arrive in tiles of 64 rows through an LDS ring filled
 //     by global_load_lds_dwordx4 (no register staging). The P.V pass uses
 //     three K+V stages: tile t+2 is requested while tile t is computed, and
@@ -29,8 +31,10 @@
 //     shared exp table; the entries are summed into E; (3) the same table
 //     entry e gives the probability byte arithmetically: the top byte of
 //     e * 2R + 2^23 + 2^31 (mod 2^32) is p XOR 0x80, i.e. p - 128 as int8,
-//     which is the P operand of P.V. The +128 * colsum(V) correction is
-//     summed from the same B operands, each tile by one wave in turn;
+//     which is the P operand of P.V (with uint8 P the tile's two key blocks
+//     are interleaved: one block's MFMAs run under the other's integer
+//     work). The +128 * colsum(V) correction is summed from the same B
+//     operands, each tile by one wave in turn;
 //   * rows past Skv read in-bounds bytes of the last valid row; their scores
 //     are masked to p = 0, and since colsum covers exactly the rows fed,
 //     their values cancel: sum (p - 128) v + 128 sum v = sum p v;
