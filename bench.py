@@ -442,8 +442,8 @@ def variants(steps=None):
 
     # decode with keys split over several workgroups per head (workspace):
     # batch 1 (32 heads: one workgroup each on the decode kernel) and caches
-    # past the decode kernel's 16384 keys (the long-row kernel without a
-    # workspace); HBM GB/s of K + V read once
+    # past the decode kernel's 16384 keys (without a workspace: one workgroup
+    # per head streaming K three times); HBM GB/s of K + V read once
     res["split_decode"] = {}
     for (Bc, Hc, Skv) in ((1, 32, 8192), (8, 32, 32768), (2, 32, 65535)):
         ql = codes((Bc, Hc, 1, D))

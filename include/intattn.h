@@ -180,11 +180,12 @@ typedef struct intattn_variant {
                             over several workgroups per head (exact: the row
                             max and sum are combined before any probability,
                             and the P.V partials are integers). NULL: those
-                            shapes run on the long-row kernel (Skv > 16384;
-                            K is then read three times by one workgroup per
-                            head, about 10x slower: 0.46 TB/s measured on a
-                            65535-key cache) or on the decode kernel (one
-                            workgroup per head). intattn_forward never
+                            shapes run one workgroup per head, on the decode
+                            kernel (Skv <= 16384) or, past 16384 keys, on its
+                            three-pass form that keeps no scores and reads K
+                            three times (about 3x slower than split on a
+                            65535-key cache at 64 heads: 1.5 against
+                            4.9 TB/s of K and V). intattn_forward never
                             splits: it has no workspace                       */
     uint64_t workspace_bytes; /* size of workspace                           */
 } intattn_variant;

@@ -367,10 +367,11 @@ def forward_ex(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False
     (skv > 16384), and fewer than 128 heads (B*H < 128) with skv >= 4096.
     The workspace is a uint8 tensor on q's device of at least
     workspace_bytes(...) bytes; when not given it is allocated here on every
-    such call (pass one to avoid that). workspace=False runs without one:
-    skv > 16384 then falls to the long-row kernel (about 0.46 TB/s on a
-    65535-key cache, against about 5 TB/s split), and the few-heads case
-    runs the decode kernel with one workgroup per head. Returns out, or
+    such call (pass one to avoid that). workspace=False runs without one,
+    one workgroup per head: skv > 16384 then streams K three times without
+    keeping the scores (about 1.5 TB/s of K and V on a 65535-key cache at 64
+    heads, against about 5 TB/s split), and the few-heads case runs the
+    decode kernel. Returns out, or
     (out, row_max, row_sum) with stats (row_sum in Q15 units: 128 times the
     uint8 table's sum)."""
     import torch

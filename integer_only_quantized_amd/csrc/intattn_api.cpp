@@ -145,7 +145,7 @@ int dispatch(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int
              void* workspace = nullptr) {
     if (workspace != nullptr && uses_split(kp.B, kp.H, kp.Sq, kp.Skv))
         return ia::launch_decode_split(q, k, v, out, D, kp, stream, workspace, row_max, row_sum);
-    if (kp.Sq == 1 && kp.Skv <= ia::decode_max_keys())
+    if (kp.Sq == 1)   // past decode_max_keys() keys: three passes over K, no scores kept
         return ia::launch_decode(q, k, v, out, D, kp, stream, row_max, row_sum);
     if (kp.Skv <= ia::short_max_keys(D))
         return ia::launch_short(q, k, v, out, D, kp, stream, row_max, row_sum);

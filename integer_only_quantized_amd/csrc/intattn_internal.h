@@ -92,7 +92,8 @@ int launch_short(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out,
 int launch_short16(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,
                    const IaKernelParams& kp, void* stream, int32_t* row_max, uint32_t* row_sum);
 
-// Sq == 1 and Skv <= decode_max_keys(): one head per workgroup, HBM streaming.
+// Sq == 1: one head per workgroup, HBM streaming; past decode_max_keys() keys
+// the scores are not kept and K is streamed three times.
 int decode_max_keys();
 
 // Decode over long caches, keys split into chunks over several workgroups

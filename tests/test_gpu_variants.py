@@ -324,5 +324,54 @@ def test_split_decode_bit_exact(B, H, Hkv, Skv, D, lut, prob_bits, lut_bits, cap
                       lut_bits=lut_bits, workspace=False)
     torch.cuda.synchronize()
     _eq("split repeat", b.cpu().numpy(), a.cpu().numpy())
-    _eq("split vs long-row kernel", c.cpu().numpy(), ref)
+    _eq("split vs the call without a workspace", c.cpu().numpy(), ref)
     _eq("split through a given workspace", a.cpu().numpy(), ref)
+
+
+# Decode past 16384 keys without a workspace: one workgroup per head, K
+# streamed three times, P formed chunk by chunk (8192 keys) in LDS.
+LONG_DECODE_CASES = [
+    # (B, H, Hkv, Skv, D, lut, prob_bits, lut_bits, cap_extra, seed, kind): one key past the
+    # decode kernel's limit, a ragged last chunk, exactly two chunks, the largest cache,
+    # grouped heads, cache prefixes, every table and probability width
+    (2, 3, 3, 16385, 128, 32, 8, 16, 0, 950, "normal"),
+    (1, 4, 2, 16384 + 255, 64, 32, 8, 16, 33, 951, "channel_outliers"),
+    (1, 2, 1, 3 * 8192, 128, 64, 8, 8, 0, 952, "student_t_tail"),
+    (1, 2, 2, 65535, 128, 32, 8, 16, 0, 953, "normal"),
+    (2, 4, 1, 30001, 64, 128, 16, 16, 5, 954, "channel_outliers"),
+    (1, 3, 3, 40961, 128, 32, 16, 8, 0, 955, "student_t_tail"),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,Skv,D,lut,prob_bits,lut_bits,cap_extra,seed,kind", LONG_DECODE_CASES)
+def test_long_decode_without_workspace_bit_exact(B, H, Hkv, Skv, D, lut, prob_bits, lut_bits, cap_extra, seed,
+                                                 kind):
+    w = W.make_random(B, H, 1, Skv + cap_extra, D, False, seed, kind, name="longdec")
+    k = np.ascontiguousarray(w.k[:, :Hkv])
+    v = np.ascontiguousarray(w.v[:, :Hkv])
+    _say(f"case long decode B={B} H={H} Hkv={Hkv} Skv={Skv} cap={Skv + cap_extra} D={D} lut={lut} "
+         f"prob_bits={prob_bits} lut_bits={lut_bits}")
+    out, rm, rs = IA.forward_ex(_dev(w.q), _dev(k), _dev(v), w.scales, O.DEFAULT_CLIP, False, lut, stats=True,
+                                skv=Skv, prob_bits=prob_bits, lut_bits=lut_bits, workspace=False)
+    torch.cuda.synchronize()
+    ref, m, E, _ = O.forward(w.q, k[:, :, :Skv], v[:, :, :Skv], w.scales, O.DEFAULT_CLIP, False, stats=True,
+                             lut_size=lut, kv_heads=Hkv, prob_bits=prob_bits, lut_bits=lut_bits)
+    _eq("long decode out", out.cpu().numpy(), ref)
+    _eq("long decode row_max", rm.cpu().numpy(), m)
+    _eq("long decode row_sum", rs.cpu().numpy().view(np.uint32), E * (128 if lut_bits == 8 else 1))
+
+
+def test_long_decode_plain_entry_point_and_debug():
+    """intattn_forward and intattn_forward_debug (no workspace argument) on
+    a 20000-key decode: the same bits as the oracle, row statistics too."""
+    w = W.make_random(2, 4, 1, 20000, 128, False, 960, "normal", name="longdec")
+    _say("case long decode plain/debug B=2 H=4 Skv=20000 D=128")
+    ref, m, E, _ = O.forward(w.q, w.k, w.v, w.scales, O.DEFAULT_CLIP, False, stats=True)
+    out = IA.forward(_dev(w.q), _dev(w.k), _dev(w.v), w.scales, O.DEFAULT_CLIP, False)
+    o2, rm, rs, pr = IA.forward_debug(_dev(w.q), _dev(w.k), _dev(w.v), w.scales, O.DEFAULT_CLIP, False)
+    torch.cuda.synchronize()
+    assert pr is None
+    _eq("plain out", out.cpu().numpy(), ref)
+    _eq("debug out", o2.cpu().numpy(), ref)
+    _eq("debug row_max", rm.cpu().numpy(), m)
+    _eq("debug row_sum", rs.cpu().numpy().view(np.uint32), E)
