@@ -13,7 +13,8 @@ namespace {
 constexpr int kDecodeMaxKeys = 16384;
 
 // Decode kernel: one query row per head (Sq = 1), keys streamed from HBM.
-// One workgroup (4 waves) per (b, h). D/16 consecutive lanes cover one key
+// One workgroup (NWQ = 4 waves, or 16 with fewer heads than compute units)
+// per (b, h). D/16 consecutive lanes cover one key
 // row with 16-byte loads (fully coalesced); each lane handles 4 keys.
 //   A: scores s_j = q . k_j: four sdot4 per 16 bytes, then a butterfly over
 //      the D/16 lanes of a row (DPP), scores kept in LDS (int32 per key);
@@ -30,13 +31,13 @@ constexpr int kDecodeThreads = 256;
 constexpr int kDecodeUnroll = 2;
 
 
-template <int D, bool P16, int QH>
-__global__ __launch_bounds__(kDecodeThreads * QH) void ia_decode_kernel(
+template <int D, bool P16, int QH, int NWQ>
+__global__ __launch_bounds__(64 * NWQ * QH) void ia_decode_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ k, const int8_t* __restrict__ v,
     int8_t* __restrict__ out, const IaKernelParams P, int skv_pad, int32_t* __restrict__ row_max,
     uint32_t* __restrict__ row_sum) {
     static_assert(QH == 1 || (QH == 2 && !P16), "two query heads a workgroup with uint8 P only");
-    constexpr int NT = kDecodeThreads * QH;     // threads: 4 waves per query head
+    constexpr int NT = 64 * NWQ * QH;           // threads: NWQ waves per query head
     constexpr int NW = NT / 64;                 // waves
     constexpr int CPR = D / 16;                 // lanes per key row
     constexpr int GPW = 64 / CPR;               // key groups (of 4 keys) per wave
@@ -561,17 +562,17 @@ int launch_decode_long_t(const int8_t* q, const int8_t* k, const int8_t* v, int8
 
 int decode_max_keys() { return kDecodeMaxKeys; }
 
-template <int D, bool P16, int QH>
+template <int D, bool P16, int QH, int NWQ = kDecodeThreads / 64>
 int launch_decode_t(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, const IaKernelParams& kp,
                     hipStream_t stream, unsigned blocks, int skv_pad, int32_t* row_max, uint32_t* row_sum) {
     constexpr int kBytesPerKey = P16 ? 6 : 5 * QH;     // int32 score/slot + uint8 or uint16 p, per query head
     constexpr int kMaxKeys = QH == 1 ? kDecodeMaxKeys : kDecodeMaxKeys / 2;
     static std::atomic<uint64_t> lds_set{0};
-    const int st = ensure_dynamic_lds(reinterpret_cast<const void*>(&ia_decode_kernel<D, P16, QH>),
+    const int st = ensure_dynamic_lds(reinterpret_cast<const void*>(&ia_decode_kernel<D, P16, QH, NWQ>),
                                       kBytesPerKey * kMaxKeys, lds_set);
     if (st != INTATTN_OK) return st;
     const size_t shm = static_cast<size_t>(skv_pad) * kBytesPerKey;
-    hipLaunchKernelGGL((ia_decode_kernel<D, P16, QH>), dim3(blocks), dim3(kDecodeThreads * QH), shm, stream, q, k, v, out,
+    hipLaunchKernelGGL((ia_decode_kernel<D, P16, QH, NWQ>), dim3(blocks), dim3(64 * NWQ * QH), shm, stream, q, k, v, out,
                        kp, skv_pad, row_max, row_sum);
     return hipGetLastError() == hipSuccess ? INTATTN_OK : INTATTN_E_HIP;
 }
@@ -590,6 +591,15 @@ int launch_decode(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out
                        : launch_decode_long_t<128, false>(q, k, v, out, kp, stream, nb, row_max, row_sum);
     }
     const int skv_pad = (kp.Skv + 255) / 256 * 256;
+    // fewer heads than compute units: 16 waves a head (more loads in flight
+    // per compute unit), as for the three-pass form
+    if (heads < 256) {
+        if (kp.prob_bits == 16)
+            return D == 64 ? launch_decode_t<64, true, 1, 16>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum)
+                           : launch_decode_t<128, true, 1, 16>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum);
+        return D == 64 ? launch_decode_t<64, false, 1, 16>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum)
+                       : launch_decode_t<128, false, 1, 16>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum);
+    }
     if (kp.prob_bits == 16)
         return D == 64 ? launch_decode_t<64, true, 1>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum)
                        : launch_decode_t<128, true, 1>(q, k, v, out, kp, stream, nb, skv_pad, row_max, row_sum);
