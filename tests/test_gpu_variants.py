@@ -140,7 +140,8 @@ def test_bert_size_fine_table_all_heads():
 
 P16_CASES = [
     # (B, H, Hkv, Sq, Skv, D, causal, lut, seed, kind): uint16 probabilities on
-    # the long-row kernel (every Sq > 1 shape) and the decode kernel (Sq = 1)
+    # the long-row kernel (longer rows), the decode kernel (Sq = 1) and, below,
+    # the short-row kernel
     (2, 2, 2, 128, 128, 64, False, 32, 600, "normal"),
     (1, 2, 2, 197, 197, 64, False, 64, 601, "channel_outliers"),
     (1, 2, 2, 300, 1100, 128, True, 32, 602, "student_t_tail"),
@@ -149,7 +150,7 @@ P16_CASES = [
     (2, 2, 2, 1, 3001, 64, False, 64, 605, "channel_outliers"),
     (1, 2, 1, 1, 777, 128, True, 128, 606, "normal"),
     # the decode kernel's largest key count (96 KB of LDS with uint16 P), and
-    # one key past it (a single query row on the long-row kernel)
+    # one key past it (without a workspace: the three-pass decode kernel)
     (1, 2, 2, 1, 16384, 128, False, 32, 608, "normal"),
     (1, 2, 1, 1, 16385, 64, False, 32, 609, "student_t_tail"),
     # the short-row kernel (Skv <= 512 at d = 64, <= 256 at d = 128): full
@@ -312,7 +313,7 @@ def test_split_decode_bit_exact(B, H, Hkv, Skv, D, lut, prob_bits, lut_bits, cap
     _eq("split out", out.cpu().numpy(), ref)
     _eq("split row_max", rm.cpu().numpy(), m)
     _eq("split row_sum", rs.cpu().numpy().view(np.uint32), E * (128 if lut_bits == 8 else 1))
-    # the same call without a workspace (long-row kernel) agrees, and a second
+    # the same call without a workspace (one workgroup per head) agrees, and a second
     # call through the same workspace gives the same result (accumulators cleared)
     ws = torch.empty(IA.workspace_bytes(B, H, 1, Skv, D), dtype=torch.uint8, device="cuda")
     qd, kd, vd = _dev(w.q), _dev(k), _dev(v)
