@@ -175,8 +175,9 @@ typedef struct intattn_variant {
     int32_t lut_bits;    /* table entry width: 16 (Q15, the specification
                             above) or 8 (uint8 entries); 0 means 16          */
     void*    workspace;  /* device memory, caller-owned, for decode (Sq = 1)
-                            with Skv > 16384, or with fewer than 128 heads
-                            (B*H) and Skv >= 4096: keys are split into chunks
+                            with Skv > 16384, or with Skv >= 4096 and
+                            Skv > 128*B*H (few heads for the cache length,
+                            each a workgroup): keys are split into chunks
                             over several workgroups per head (exact: the row
                             max and sum are combined before any probability,
                             and the P.V partials are integers). NULL: those
@@ -231,7 +232,7 @@ int intattn_derive_params_ex(const intattn_shape* shape, const intattn_scales* s
 /* Bytes of workspace intattn_forward_ex uses for this shape and variant
  * (256-byte aligned; int32 scores per key and head, per-chunk maxima and
  * sums, per-head accumulators), 0 when the shape does not use one (only
- * Sq = 1 with Skv > 16384, or B*H < 128 and Skv >= 4096, does). Host only,
+ * Sq = 1 with Skv > 16384, or Skv >= 4096 and Skv > 128*B*H, does). Host only,
  * pure. Returns 0 for an invalid shape as well. */
 uint64_t intattn_workspace_bytes(const intattn_shape* shape, const intattn_variant* variant);
 

@@ -364,7 +364,8 @@ def forward_ex(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False
     prob_bits-wide probabilities. Decode shapes (Sq = 1) split their keys
     over several workgroups per head, in a device workspace, in two cases:
     a cache longer than the single-workgroup decode kernel takes
-    (skv > 16384), and fewer than 128 heads (B*H < 128) with skv >= 4096.
+    (skv > 16384), and few heads for the cache length: skv >= 4096 and
+    skv > 128 * B * H.
     The workspace is a uint8 tensor on q's device of at least
     workspace_bytes(...) bytes; when not given it is allocated here on every
     such call (pass one to avoid that). workspace=False runs without one,

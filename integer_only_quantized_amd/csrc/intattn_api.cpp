@@ -3,7 +3,11 @@
 //
 // Kernel choice (all bit-identical to the specification in include/intattn.h,
 // for every table size and K/V head grouping):
-//   Sq == 1 and Skv <= 16384                -> decode kernel (HBM streaming)
+//   Sq == 1                                  -> decode kernel (HBM streaming;
+//                                               past 16384 keys its three-pass
+//                                               form), or with a workspace
+//                                               the split-decode kernels for
+//                                               the shapes uses_split names
 //   Skv <= 512 (d = 64) or 256 (d = 128)      -> short-row kernel (K/V in LDS)
 //   otherwise                                -> long-row kernel (tiled, 3 passes)
 // (table sizes, entry widths, K/V head groupings and probability widths all
@@ -132,12 +136,15 @@ long long rows_of(const IaKernelParams& kp) { return static_cast<long long>(kp.B
 
 // Decode shapes split their keys over several workgroups per head when the
 // caller gives a workspace: past the single-workgroup decode kernel's key
-// limit, and when fewer than 128 heads (a workgroup each) would leave most of
-// the GPU idle, from 4096 keys on (the split's four launches cost about
-// 17 us; one workgroup per head at 32 heads takes 29 us for 4096 keys).
+// limit, and when the heads (a workgroup each) are few for the cache length:
+// from 4096 keys on, once Skv > 128 * heads. Measured on MI355X with 16-wave
+// workgroups, 128-wide heads: 32 heads take 17 us unsplit against 21 us
+// split at 4096 keys but 30 against 24 at 8192; 64 heads take 32 against
+// 35 at 8192 keys and about the same either way at 16384; 96 heads 36
+// against 45 at 8192 but 106 against 88 at 16384.
 bool uses_split(int B, int H, int Sq, int Skv) {
     const long long heads = static_cast<long long>(B) * H;
-    return Sq == 1 && (Skv > ia::decode_max_keys() || (heads < 128 && Skv >= 4096));
+    return Sq == 1 && (Skv > ia::decode_max_keys() || (Skv >= 4096 && Skv > 128 * heads));
 }
 
 int dispatch(const int8_t* q, const int8_t* k, const int8_t* v, int8_t* out, int D,

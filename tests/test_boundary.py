@@ -336,8 +336,8 @@ def test_parameter_derivation_from_many_threads():
 
 
 def test_workspace_size_and_validation_before_any_device_call():
-    """Decode takes a workspace past the decode kernel's 16384 keys, and with
-    fewer than 128 heads from 4096 keys on: int32 scores per key and head,
+    """Decode takes a workspace past the decode kernel's 16384 keys, and from
+    4096 keys on when the keys outnumber 128 per head (B*H): int32 scores per key and head,
     per-chunk maxima and sums and per-head accumulators, each region 256-byte
     aligned; chunks of 4096 keys, halved down to 512 while the grid has fewer
     than 1024 workgroups. A workspace below that size, or not 256-byte
@@ -347,9 +347,12 @@ def test_workspace_size_and_validation_before_any_device_call():
     assert B.workspace_bytes(16, 32, 1, 16384, 128) == 0             # 512 heads: one workgroup each
     assert B.workspace_bytes(4, 32, 1, 8192, 128) == 0               # 128 heads
     assert B.workspace_bytes(1, 32, 1, 4095, 128) == 0               # too few keys to split
+    assert B.workspace_bytes(1, 32, 1, 4096, 128) == 0               # 128 keys per head: not more
+    assert B.workspace_bytes(2, 32, 1, 8192, 64) == 0                # 64 heads, 8192 keys
+    assert B.workspace_bytes(3, 32, 1, 16384, 128) > 0               # 96 heads, 16384 keys
     assert B.workspace_bytes(2, 32, 2, 40000, 128) == 0              # not a decode shape
     for (b, h, skv, d) in [(16, 32, 16385, 128), (2, 32, 65535, 128), (1, 3, 20000, 64), (1, 32, 8192, 128),
-                           (1, 32, 4096, 64)]:
+                           (1, 2, 4096, 64), (1, 32, 4097, 64)]:
         heads, chunk = b * h, 4096
         while chunk > 512 and heads * -(-skv // chunk) < 1024:
             chunk //= 2

@@ -120,7 +120,7 @@ def test_large_multiplier_variants(prob_bits, lut_bits):
 
 def test_large_multiplier_split_decode():
     """Keys split over workgroups (caller workspace): past 16384 keys, and
-    few heads from 4096 keys on."""
+    few heads for the cache length (Skv >= 4096 and Skv > 128 B H)."""
     for (B, H, Skv, D), n, mu in (((1, 4, 20000, 128), 32, 0.9), ((1, 2, 5000, 64), 128, 12.0)):
         s = _scale_for(mu, D, n)
         q, k, v = _inputs(B, H, 1, Skv, D, 4000 + Skv, 3)
