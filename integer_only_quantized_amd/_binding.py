@@ -115,6 +115,14 @@ def _load():
 
 _lib = _load()
 
+import torch as _torch  # noqa: E402  (already loaded by _load, ahead of the library)
+
+_I8 = _torch.int8
+# the current device and its raw stream handle, by torch's direct accessors
+# where present (the per-call host cost of the binding is part of every call)
+_cur_device = getattr(_torch._C, "_cuda_getDevice", None) or _torch.cuda.current_device
+_raw_stream = getattr(_torch._C, "_cuda_getCurrentRawStream", None)
+
 
 def strerror(code: int) -> str:
     return _lib.intattn_strerror(int(code)).decode()
@@ -164,12 +172,14 @@ _STRUCTS = {}
 
 
 def _structs(shape, scales):
-    """ctypes Shape/Scales for a call, cached per (shape, scales) so repeated
-    calls on the same workload marshal nothing new."""
+    """ctypes Shape/Scales for a call and their byref handles, cached per
+    (shape, scales) so repeated calls on the same workload marshal nothing
+    new."""
     key = (shape, scales if isinstance(scales, tuple) else tuple(scales))
     st = _STRUCTS.get(key)
     if st is None:
-        st = (Shape(*[int(x) for x in shape]), Scales(*[float(s) for s in key[1]]))
+        sh, sc = Shape(*[int(x) for x in shape]), Scales(*[float(s) for s in key[1]])
+        st = (sh, sc, ctypes.byref(sh), ctypes.byref(sc))
         if len(_STRUCTS) > 256:
             _STRUCTS.clear()
         _STRUCTS[key] = st
@@ -179,27 +189,25 @@ def _structs(shape, scales):
 def forward_raw(q_ptr, k_ptr, v_ptr, out_ptr, shape, scales, clip, causal, stream=None,
                 debug=None) -> int:
     """Call the C entry point with raw integer addresses; returns the status code."""
-    sh, sc = _structs(tuple(shape), scales)
+    bsh, bsc = _structs(tuple(shape), scales)[2:]
     if debug is None:
-        return _lib.intattn_forward(q_ptr, k_ptr, v_ptr, out_ptr, ctypes.byref(sh), ctypes.byref(sc),
-                                    float(clip), int(bool(causal)), stream)
+        return _lib.intattn_forward(q_ptr, k_ptr, v_ptr, out_ptr, bsh, bsc, float(clip), 1 if causal else 0,
+                                    stream)
     rm, rs, pr = debug
-    return _lib.intattn_forward_debug(q_ptr, k_ptr, v_ptr, out_ptr, ctypes.byref(sh),
-                                      ctypes.byref(sc), float(clip), int(bool(causal)), stream,
-                                      rm, rs, pr)
+    return _lib.intattn_forward_debug(q_ptr, k_ptr, v_ptr, out_ptr, bsh, bsc, float(clip), 1 if causal else 0,
+                                      stream, rm, rs, pr)
 
 
 def _check_tensors(q, k, v, grouped: bool = False):
-    import torch
-    i8 = torch.int8
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype is not i8 or not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+        if t.dtype is not _I8 or not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous 4-D int8 CUDA tensor [B, H, S, D]")
     B, H, Sq, D = q.shape
     ks = k.shape
     if ks[0] != B or (ks[1] != H and not grouped) or ks[3] != D or v.shape != ks:
         raise ValueError("shape mismatch between q, k and v")
-    if k.device != q.device or v.device != q.device:
+    dev = q.get_device()
+    if k.get_device() != dev or v.get_device() != dev:
         raise ValueError("q, k and v must be on the same device")
     return (B, H, Sq, ks[2], D)
 
@@ -209,28 +217,28 @@ def _stream(q):
     takes); torch's raw accessor when present, else the public Stream object.
     The library launches on the calling thread's current device, so q must
     live there."""
-    import torch
-    if q.device.index is not None and q.device.index != torch.cuda.current_device():
-        raise ValueError(f"tensors are on {q.device} but the current device is cuda:{torch.cuda.current_device()}; "
+    dev = q.get_device()
+    cur = _cur_device()
+    if dev >= 0 and dev != cur:
+        raise ValueError(f"tensors are on {q.device} but the current device is cuda:{cur}; "
                          "call under torch.cuda.device(tensor.device)")
-    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-    if raw is not None:
-        return raw(q.device.index)
-    return torch.cuda.current_stream(q.device).cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(dev)
+    return _torch.cuda.current_stream(q.device).cuda_stream
 
 
 def forward(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False, out=None):
     """out[B,H,Sq,D] int8 = integer attention of int8 q, k, v (torch CUDA tensors)."""
-    import torch
     shape = _check_tensors(q, k, v)
     if out is None:
-        out = torch.empty_like(q)
-    elif (out.shape != q.shape or out.dtype is not torch.int8 or not out.is_contiguous()
-          or out.device != q.device):
+        out = _torch.empty_like(q)
+    elif (out.dtype is not _I8 or out.shape != q.shape or not out.is_contiguous()
+          or out.get_device() != q.get_device()):
         raise ValueError("out must be a contiguous int8 tensor shaped like q, on q's device")
     code = forward_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), shape, scales,
                        clip, causal, _stream(q))
-    _check(code, "intattn_forward")
+    if code:
+        _check(code, "intattn_forward")
     return out
 
 
@@ -275,7 +283,7 @@ def qk_scores(q, k, out=None):
         _check_t("out", out, torch.int32, 4, q.device)
         if tuple(out.shape) != (B, H, Sq, Skv):
             raise ValueError("out must be [B, H, Sq, Skv]")
-    sh, _ = _structs((B, H, Sq, Skv, D), (1.0, 1.0, 1.0, 1.0))
+    sh = _structs((B, H, Sq, Skv, D), (1.0, 1.0, 1.0, 1.0))[0]
     _check(_lib.intattn_qk_scores(q.data_ptr(), k.data_ptr(), out.data_ptr(), ctypes.byref(sh), _stream(q)),
            "intattn_qk_scores")
     return out
@@ -303,7 +311,7 @@ def index_softmax(scores, D, scales, clip: float = DEFAULT_CLIP, causal: bool = 
     if stats:
         rm = torch.empty(scores.shape[:3], dtype=torch.int32, device=scores.device)
         rs = torch.empty(scores.shape[:3], dtype=torch.int32, device=scores.device)
-    sh, sc = _structs(shape, scales)
+    sh, sc = _structs(shape, scales)[:2]
     _check(_lib.intattn_index_softmax(scores.data_ptr(), probs.data_ptr(),
                                       rm.data_ptr() if stats else None, rs.data_ptr() if stats else None,
                                       ctypes.byref(sh), ctypes.byref(sc), float(clip), int(bool(causal)),
@@ -322,7 +330,7 @@ def fp_softmax(scores, D, scales, causal: bool = False, probs=None):
         _check_t("probs", probs, torch.uint8, 4, scores.device)
         if probs.shape != scores.shape:
             raise ValueError("probs must be shaped like scores")
-    sh, sc = _structs(shape, scales)
+    sh, sc = _structs(shape, scales)[:2]
     _check(_lib.intattn_fp_softmax(scores.data_ptr(), probs.data_ptr(), ctypes.byref(sh), ctypes.byref(sc),
                                    int(bool(causal)), _stream(scores)), "intattn_fp_softmax")
     return probs
@@ -343,7 +351,7 @@ def pv(probs, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False, out=N
         _check_t("out", out, torch.int8, 4, probs.device)
         if tuple(out.shape) != (B, H, Sq, D):
             raise ValueError("out must be [B, H, Sq, D]")
-    sh, sc = _structs((B, H, Sq, Skv, D), scales)
+    sh, sc = _structs((B, H, Sq, Skv, D), scales)[:2]
     _check(_lib.intattn_pv(probs.data_ptr(), v.data_ptr(), out.data_ptr(), ctypes.byref(sh), ctypes.byref(sc),
                            float(clip), int(bool(causal)), _stream(probs)), "intattn_pv")
     return out
@@ -384,7 +392,7 @@ def forward_ex(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool = False
           or out.device != q.device):
         raise ValueError("out must be a contiguous int8 tensor shaped like q, on q's device")
     var = Variant(int(lut_size), int(k.shape[1]), int(C), int(prob_bits), int(lut_bits))
-    sh, sc = _structs((B, H, Sq, skv, D), scales)
+    sh, sc = _structs((B, H, Sq, skv, D), scales)[:2]
     if workspace is not False:
         need = int(_lib.intattn_workspace_bytes(ctypes.byref(sh), ctypes.byref(var)))
         if need > 0:
@@ -421,7 +429,7 @@ def forward_ex_noalloc(q, k, v, scales, clip: float = DEFAULT_CLIP, causal: bool
           or out.device != q.device):
         raise ValueError("out must be a contiguous int8 tensor shaped like q, on q's device")
     var = Variant(int(lut_size), int(k.shape[1]), int(C), int(prob_bits), int(lut_bits))
-    sh, sc = _structs((B, H, Sq, skv, D), scales)
+    sh, sc = _structs((B, H, Sq, skv, D), scales)[:2]
     rm = rs = None
     if stats:
         rm = torch.empty((B, H, Sq), dtype=torch.int32, device=q.device)
