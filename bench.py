@@ -326,6 +326,32 @@ def _time_calls(fn, stream, n, warm_s=0.3):
     return e0.elapsed_time(e1) / n * 1e3
 
 
+def _time_calls_held(fn, stream, n, warm_s=0.3):
+    """(GPU us per call, host us per call) for calls whose host submission
+    may be as long as their GPU time (several launches a call): the host
+    time is taken over n calls first, then the GPU is held by a spin kernel
+    long enough for the host to queue n more, and the events time those."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        fn()
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for _ in range(n):
+        fn()
+    host_us = (time.perf_counter() - h0) / n * 1e6
+    torch.cuda.synchronize()
+    hold_gpu(stream)                          # calibrates the spin rate on first use
+    torch.cuda._sleep(int((1.5 * n * host_us + 200.0) * _SLEEP_CYCLES_PER_US))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3, host_us
+
+
 def variants(steps=None):
     """The variants beside the 32-entry MHA path: finer exp tables (64, 128
     entries), uint8 table entries and uint16 probabilities on the BERT and
@@ -363,7 +389,8 @@ def variants(steps=None):
             tops = ops / (us * 1e-6) / 1e12
             row[str(n)] = {"us_per_call": us, "int8_TOPS": tops, "mfma_frac": tops / PEAK_INT8_TOPS}
         res["fine_tables"][cfg] = row
-        # uint16 probabilities (32-entry table): the long-row kernel for every Sq > 1 shape
+        # uint16 probabilities (32-entry table): the short-row kernel's uint16 instances on BERT, the
+        # long-row kernel on causal prefill
         fn = lambda: ia.forward_ex(q, k, v, w.scales, w.clip, w.causal, 32, out=out, prob_bits=16)
         us = _time_calls(fn, stream, steps or (200 if cfg == "bert" else 30))
         tops = ops / (us * 1e-6) / 1e12
@@ -375,6 +402,7 @@ def variants(steps=None):
         tops = ops / (us * 1e-6) / 1e12
         res.setdefault("uint8_table", {})[cfg] = {"us_per_call": us, "int8_TOPS": tops,
                                                   "mfma_frac": tops / PEAK_INT8_TOPS}
+        print(f"# variants: tables and widths on {cfg} done", file=sys.stderr, flush=True)
 
     # grouped K/V heads on the decode shape: B=16, H=32, Skv=8192, d=128
     B, H, Skv, D = 16, 32, 8192, 128
@@ -407,6 +435,7 @@ def variants(steps=None):
             res.setdefault("uint8_table", {})["decode"] = {"us_per_call": us8, "GBs": gbs8,
                                                            "hbm_frac": gbs8 / PEAK_HBM_GBS}
         del k, v
+        print(f"# variants: grouped decode Hkv={hkv} done", file=sys.stderr, flush=True)
     torch.cuda.empty_cache()
 
     # cache update: one decode token and a 4096-token prefill chunk
@@ -443,7 +472,10 @@ def variants(steps=None):
     # decode with keys split over several workgroups per head (workspace):
     # batch 1 (32 heads: one workgroup each on the decode kernel) and caches
     # past the decode kernel's 16384 keys (without a workspace: one workgroup
-    # per head streaming K three times); HBM GB/s of K + V read once
+    # per head streaming K three times); HBM GB/s of K + V read once. A split
+    # call is four launches, whose host submission through the binding can
+    # outlast the GPU work at batch 1, so the GPU time is taken with the
+    # calls queued ahead, and the host time per call is reported beside it
     res["split_decode"] = {}
     for (Bc, Hc, Skv) in ((1, 32, 8192), (8, 32, 32768), (2, 32, 65535)):
         ql = codes((Bc, Hc, 1, D))
@@ -455,10 +487,11 @@ def variants(steps=None):
         row = {"workspace_bytes": ws.numel(), "bytes": nbytes}
         for name, w in (("split", ws), ("without_workspace", False)):
             fn = lambda w=w: ia.forward_ex(ql, kl, vl, scales, W.DEFAULT_CLIP, False, 32, out=ol, workspace=w)
-            us = _time_calls(fn, stream, steps or 30)
+            us, host_us = _time_calls_held(fn, stream, steps or 30)
             gbs = nbytes / (us * 1e-6) / 1e9
-            row[name] = {"us_per_call": us, "GBs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+            row[name] = {"us_per_call": us, "host_us_per_call": host_us, "GBs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
         res["split_decode"][f"B={Bc} H={Hc} Skv={Skv}"] = row
+        print(f"# variants: split decode B={Bc} H={Hc} Skv={Skv} done", file=sys.stderr, flush=True)
         del ql, kl, vl, ol, ws
         torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)

@@ -137,11 +137,12 @@ long long rows_of(const IaKernelParams& kp) { return static_cast<long long>(kp.B
 // Decode shapes split their keys over several workgroups per head when the
 // caller gives a workspace: past the single-workgroup decode kernel's key
 // limit, and when the heads (a workgroup each) are few for the cache length:
-// from 4096 keys on, once Skv > 128 * heads. Measured on MI355X with 16-wave
-// workgroups, 128-wide heads: 32 heads take 17 us unsplit against 21 us
-// split at 4096 keys but 30 against 24 at 8192; 64 heads take 32 against
-// 35 at 8192 keys and about the same either way at 16384; 96 heads 36
-// against 45 at 8192 but 106 against 88 at 16384.
+// from 4096 keys on, once Skv > 128 * heads. GPU time on MI355X (128-wide
+// heads, calls queued ahead of the GPU): 32 heads take 16.6 us unsplit
+// against 15.9 us split at 4096 keys (a near tie, left unsplit: one launch
+// instead of four costs the host less) but 29.8 against 24.3 at 8192; 64
+// heads 31.6 against 34.2 at 8192 keys and 55.8 against 58.1 at 16384; 96
+// heads 36.2 against 45.3 at 8192 but 106.5 against 88.6 at 16384.
 bool uses_split(int B, int H, int Sq, int Skv) {
     const long long heads = static_cast<long long>(B) * H;
     return Sq == 1 && (Skv > ia::decode_max_keys() || (Skv >= 4096 && Skv > 128 * heads));
