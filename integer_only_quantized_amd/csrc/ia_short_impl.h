@@ -123,41 +123,77 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
         voff[par] = static_cast<uint32_t>(row * D + 16 * ((lane % CPR) ^ v_swz<D>(row)) - par * 1024);
     }
     const bool stage_tail = L::KVBytes / D > P.Skv;     // some staged rows lie past Skv
-    auto stage = [&](const int8_t* src, bool is_v, int kb_first, int nblk, bool split) {
-        const uint32_t* off = is_v ? voff : koff;
+    // One wave's loads of a run of 1 KB pieces: piece lb (a compile-time
+    // index) goes from gsrc + lb KB + off[parity] to ldst + lb KB. Four
+    // consecutive pieces share one scalar base and one M0 value: the
+    // instruction's immediate offset (applied to the global and the LDS
+    // address alike) selects the piece within its 4 KB window, so a piece
+    // costs no scalar address arithmetic of its own. par0 is the parity of
+    // the run's first piece (the per-lane offsets alternate with the parity).
+    auto load_run = [&](const int8_t* gsrc, int8_t* ldst, uint32_t off0, uint32_t off1, int par0, auto lb_c) {
+        constexpr int lb = decltype(lb_c)::value;
+        constexpr int w = lb >> 2;
+        const uint32_t o = ((par0 + lb) & 1) ? off1 : off0;
+        __builtin_amdgcn_global_load_lds(gsrc + w * 4096 + o, (lds_void_t*)(ldst + w * 4096), 16, (lb & 3) * 1024, 0);
+    };
+    auto stage = [&](const int8_t* src, bool is_v, int kb_first, int nblk, auto split_c) {
+        constexpr bool split = decltype(split_c)::value;
+        const uint32_t off0 = is_v ? voff[0] : koff[0];
+        const uint32_t off1 = is_v ? voff[1] : koff[1];
+        // split: this wave loads pieces i0 .. i0 + LPB/2 - 1 of every block
         const int i0 = split ? qg * (LPB / 2) : 0;
-        const int ni = split ? LPB / 2 : LPB;
+        constexpr int NI = split ? LPB / 2 : LPB;
         if (!stage_tail) {
-#pragma unroll
-            for (int j = 0; j < NBH; ++j) {
-                if (j >= nblk) break;
-#pragma unroll
-                for (int ii = 0; ii < LPB; ++ii) {
-                    if (ii >= ni) break;
-                    const int i = i0 + ii;
-                    const int blk = (kb_first + j) * LPB + i;
-                    __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(blk) * 1024 + off[blk & 1],
-                                                     (lds_void_t*)(lds.kv + blk * 1024), 16, 0, 0);
-                }
+            const int first = kb_first * LPB + i0;
+            const int8_t* g = src + static_cast<size_t>(first) * 1024;
+            int8_t* l = lds.kv + first * 1024;
+            if constexpr (split && NI == 1) {
+                // one piece a block, LPB apart: piece j of the run is block j
+                static_for<NBH>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    if (j < nblk) load_run(g, l, off0, off1, first, std::integral_constant<int, j * LPB>{});
+                });
+            } else {
+                static_for<NBH>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    if (j < nblk) {
+                        static_for<NI>([&](auto ic) {
+                            constexpr int ii = decltype(ic)::value;
+                            load_run(g, l, off0, off1, first, std::integral_constant<int, j * LPB + ii>{});
+                        });
+                    }
+                });
             }
             // distinct markers keep the two paths apart (a merged last load
             // would hide the count of loads in flight from the compiler)
             asm volatile("; staged, no tail");
         } else {
+            // blocks wholly below Skv as above; only a block holding rows
+            // past Skv clamps its rows per lane
+            const int first = kb_first * LPB + i0;
+            const int8_t* g = src + static_cast<size_t>(first) * 1024;
+            int8_t* l = lds.kv + first * 1024;
+            static_for<NBH>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if (j < nblk) {
+                    if ((kb_first + j + 1) * 32 <= P.Skv) {
+                        static_for<NI>([&](auto ic) {
+                            load_run(g, l, off0, off1, first, std::integral_constant<int, j * LPB + decltype(ic)::value>{});
+                        });
+                    } else {
 #pragma unroll
-            for (int j = 0; j < NBH; ++j) {
-                if (j >= nblk) break;
-#pragma unroll
-                for (int ii = 0; ii < LPB; ++ii) {
-                    if (ii >= ni) break;
-                    const int i = i0 + ii;
-                    const int blk = (kb_first + j) * LPB + i;
-                    const int row = blk * (1024 / D) + lane / CPR;
-                    const int chunk = (lane % CPR) ^ (is_v ? v_swz<D>(row) : k_swz<D>(row));
-                    __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(min(row, P.Skv - 1)) * D + 16 * chunk,
-                                                     (lds_void_t*)(lds.kv + blk * 1024), 16, 0, 0);
+                        for (int ii = 0; ii < NI; ++ii) {
+                            const int i = i0 + ii;
+                            const int blk = (kb_first + j) * LPB + i;
+                            const int row = blk * (1024 / D) + lane / CPR;
+                            const int chunk = (lane % CPR) ^ (is_v ? v_swz<D>(row) : k_swz<D>(row));
+                            __builtin_amdgcn_global_load_lds(
+                                src + static_cast<size_t>(min(row, P.Skv - 1)) * D + 16 * chunk,
+                                (lds_void_t*)(lds.kv + blk * 1024), 16, 0, 0);
+                        }
+                    }
                 }
-            }
+            });
             asm volatile("; staged, tail rows clamped");
         }
     };
@@ -190,10 +226,9 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     // the block-by-block waits below.
     if (nvalid > 0) {
         if (qw0 + 32 <= P.Sq) {
-#pragma unroll
-            for (int i = 0; i < LPB; ++i)
-                __builtin_amdgcn_global_load_lds(qh + static_cast<size_t>(qw0) * D + i * 1024 + koff[i & 1],
-                                                 (lds_void_t*)(&lds.q[qg][i * 1024]), 16, 0, 0);
+            static_for<LPB>([&](auto ic) {
+                load_run(qh + static_cast<size_t>(qw0) * D, &lds.q[qg][0], koff[0], koff[1], 0, ic);
+            });
             asm volatile("; Q staged");
         } else {
 #pragma unroll
@@ -213,7 +248,7 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     const int nv_max = SKIP ? max(nvp, max(nvalid_of(0, half ^ 1), nvalid_of(1, half ^ 1))) : NBH;
     // K after Q: waiting for a K block also covers the (older) Q loads
     constexpr bool kSplitK = split_k_staging<NBH, SKIP>();
-    stage(kh, false, kb0, kSplitK ? nvp : nvalid, kSplitK);
+    stage(kh, false, kb0, kSplitK ? nvp : nvalid, std::integral_constant<bool, kSplitK>{});
     v4i qf[KS];                          // Q^T fragments, read from LDS in pass 1
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = v4i{0, 0, 0, 0};
@@ -345,7 +380,7 @@ __global__ __launch_bounds__(256) void ia_short_kernel(
     E += __shfl_xor(E, 32);
     if (hh == 0) lds.xe[qg][half][l32] = E;
     lds_barrier();                       // every wave is also done with K (and its K loads)
-    stage(vh, true, kb0, nvalid, false);   // V replaces K (whole blocks)
+    stage(vh, true, kb0, nvalid, std::false_type{});   // V replaces K (whole blocks)
     E += lds.xe[qg][half ^ 1][l32];
     // E >= 128*255 for every row that exists (it attends at least one key,
     // whose entry is 2^15, or 128*255 for a table of uint8 entries); rows
