@@ -19,7 +19,11 @@ recorded on the stream the library launches on (the caller's current
 stream). The same events give the kernel's average duration per launch used
 for the roofline fraction. Five more blocks of K calls give the median, and
 one block cycling through copies of the inputs (more than 512 MB in all, so
-they do not stay in the caches) gives the cold-input rate.
+they do not stay in the caches) gives the cold-input rate. Key "graph": the
+same calls captured in a HIP graph (50 calls a graph) and replayed, five
+blocks of replays (median), with the first replay's output checked against
+the eager output;
+`value` stays the rate of plain calls, one launch each.
 
 The default run (BERT) also times every other workload in the same process
 (key "workloads": tiny, BERT, ViT, causal prefill and batched decode, the
@@ -551,7 +555,58 @@ def hold_gpu(stream):
     torch.cuda._sleep(int(150.0 * _SLEEP_CYCLES_PER_US))
 
 
-def measure(w, steps, warmup, extra_timing=False, settle_s=CLOCK_SETTLE_S):
+GRAPH_CALLS = 50          # forward calls captured in one HIP graph (graph timing)
+
+
+def graph_timing(call, out, stream, steps):
+    """The same calls captured in one HIP graph (GRAPH_CALLS forward calls,
+    torch.cuda.CUDAGraph over the library's launches on the capture stream)
+    and replayed: the GPU's rate once the host submits one graph per
+    GRAPH_CALLS calls instead of one launch per call. The first replay's
+    output must equal the eager output left in `out`."""
+    import torch
+
+    dev = out.device
+    ref = out.clone()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        call()                                   # warm on the capture stream
+    stream.wait_stream(side)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(GRAPH_CALLS):
+            call()
+    torch.cuda.synchronize(dev)
+    out.zero_()
+    g.replay()
+    torch.cuda.synchronize(dev)
+    equal = bool(torch.equal(out, ref))
+    # one replay submits GRAPH_CALLS calls in less host time than the GPU
+    # takes to run them, so the host stays ahead without a spin kernel
+    reps = max(2, steps // GRAPH_CALLS)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.3:
+        g.replay()
+    torch.cuda.synchronize(dev)
+    blocks = []
+    for _ in range(5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        blocks.append(e0.elapsed_time(e1) / (reps * GRAPH_CALLS))
+    ms = sorted(blocks)[2]
+    del g
+    return {"ms_per_step": ms, "calls_per_s": 1e3 / ms, "calls_per_graph": GRAPH_CALLS,
+            "replays_per_block": reps, "blocks_ms_per_step": blocks, "first_replay_equals_eager": equal}
+
+
+def measure(w, steps, warmup, extra_timing=False, settle_s=CLOCK_SETTLE_S, graph=False):
     """Times intattn_forward over workload w with inputs resident in HBM.
 
     First settle_s seconds of untimed calls (the GPU leaves its idle clocks),
@@ -561,7 +616,8 @@ def measure(w, steps, warmup, extra_timing=False, settle_s=CLOCK_SETTLE_S):
     the first event keeps the GPU busy while the host enqueues the calls. Returns ms_per_step, the wall
     time of the timed region, the output (numpy) and, with extra_timing,
     five more blocks (median) and one block over input copies totalling more
-    than 512 MB (cold caches).
+    than 512 MB (cold caches), and with graph the rate of the same calls
+    replayed from a captured HIP graph (graph_timing).
     """
     import torch
 
@@ -617,6 +673,8 @@ def measure(w, steps, warmup, extra_timing=False, settle_s=CLOCK_SETTLE_S):
         res["timing"] = {"repeats_ms_per_step": reps, "median_ms_per_step": sorted(reps)[2],
                          "cold_ms_per_step": cold, "cold_input_sets": n_sets,
                          "cold_input_bytes": n_sets * per_set}
+    if graph:
+        res["graph"] = graph_timing(call, out, stream, steps)
     res["out"] = out.cpu().numpy()
     del q, k, v, out
     torch.cuda.empty_cache()
@@ -637,7 +695,7 @@ def all_workloads(bert_w, args):
         w = bert_w if name == "bert" else W.make_config(name)
         steps = DEFAULT_STEPS[name]
         warmup = min(DEFAULT_WARMUP[name], 200)
-        m = measure(w, steps, warmup)
+        m = measure(w, steps, warmup, graph=True)
         ops, nbytes, scores = algorithmic_work(w)
         sec = m["ms_per_step"] / 1e3
         tops, gbs = ops / sec / 1e12, nbytes / sec / 1e9
@@ -651,6 +709,7 @@ def all_workloads(bert_w, args):
             "ms_per_step": m["ms_per_step"], "calls_per_s": 1.0 / sec,
             "int8_tops": tops, "gb_per_s": gbs, "roofline": roofline(name, tops, gbs),
             "parity_on_sample": parity, "parity_heads": [list(bh) for bh in heads],
+            "graph": m["graph"],
         }
         if not args.no_cpu_baseline:
             cpu, _ = cpu_baseline(w, min(args.cpu_budget, 2.0))
@@ -681,7 +740,7 @@ def main(argv=None):
     ap.add_argument("--variants", action="store_true",
                     help="finer exp tables, grouped K/V heads and the cache update (one JSON line)")
     ap.add_argument("--no-extra-timing", action="store_true",
-                    help="skip the median-of-5 and cold-input blocks")
+                    help="skip the median-of-5, cold-input and HIP-graph blocks")
     ap.add_argument("--no-workloads", action="store_true",
                     help="time the headline workload only (default: also every other workload)")
     args = ap.parse_args(argv)
@@ -708,7 +767,7 @@ def main(argv=None):
     steps = args.steps or DEFAULT_STEPS[args.config]
     warmup = DEFAULT_WARMUP[args.config] if args.warmup is None else args.warmup
     w = W.make_config(args.config)
-    m = measure(w, steps, warmup, extra_timing=not args.no_extra_timing)
+    m = measure(w, steps, warmup, extra_timing=not args.no_extra_timing, graph=not args.no_extra_timing)
     ms_per_step = m["ms_per_step"]
     ops, nbytes, scores = algorithmic_work(w)
     sec = ms_per_step / 1e3
@@ -763,6 +822,7 @@ def main(argv=None):
         "roofline": roof,
         "valu_roofline": valu,
         "timing": m.get("timing"),
+        "graph": m.get("graph"),
         "cpu_baseline": cpu,
     }
     del m
