@@ -41,6 +41,12 @@
  * HIP device, and `stream` (NULL: the null stream) must belong to it; the
  * tensors must be memory that device can read and write.
  *
+ * Graph capture: the attention entry points queue only kernel launches on
+ * `stream` (no allocation, memset, copy or synchronisation), so their calls
+ * can be captured in a HIP graph and replayed. The long-row and decode
+ * kernels raise their dynamic LDS limit once per device on first use, a
+ * host-side call: make one uncaptured call of a shape before capturing it.
+ *
  * Ownership: all tensor pointers are caller-owned device memory and must stay
  * valid until the work queued on `stream` has finished. Structs are
  * caller-owned host memory read during the call only. The library keeps no
